@@ -52,15 +52,16 @@ def verify_attention(q, k, v, scale, softcap=0.0, window=0, return_weights=False
     weights = {}
     for i in range(n):
         p = L - n + i
-        keys = visible_keys(p, window)
+        keys = visible_keys(p, window)  # a contiguous range lo..p
+        lo, hi = int(keys[0]), int(keys[-1]) + 1
         for h in range(hq):
             kv = h // g
-            s = scale * (k[keys, kv, :] @ q[i, h, :])
+            s = scale * (k[lo:hi, kv, :] @ q[i, h, :])
             if softcap > 0.0:
                 s = softcap * np.tanh(s / softcap)
             e = np.exp(s - s.max())
             w = e / e.sum()
-            out[i, h, :] = w @ v[keys, kv, :]
+            out[i, h, :] = w @ v[lo:hi, kv, :]
             if return_weights:
                 weights[(i, h)] = (keys, w)
     if return_weights:

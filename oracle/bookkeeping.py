@@ -17,7 +17,9 @@ Readings where the pages are silent:
 * an append of n tokens needs ceil((seq_len + n) / 256) blocks in all; the
   missing ones are popped from the front of the free list, in order.  A
   multi-sequence append is all-or-nothing: if the pool cannot cover every
-  sequence in the call, nothing changes and ENOMEM is returned.
+  sequence in the call, nothing changes and ENOMEM is returned.  Entries are
+  validated in call order and the first bad one decides the status (bad id:
+  ENOSEQ; repeated id: EINVAL; table overflow: ERANGE); ENOMEM comes last.
 * rollback r requires 0 <= r <= seq_len and only moves seq_len; the blocks stay
   owned and the next append overwrites the rolled-back slots.
 * freeing a sequence pushes its blocks back onto the front of the free list in
@@ -72,12 +74,14 @@ class KVModel:
         """Append payloads[i] (a list, one entry per new token) to seqs[i]."""
         if len(seqs) != len(payloads):
             return EINVAL
-        if len(set(seqs)) != len(seqs):
-            return EINVAL
         need = []
-        for s, items in zip(seqs, payloads):
+        seen = set()
+        for s, items in zip(seqs, payloads):  # entries checked in call order
             if not (0 <= s < self.max_seqs):
                 return ENOSEQ
+            if s in seen:
+                return EINVAL
+            seen.add(s)
             total = self.blocks_needed(self.seq_len[s] + len(items))
             if total > self.max_blocks_per_seq:
                 return ERANGE
