@@ -1,0 +1,225 @@
+/*
+ * svattn.h - C ABI of the speculative-verify attention library (libsvattn.so).
+ *
+ * One handle (kv_cache) is one layer's paged KV cache on one GPU.  Each
+ * sequence of the cache owns 256-token blocks from a shared pool; a decode
+ * step appends the k draft tokens (plus the last accepted token) of every
+ * sequence, runs spec_verify_attn over the 1+k newest positions, and rolls
+ * back the rejected drafts by moving seq_len only.
+ *
+ * Sources on the pages:
+ *  - AX Engine page ("AX Engine: An LLM Inference Engine Built Exclusively
+ *    for Apple Silicon M4+"), "Core Technical Architecture & Methods": up to
+ *    4 drafts per step checked in one target forward; a deterministic,
+ *    synchronous KV/block manager; KV grown by slice-updates into preallocated
+ *    buffers; O(1) rollback that only moves the sequence-length pointer;
+ *    work on dedicated streams.
+ *  - AX Engine page, "Supported Model Families": dense GQA (Qwen3-4B); sliding
+ *    window + full layers and a logit soft cap (Gemma4).
+ *  - mlx-engine blog ("Improving LM Studio's MLX engine for agentic
+ *    workflows"), model-architecture and prompt-caching sections: 512-token
+ *    sliding-window local layers; caches handled in 256-token blocks; a cache
+ *    must rewind to an earlier length.
+ *  - SwiftLM page, TurboQuant KV-cache compression passage: keys as 3-bit
+ *    Lloyd-Max codes + 1-bit QJL (4.25 bits/dim), values as 3-bit codes
+ *    (3.125 bits/dim), encoded natively and dequantized inside attention.
+ *
+ * Conventions for every entry point:
+ *  - Every function returns an int status: KV_OK (0) or a negative KV_E*
+ *    code.  Arguments are validated on the host before anything is enqueued;
+ *    a call that fails changes no state (host or device) and enqueues no work.
+ *    kv_last_error() gives a message for the last failure on a handle.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work of a call is enqueued on it; no call waits for the device
+ *    except kv_create (once, for its constant uploads) and kv_destroy.  A
+ *    handle is not thread-safe; calls on one handle must be issued from one
+ *    thread and, if they use different streams, ordered by the caller.
+ *  - "host" pointer arguments are read during the call only.  "device"
+ *    pointers must stay valid until the enqueued work has finished.
+ *  - Device faults are not detected synchronously; a sticky HIP error seen at
+ *    the start of a later call is returned as KV_EDEVICE.
+ */
+#ifndef SVATTN_H
+#define SVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_OK 0
+#define KV_EINVAL (-1)  /* malformed argument (sizes, pointers, formats) */
+#define KV_ENOMEM (-2)  /* the pool has too few free blocks, or a buffer is too small */
+#define KV_ERANGE (-3)  /* a length out of range (rollback beyond seq_len, table full) */
+#define KV_ENOSEQ (-4)  /* sequence id outside [0, max_seqs) */
+#define KV_EDEVICE (-5) /* a HIP runtime call failed */
+
+/* Storage format of the cached K and V. */
+#define KV_FP32 0 /* float32 keys and values */
+#define KV_BF16 1 /* bfloat16 keys and values */
+#define KV_TQ3 2  /* compressed: see kv_encode */
+
+#define KV_BLOCK_SIZE 256 /* token positions per block (fixed) */
+#define KV_MAX_ROWS 8     /* query rows per sequence per verify call (1 + k) */
+
+typedef struct kv_cache kv_cache; /* opaque */
+
+typedef struct {
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* d: 64, 128 or 256 */
+  int32_t block_size;         /* must be KV_BLOCK_SIZE */
+  int32_t num_blocks;         /* blocks in the pool, >= 1 */
+  int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1 */
+  int32_t max_blocks_per_seq; /* table width: positions < 256 * this */
+  int32_t format;             /* KV_FP32, KV_BF16 or KV_TQ3 */
+  int32_t reserved;           /* must be 0 */
+  uint64_t alloc_seed;        /* free-list order: 0 = identity, else a SplitMix64 Fisher-Yates shuffle */
+  uint64_t codec_seed;        /* KV_TQ3 only: seeds the rotation signs and the QJL matrix */
+  void* pool;                 /* device memory owned by the caller, 256-byte aligned */
+  size_t pool_bytes;          /* >= kv_pool_bytes(params) */
+} kv_params;
+
+/*
+ * Bytes of device memory a pool for these parameters needs (blocks followed
+ * by the library's metadata: the device block table and, for KV_TQ3, the
+ * codec constants).  p->pool and p->pool_bytes are ignored.
+ *
+ * Block layout (per block, per kv head h, d = head_dim; all offsets are in
+ * the block's region, heads stored one after another):
+ *  KV_FP32 / KV_BF16 (e = 4 or 2 bytes): K as [256 tokens][d]; V as
+ *    [4 sub-tiles of 64 tokens][d][64 tokens] (token-minor inside a sub-tile).
+ *  KV_TQ3: K codes as [256][d/2] bytes, dimension i in nibble i (low nibble
+ *    first) holding code | sign_bit << 3; K norms n16 as [256] fp16; K
+ *    residual norms g16 as [256] fp16; V codes as [4][d][24 bytes], the 24
+ *    bytes holding 64 tokens' 3-bit codes, token t at bits 3t..3t+2
+ *    (little-endian bit order); V norms as [256] fp16.
+ */
+int kv_pool_bytes(const kv_params* p, size_t* out);
+
+/*
+ * Create a handle over a caller-owned pool.  Every sequence starts empty.
+ * Uploads the codec constants (KV_TQ3) on `stream` and waits for them.
+ * The pool must outlive the handle; the handle never allocates device memory.
+ * Errors: KV_EINVAL (bad params), KV_ENOMEM (pool too small), KV_EDEVICE.
+ */
+int kv_create(const kv_params* p, void* stream, kv_cache** out);
+
+/* Destroy a handle (waits for nothing; the caller orders it after the last
+ * enqueued call).  NULL is accepted. */
+int kv_destroy(kv_cache* c);
+
+/*
+ * Append n_new[i] new token positions to sequence seq_ids[i], for i < n_seqs,
+ * as one all-or-nothing reservation (AX Engine page, "Core Technical
+ * Architecture & Methods": slice-update into preallocated buffers).
+ *  seq_ids, n_new: host arrays of n_seqs entries; ids distinct; n_new >= 0.
+ *  k, v: device arrays [sum(n_new)][num_kv_heads][head_dim], rows in the
+ *    order of seq_ids; dtype float32 for KV_FP32 and KV_TQ3, bfloat16 for
+ *    KV_BF16.  For KV_TQ3 the rows are encoded as they are stored (the
+ *    quantize-on-append path).
+ * Blocks are popped from the front of the free list as a sequence's length
+ * crosses 256-token boundaries.  Errors: KV_ENOSEQ, KV_EINVAL, KV_ERANGE
+ * (a table would overflow), KV_ENOMEM (not enough free blocks for the whole
+ * call), KV_EDEVICE.
+ */
+int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+              const void* k, const void* v, void* stream);
+
+/*
+ * Drop the newest n_tokens positions of a sequence: seq_len -= n_tokens, in
+ * O(1), host only (AX Engine page, "Core Technical Architecture & Methods").
+ * Blocks stay owned; the next append overwrites the dropped slots.
+ * Errors: KV_ENOSEQ, KV_EINVAL (n_tokens < 0), KV_ERANGE (n_tokens > seq_len).
+ */
+int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens);
+
+/* Release every block of a sequence (pushed back onto the front of the free
+ * list, first-owned block first) and reset its length to 0.  The caller must
+ * not free a sequence that enqueued work still reads.  Errors: KV_ENOSEQ. */
+int kv_seq_free(kv_cache* c, int32_t seq_id);
+
+/*
+ * Encode n_vecs vectors with the handle's codec (KV_TQ3 handles only): the
+ * quantize step of the compressed cache on its own, without touching the
+ * pool (SwiftLM page, TurboQuant KV-cache compression passage).
+ *  src: device float32 [n_vecs][d].
+ *  dst: device, n_vecs records of kv_record_bytes(d, is_key) bytes each:
+ *    key record  = d/2 code|sign nibbles, fp16 n16, fp16 g16 (68 B at d=128);
+ *    value record = 3d/8 bytes of 3-bit codes (dimension i at bits 3i..3i+2,
+ *    little-endian), fp16 n16 (50 B at d=128).
+ * The encoder works in double precision: n = |x|, z = sqrt(d) * Pi x / n with
+ * Pi = H_d diag(D) / sqrt(d), code = number of Lloyd-Max thresholds <= z_i,
+ * n16 = fp16(n); keys also r = Pi x - n16 * c16[code] / sqrt(d),
+ * g16 = fp16(|r|), sign bit = [(S r)_i >= 0].
+ * Errors: KV_EINVAL (not a KV_TQ3 handle, n_vecs < 0), KV_EDEVICE.
+ */
+int kv_encode(const kv_cache* c, int64_t n_vecs, const float* src, int32_t is_key, void* dst,
+              void* stream);
+
+/* Bytes of one kv_encode record. */
+int kv_record_bytes(int32_t head_dim, int32_t is_key, int32_t* out);
+
+/*
+ * Workspace bytes spec_verify_attn needs for this call shape (same arguments
+ * as spec_verify_attn).  Errors as spec_verify_attn's validation.
+ */
+int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids,
+                       const int32_t* n_rows, int32_t num_q_heads, int32_t window, size_t* out);
+
+/*
+ * Verify attention over the newest positions of each sequence: the one kernel
+ * path these pages revolve around (AX Engine page, "Core Technical
+ * Architecture & Methods"; SwiftLM page, speculative-decoding passage: N+1
+ * positions verified at once).
+ *  seq_ids, n_rows: host arrays of n_seqs entries; 1 <= n_rows[i] <=
+ *    min(KV_MAX_ROWS, seq_len); row r of sequence i sits at position
+ *    seq_len - n_rows[i] + r, so the rows' K/V must already be appended.
+ *  q: device float32 [sum(n_rows)][num_q_heads][head_dim], rows in the order
+ *    of seq_ids.  num_q_heads must be a multiple of num_kv_heads; query head
+ *    h reads kv head h / (num_q_heads / num_kv_heads).
+ *  scale: multiplies <q, k>.  softcap: 0 = off, else s <- softcap *
+ *    tanh(s / softcap) after scaling.  window: 0 = full, else position p sees
+ *    keys j with 0 <= p - j < window.  Row p never sees keys beyond itself.
+ *  out: device float32 [sum(n_rows)][num_q_heads][head_dim].
+ *  workspace: device, ws_bytes >= kv_workspace_bytes(...), 256-byte aligned;
+ *    it holds split-context partial results.  Calls that share a workspace
+ *    must be ordered on one stream.
+ * KV_TQ3: queries are rotated in the kernel path (q' = Pi q, q'' = S q'),
+ * scores use the stored codes and norms, and the output is rotated back.
+ * Errors: KV_ENOSEQ, KV_EINVAL, KV_ERANGE (n_rows > seq_len), KV_ENOMEM
+ * (workspace too small), KV_EDEVICE.
+ */
+int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                     const float* q, int32_t num_q_heads, float scale, float softcap,
+                     int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- introspection (host only; never touches the device) ---- */
+
+/* Current length of a sequence.  Errors: KV_ENOSEQ. */
+int kv_seq_len(const kv_cache* c, int32_t seq_id, int32_t* out);
+
+/* Copy up to cap entries of a sequence's block table to out (host) and the
+ * number of blocks it owns to *n_owned.  Errors: KV_ENOSEQ, KV_EINVAL. */
+int kv_block_table(const kv_cache* c, int32_t seq_id, int32_t* out, int32_t cap, int32_t* n_owned);
+
+/* Number of blocks on the free list. */
+int kv_free_blocks(const kv_cache* c, int32_t* out);
+
+/* KV_TQ3 codec constants as the library computed them (host copies; any
+ * pointer may be NULL): signs[d] (+-1), s_matrix[d*d] row-major float32,
+ * levels[8] (the Lloyd-Max centroids, fp64), levels16[8] (the stored fp16
+ * reconstruction levels, as fp64 values), thresholds[7] (fp64).
+ * Errors: KV_EINVAL (not KV_TQ3). */
+int kv_codec(const kv_cache* c, int8_t* signs, float* s_matrix, double* levels,
+             double* levels16, double* thresholds);
+
+/* Message for the last failed call on this handle ("" if none). */
+const char* kv_last_error(const kv_cache* c);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVATTN_H */

@@ -1,0 +1,89 @@
+"""Build the native libraries in-tree.
+
+* ``libsvattn.so``       - the C ABI (include/svattn.h): host core + HIP
+  kernels for gfx950, built with hipcc.
+* ``libsvattn_core.so``  - the HIP-free host core alone (include/svcore.h),
+  built with g++, for host-logic tests on machines without a GPU.
+
+Usage: ``python -m speculative_verify_attention_amd.build`` (or ``build()``).
+Every call compiles from source; objects go to ``_build/`` beside the
+package.
+"""
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsvattn.so")
+CORE_LIB = os.path.join(PKG, "libsvattn_core.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    # packed fp32 ops are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+HIP_SOURCES = ["attn.hip", "append.hip", "svattn.cpp", "kvcore.cpp"]
+CORE_SOURCES = ["kvcore.cpp", "svcore_capi.cpp"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout)
+    return r.stdout
+
+
+def _compile_hip(src):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    return obj
+
+
+def build_core():
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = CORE_LIB + ".tmp"
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-I", INCLUDE, "-I", CSRC,
+          *[os.path.join(CSRC, s) for s in CORE_SOURCES], "-o", tmp])
+    os.replace(tmp, CORE_LIB)
+    return CORE_LIB
+
+
+def build_hip(jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(4, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile_hip, HIP_SOURCES))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build():
+    core = build_core()
+    lib = build_hip()
+    return lib, core
+
+
+if __name__ == "__main__":
+    for p in build():
+        print(p)
+    sys.exit(0)

@@ -1,0 +1,412 @@
+// append.hip - the write side of the cache on gfx950:
+//  * block-table update (new blocks of an append become visible to readers);
+//  * slice-update of new K/V positions into their blocks (fp32 / bf16);
+//  * quantize-on-append for the compressed format, and the same encoder as a
+//    stand-alone pass (kv_encode).
+//
+// AX Engine page, "Core Technical Architecture & Methods": the cache grows by
+// slice-updates into preallocated buffers.  SwiftLM page, TurboQuant KV-cache
+// compression passage: keys get 3-bit Lloyd-Max codes plus a 1-bit QJL
+// residual, values 3-bit codes only, encoded natively.
+//
+// The encoder works in double precision, one wavefront per vector; the
+// rotation is a fast Walsh-Hadamard transform done in registers with
+// cross-lane exchanges.  It is off the throughput path (a few vectors per
+// sequence per step), so it is written for exactness, not speed.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace svattn {
+
+PoolLayout make_layout(int fmt, int hkv, int d) {
+  PoolLayout L{};
+  L.fmt = fmt;
+  L.hkv = hkv;
+  L.d = d;
+  if (fmt == 2) {
+    L.kc_off = 0;
+    L.kn_off = L.kc_off + (int64_t)hkv * 256 * (d / 2);
+    L.kg_off = L.kn_off + (int64_t)hkv * 256 * 2;
+    L.vc_off = L.kg_off + (int64_t)hkv * 256 * 2;
+    L.vn_off = L.vc_off + (int64_t)hkv * 4 * d * 24;
+    L.block_bytes = L.vn_off + (int64_t)hkv * 256 * 2;
+  } else {
+    int64_t e = fmt == 0 ? 4 : 2;
+    L.k_off = 0;
+    L.v_off = (int64_t)hkv * 256 * d * e;
+    L.block_bytes = 2 * L.v_off;
+  }
+  return L;
+}
+
+// ---- block-table update -------------------------------------------------------
+
+__global__ void table_update_kernel(TableUpdateArgs a) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.count) a.table[a.index[i]] = a.block[i];
+}
+
+hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_update_kernel, dim3((a.count + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- helpers --------------------------------------------------------------------
+
+__device__ inline int find_seg(const int32_t* unit0, int n_segs, int unit) {
+  int lo = 0, hi = n_segs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (unit0[mid] <= unit)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// IEEE half (bits) of a non-negative double, nearest-even, saturating at 65504.
+__device__ inline uint16_t half_rne(double x, uint32_t* sat) {
+  if (!(x == x)) return 0x7E00;
+  if (x >= 65520.0) {
+    *sat = 1;
+    return 0x7BFF;
+  }
+  if (x < 0x1p-14) return (uint16_t)__builtin_rint(x * 0x1p24);
+  int e = ilogb(x);
+  double m = __builtin_rint(ldexp(x, 10 - e));
+  if (m == 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  if (e + 15 >= 31) {
+    *sat = 1;
+    return 0x7BFF;
+  }
+  return (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+__device__ inline double half_value(uint16_t h) {
+  int e = (h >> 10) & 31, f = h & 1023;
+  return e == 0 ? (double)f * 0x1p-24 : ldexp((double)(f + 1024), e - 25);
+}
+
+// Encoded form of one vector, spread over a wavefront: lane l owns
+// dimensions l*E .. l*E+E-1 (E = D / 64).
+template <int D>
+struct EncOut {
+  static constexpr int E = D / 64;
+  uint8_t code[E];
+  uint8_t bit[E];
+  uint16_t n16, g16;
+};
+
+// Encode x (global, fp32, D values) with one full wavefront.  rbuf: this
+// wave's D doubles of LDS.
+template <int D>
+__device__ void encode_vector(const float* __restrict__ x, bool is_key, const int8_t* __restrict__ signs,
+                              const float* __restrict__ s_t, const double* thr, const double* lev16,
+                              double* rbuf, EncOut<D>& o, uint32_t* sat) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  double v[E];
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    double xi = (double)x[lane * E + e];
+    ss += xi * xi;
+    v[e] = signs[lane * E + e] < 0 ? -xi : xi;  // D x
+  }
+  ss = wave_sum(ss);
+  const double n = sqrt(ss);
+  // zx = H (D x): Walsh-Hadamard butterflies; in-lane stages first, then
+  // cross-lane stages (partner lane = lane ^ (h / E)).
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!(e & h)) {
+        double a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int hl = 1; hl < 64; hl <<= 1) {
+    const bool upper = (lane & hl) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      double p = __shfl_xor(v[e], hl);
+      v[e] = upper ? (p - v[e]) : (v[e] + p);
+    }
+  }
+  // z = sqrt(d) * Pi x / n = zx / n; code = #thresholds <= z.
+  uint32_t s = 0;
+  const uint16_t n16 = half_rne(n, &s);
+  const double n16v = half_value(n16);
+  const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  double r[E];
+  double rr = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    double z = n > 0.0 ? v[e] / n : 0.0;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) c += (thr[j] <= z) ? 1 : 0;
+    o.code[e] = (uint8_t)c;
+    // residual in the rotated frame: Pi x - n16 * c16[code] / sqrt(d)
+    r[e] = (v[e] - n16v * lev16[c]) * inv_sqrt_d;
+    rr += r[e] * r[e];
+  }
+  o.n16 = n16;
+  o.g16 = 0;
+  if (is_key) {
+    rr = wave_sum(rr);
+    o.g16 = half_rne(sqrt(rr), &s);
+    // proj = S r: every lane needs all of r, so pass it through LDS.
+#pragma unroll
+    for (int e = 0; e < E; ++e) rbuf[lane * E + e] = r[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    double proj[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) proj[e] = 0.0;
+    for (int j = 0; j < D; ++j) {
+      const double rj = rbuf[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) proj[e] += (double)s_t[j * D + lane * E + e] * rj;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) o.bit[e] = proj[e] >= 0.0 ? 1 : 0;
+    // keep rbuf stable until every lane has read it before a later reuse
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) o.bit[e] = 0;
+  }
+  if (s) *sat = 1;
+}
+
+// Write the key nibbles of one encoded vector: byte b of the record holds
+// dims 2b (low nibble) and 2b+1 (high nibble).
+template <int D>
+__device__ inline void store_key_nibbles(uint8_t* dst, const EncOut<D>& o) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  if constexpr (E == 1) {
+    uint32_t nib = (uint32_t)(o.code[0] | (o.bit[0] << 3));
+    uint32_t hi = __shfl_down(nib, 1);
+    if ((lane & 1) == 0) dst[lane >> 1] = (uint8_t)(nib | (hi << 4));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      uint32_t lo = o.code[e] | (o.bit[e] << 3);
+      uint32_t hi = o.code[e + 1] | (o.bit[e + 1] << 3);
+      dst[(lane * E + e) >> 1] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+}
+
+__device__ inline void store_half(uint8_t* p, uint16_t h) {
+  p[0] = (uint8_t)(h & 0xFF);
+  p[1] = (uint8_t)(h >> 8);
+}
+
+// ---- plain slice-update ----------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
+  const int unit = blockIdx.x;  // one source row
+  const int h = blockIdx.y;
+  const int seg = find_seg(a.unit0, a.n_segs, unit);
+  const int r = unit - a.unit0[seg];
+  const int pos = a.pos0[seg] + r;
+  const int64_t src_row = (int64_t)a.row0[seg] + r;
+  const int d = a.lay.d;
+  const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (pos >> 8)];
+  const int slot = pos & 255;
+  uint8_t* base = a.pool + (int64_t)block * a.lay.block_bytes;
+  T* kdst = reinterpret_cast<T*>(base + a.lay.k_off) + ((int64_t)h * 256 + slot) * d;
+  T* vdst = reinterpret_cast<T*>(base + a.lay.v_off) + ((int64_t)h * 4 + (slot >> 6)) * d * 64 + (slot & 63);
+  const T* ksrc = reinterpret_cast<const T*>(a.k) + (src_row * a.lay.hkv + h) * d;
+  const T* vsrc = reinterpret_cast<const T*>(a.v) + (src_row * a.lay.hkv + h) * d;
+  for (int e = threadIdx.x; e < d; e += 64) {
+    kdst[e] = ksrc[e];
+    vdst[(int64_t)e * 64] = vsrc[e];
+  }
+}
+
+// ---- quantize-on-append ----------------------------------------------------------
+
+// One workgroup (4 waves) per (segment, 64-token group, kv head).  Each wave
+// encodes whole tokens; value codes of the group are staged in LDS and then
+// packed per dimension, merging with the codes of tokens the append does not
+// touch (one writer per 24-byte row, so no two workgroups race on it).
+template <int D>
+__global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
+  constexpr int E = D / 64;
+  __shared__ double rbuf[4][D];
+  __shared__ uint8_t vcode[64][D];
+  __shared__ uint32_t sat_any;
+  const int unit = blockIdx.x;
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) sat_any = 0;
+  const int seg = find_seg(a.unit0, a.n_segs, unit);
+  const int pos0 = a.pos0[seg];
+  const int grp = (pos0 >> 6) + (unit - a.unit0[seg]);
+  const int t0 = max(pos0, grp * 64);
+  const int t1 = min(pos0 + a.n[seg], grp * 64 + 64);
+  const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 2)];
+  uint8_t* base = a.pool + (int64_t)block * a.lay.block_bytes;
+  uint32_t sat = 0;
+  __syncthreads();
+  for (int t = t0 + wave; t < t1; t += 4) {
+    const int slot = t & 255;
+    const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
+    const float* kx = reinterpret_cast<const float*>(a.k) + (src_row * a.lay.hkv + h) * D;
+    const float* vx = reinterpret_cast<const float*>(a.v) + (src_row * a.lay.hkv + h) * D;
+    EncOut<D> ko, vo;
+    encode_vector<D>(kx, true, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
+    store_key_nibbles<D>(base + a.lay.kc_off + ((int64_t)h * 256 + slot) * (D / 2), ko);
+    if (lane == 0) {
+      store_half(base + a.lay.kn_off + ((int64_t)h * 256 + slot) * 2, ko.n16);
+      store_half(base + a.lay.kg_off + ((int64_t)h * 256 + slot) * 2, ko.g16);
+    }
+    encode_vector<D>(vx, false, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
+#pragma unroll
+    for (int e = 0; e < E; ++e) vcode[t & 63][lane * E + e] = vo.code[e];
+    if (lane == 0) store_half(base + a.lay.vn_off + ((int64_t)h * 256 + slot) * 2, vo.n16);
+  }
+  if (sat) atomicOr(&sat_any, 1u);
+  __syncthreads();
+  // Pack value codes: row (h, group-in-block, dim) is 24 bytes = 6 words;
+  // token u of the group at bits 3u..3u+2.
+  const int q = grp & 3;
+  const int u0 = t0 & 63, u1 = u0 + (t1 - t0);
+  for (int dim = threadIdx.x; dim < D; dim += 256) {
+    uint32_t* row = reinterpret_cast<uint32_t*>(base + a.lay.vc_off + (((int64_t)h * 4 + q) * D + dim) * 24);
+    uint32_t w[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) w[i] = row[i];
+    for (int u = u0; u < u1; ++u) {
+      const uint32_t c = vcode[u][dim];
+      const int bit = 3 * u;
+      const int wi = bit >> 5, sh = bit & 31;
+      w[wi] = (w[wi] & ~(7u << sh)) | (c << sh);
+      if (sh > 29) {  // the code straddles two words
+        const int rem = 32 - sh;
+        w[wi + 1] = (w[wi + 1] & ~(7u >> rem)) | (c >> rem);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) row[i] = w[i];
+  }
+  if (threadIdx.x == 0 && sat_any) atomicOr(a.status, 1u);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.total_units <= 0) return hipSuccess;
+  dim3 grid(a.total_units, a.lay.hkv);
+  if (a.lay.fmt == 0) {
+    hipLaunchKernelGGL(append_plain_kernel<float>, grid, dim3(64), 0, s, a);
+  } else if (a.lay.fmt == 1) {
+    hipLaunchKernelGGL(append_plain_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+  } else {
+    switch (a.lay.d) {
+      case 64:
+        hipLaunchKernelGGL(append_tq3_kernel<64>, grid, dim3(256), 0, s, a);
+        break;
+      case 128:
+        hipLaunchKernelGGL(append_tq3_kernel<128>, grid, dim3(256), 0, s, a);
+        break;
+      case 256:
+        hipLaunchKernelGGL(append_tq3_kernel<256>, grid, dim3(256), 0, s, a);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+// ---- stand-alone encode ------------------------------------------------------------
+
+// One wave per vector, 4 vectors per workgroup.  Record layout: key = D/2
+// nibble bytes, n16, g16; value = 3D/8 bytes of 3-bit codes (dim i at bits
+// 3i..3i+2), n16.
+template <int D>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+  constexpr int E = D / 64;
+  __shared__ double rbuf[4][D];
+  __shared__ uint8_t codes[4][D];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t vec = (int64_t)blockIdx.x * 4 + wave;
+  uint32_t sat = 0;
+  if (vec < a.n) {
+    const int rec = a.is_key ? (D / 2 + 4) : (3 * D / 8 + 2);
+    uint8_t* dst = a.dst + vec * rec;
+    EncOut<D> o;
+    encode_vector<D>(a.src + vec * D, a.is_key != 0, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], o, &sat);
+    if (a.is_key) {
+      store_key_nibbles<D>(dst, o);
+      if (lane == 0) {
+        store_half(dst + D / 2, o.n16);
+        store_half(dst + D / 2 + 2, o.g16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) codes[wave][lane * E + e] = o.code[e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int b = lane; b < 3 * D / 8; b += 64) {
+        uint32_t val = 0;
+        const int first = (8 * b) / 3, last = (8 * b + 7) / 3;
+        for (int i = first; i <= last && i < D; ++i) {
+          const int pos = 3 * i - 8 * b;  // bit of code i relative to byte b
+          const uint32_t c = codes[wave][i];
+          val |= pos >= 0 ? (c << pos) : (c >> (-pos));
+        }
+        dst[b] = (uint8_t)(val & 0xFF);
+      }
+      if (lane == 0) store_half(dst + 3 * D / 8, o.n16);
+    }
+    if (sat && lane == 0) atomicOr(a.status, 1u);
+  }
+}
+
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((a.n + 3) / 4));
+  switch (a.d) {
+    case 64:
+      hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(256), 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(256), 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(encode_kernel<256>, grid, dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svattn

@@ -1,0 +1,468 @@
+// svattn.cpp - the C ABI (include/svattn.h) over the host core and the
+// gfx950 kernels.  Validation happens on the host before anything is
+// enqueued; the core's state changes only after every launch of a call has
+// been enqueued successfully.
+#include "svattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "kvcore.h"
+
+using namespace svattn;
+
+struct kv_cache {
+  Core core;
+  PoolLayout lay;
+  uint8_t* pool = nullptr;
+  size_t pool_bytes = 0;
+  int32_t* dtable = nullptr;   // device block table [max_seqs][max_blocks_per_seq]
+  uint32_t* dstatus = nullptr; // device status word
+  int8_t* dsigns = nullptr;    // TQ3: D
+  float* ds_t = nullptr;       // TQ3: S transposed
+  std::vector<int8_t> h_signs;
+  std::vector<float> h_s_t;
+  std::vector<uint32_t> h_zero;
+  std::string err;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct MetaLayout {
+  size_t blocks_bytes, table_off, status_off, signs_off, st_off, total;
+};
+
+MetaLayout meta_layout(const kv_params& p, const PoolLayout& lay) {
+  MetaLayout m;
+  m.blocks_bytes = (size_t)p.num_blocks * (size_t)lay.block_bytes;
+  m.table_off = align_up(m.blocks_bytes);
+  m.status_off = align_up(m.table_off + (size_t)p.max_seqs * p.max_blocks_per_seq * 4);
+  m.signs_off = m.status_off + kAlign;
+  m.st_off = m.signs_off;
+  m.total = m.status_off + kAlign;
+  if (p.format == KV_TQ3) {
+    m.st_off = align_up(m.signs_off + (size_t)p.head_dim);
+    m.total = align_up(m.st_off + (size_t)p.head_dim * p.head_dim * 4);
+  }
+  return m;
+}
+
+int set_err(kv_cache* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+int check_device(kv_cache* c) {
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess) {
+    hipGetLastError();
+    return set_err(c, KV_EDEVICE, std::string("HIP error before call: ") + hipGetErrorString(e));
+  }
+  return KV_OK;
+}
+
+int hip_fail(kv_cache* c, hipError_t e, const char* what) {
+  return set_err(c, KV_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+CoreParams core_params(const kv_params& p) {
+  CoreParams cp;
+  cp.num_kv_heads = p.num_kv_heads;
+  cp.head_dim = p.head_dim;
+  cp.block_size = p.block_size;
+  cp.num_blocks = p.num_blocks;
+  cp.max_seqs = p.max_seqs;
+  cp.max_blocks_per_seq = p.max_blocks_per_seq;
+  cp.format = p.format;
+  cp.alloc_seed = p.alloc_seed;
+  cp.codec_seed = p.codec_seed;
+  return cp;
+}
+
+// ---- verify-call planning (shared by kv_workspace_bytes and spec_verify_attn) ----
+
+struct VerifyLaunch {
+  int first, count;  // sequences [first, first+count) of the call
+  int total_tiles, tiles_per_wg, n_wg, n_pairs;
+  int64_t slot0;     // first partial slot of this launch
+  std::vector<int32_t> tile_base;
+};
+
+struct VerifyPlan {
+  int nct = 1, rpad = 32;
+  int64_t slot_stride = 0, slots = 0, rows = 0;
+  size_t part_bytes = 0, q_bytes = 0, total = 0;
+  std::vector<VerifyLaunch> launches;
+};
+
+int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                int32_t num_q_heads, int32_t window, VerifyPlan* vp, std::string* err) {
+  const CoreParams& P = c->core.params();
+  auto fail = [&](int code, const std::string& m) {
+    if (err) *err = m;
+    return code;
+  };
+  if (n_seqs < 1) return fail(KV_EINVAL, "n_seqs must be >= 1");
+  if (!seq_ids || !n_rows) return fail(KV_EINVAL, "null seq_ids / n_rows");
+  if (num_q_heads < 1 || num_q_heads % P.num_kv_heads) return fail(KV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (window < 0) return fail(KV_EINVAL, "window < 0");
+  const int g = num_q_heads / P.num_kv_heads;
+  int max_rows = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (!c->core.valid_seq(seq_ids[i])) return fail(KV_ENOSEQ, "sequence id " + std::to_string(seq_ids[i]) + " out of range");
+    int32_t len;
+    c->core.seq_len(seq_ids[i], &len);
+    if (n_rows[i] < 1 || n_rows[i] > KV_MAX_ROWS) return fail(KV_EINVAL, "n_rows must be in [1, 8]");
+    if (n_rows[i] > len) return fail(KV_ERANGE, "n_rows exceeds seq_len of sequence " + std::to_string(seq_ids[i]));
+    max_rows = std::max(max_rows, (int)n_rows[i]);
+    vp->rows += n_rows[i];
+  }
+  const int R = max_rows * g;
+  if (R > 64) return fail(KV_EINVAL, "n_rows * (num_q_heads / num_kv_heads) must be <= 64");
+  vp->nct = R > 32 ? 2 : 1;
+  vp->rpad = 32 * vp->nct;
+  vp->slot_stride = (int64_t)vp->rpad * (2 + P.head_dim);
+  const int TL = 4 / vp->nct;
+  const int target_wg = P.head_dim > 128 ? 256 : 512;
+  for (int first = 0; first < n_seqs; first += kMaxAttnSeqs) {
+    VerifyLaunch L;
+    L.first = first;
+    L.count = std::min(kMaxAttnSeqs, n_seqs - first);
+    L.tile_base.assign(L.count + 1, 0);
+    for (int i = 0; i < L.count; ++i) {
+      int32_t len;
+      c->core.seq_len(seq_ids[first + i], &len);
+      const int n = n_rows[first + i];
+      const int klo = window > 0 ? std::max(0, len - n - window + 1) : 0;
+      const int nt = (len + kTileKeys - 1) / kTileKeys - klo / kTileKeys;
+      L.tile_base[i + 1] = L.tile_base[i] + nt * P.num_kv_heads;
+    }
+    L.total_tiles = L.tile_base[L.count];
+    L.tiles_per_wg = std::max(TL, (L.total_tiles + target_wg - 1) / target_wg);
+    L.n_wg = (L.total_tiles + L.tiles_per_wg - 1) / L.tiles_per_wg;
+    L.n_pairs = L.count * P.num_kv_heads;
+    L.slot0 = vp->slots;
+    vp->slots += L.n_wg + L.n_pairs;
+    vp->launches.push_back(std::move(L));
+  }
+  vp->part_bytes = align_up((size_t)vp->slots * vp->slot_stride * 4);
+  if (P.format == KV_TQ3) vp->q_bytes = align_up((size_t)vp->rows * num_q_heads * P.head_dim * 4);
+  vp->total = vp->part_bytes + 2 * vp->q_bytes;
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_pool_bytes(const kv_params* p, size_t* out) {
+  if (!p || !out) return KV_EINVAL;
+  Core probe;
+  std::string err;
+  kv_params q = *p;
+  if (probe.init(core_params(q), &err) != KV_OK) return KV_EINVAL;
+  PoolLayout lay = make_layout(p->format, p->num_kv_heads, p->head_dim);
+  *out = meta_layout(*p, lay).total;
+  return KV_OK;
+}
+
+int kv_record_bytes(int32_t head_dim, int32_t is_key, int32_t* out) {
+  if (!out || (head_dim != 64 && head_dim != 128 && head_dim != 256)) return KV_EINVAL;
+  *out = is_key ? head_dim / 2 + 4 : 3 * head_dim / 8 + 2;
+  return KV_OK;
+}
+
+int kv_create(const kv_params* p, void* stream, kv_cache** out) {
+  if (!p || !out) return KV_EINVAL;
+  *out = nullptr;
+  if (p->reserved != 0) return KV_EINVAL;
+  kv_cache* c = new kv_cache();
+  std::string err;
+  int rc = c->core.init(core_params(*p), &err);
+  if (rc != KV_OK) {
+    delete c;
+    return rc;
+  }
+  c->lay = make_layout(p->format, p->num_kv_heads, p->head_dim);
+  MetaLayout m = meta_layout(*p, c->lay);
+  if (!p->pool || (reinterpret_cast<uintptr_t>(p->pool) % kAlign) != 0) {
+    delete c;
+    return KV_EINVAL;
+  }
+  if (p->pool_bytes < m.total) {
+    delete c;
+    return KV_ENOMEM;
+  }
+  if (check_device(c) != KV_OK) {
+    delete c;
+    return KV_EDEVICE;
+  }
+  c->pool = static_cast<uint8_t*>(p->pool);
+  c->pool_bytes = p->pool_bytes;
+  c->dtable = reinterpret_cast<int32_t*>(c->pool + m.table_off);
+  c->dstatus = reinterpret_cast<uint32_t*>(c->pool + m.status_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  c->h_zero.assign(kAlign / 4, 0u);
+  hipError_t e = hipMemcpyAsync(c->dstatus, c->h_zero.data(), kAlign, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && p->format == KV_TQ3) {
+    const Codec& cd = c->core.codec();
+    const int d = p->head_dim;
+    c->dsigns = reinterpret_cast<int8_t*>(c->pool + m.signs_off);
+    c->ds_t = reinterpret_cast<float*>(c->pool + m.st_off);
+    c->h_signs = cd.signs;
+    c->h_s_t.resize((size_t)d * d);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) c->h_s_t[(size_t)j * d + i] = cd.s[(size_t)i * d + j];
+    e = hipMemcpyAsync(c->dsigns, c->h_signs.data(), d, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(c->ds_t, c->h_s_t.data(), (size_t)d * d * 4, hipMemcpyHostToDevice, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete c;
+    return KV_EDEVICE;
+  }
+  *out = c;
+  return KV_OK;
+}
+
+int kv_destroy(kv_cache* c) {
+  delete c;
+  return KV_OK;
+}
+
+int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k,
+              const void* v, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  AppendPlan plan;
+  rc = c->core.plan_append(n_seqs, seq_ids, n_new, &plan, &c->err);
+  if (rc != KV_OK) return rc;
+  if (plan.total_rows > 0 && (!k || !v)) return set_err(c, KV_EINVAL, "null k / v");
+  if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. new blocks become visible in the device table
+  for (size_t i = 0; i < plan.popped.size(); i += kMaxTableUpdates) {
+    TableUpdateArgs ta;
+    ta.table = c->dtable;
+    ta.count = (int32_t)std::min<size_t>(kMaxTableUpdates, plan.popped.size() - i);
+    for (int j = 0; j < ta.count; ++j) {
+      ta.index[j] = plan.table_index[i + j];
+      ta.block[j] = plan.popped[i + j];
+    }
+    hipError_t e = launch_table_update(ta, s);
+    if (e != hipSuccess) return hip_fail(c, e, "table update launch");
+  }
+  // 2. slice-update / quantize-on-append, in launches of <= kMaxAppendSegs segments
+  const CoreParams& P = c->core.params();
+  std::vector<const AppendSeg*> segs;
+  for (const AppendSeg& g : plan.segs)
+    if (g.n > 0) segs.push_back(&g);
+  const bool tq3 = P.format == KV_TQ3;
+  for (size_t i = 0; i < segs.size();) {
+    AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = c->pool;
+    a.table = c->dtable;
+    a.k = k;
+    a.v = v;
+    a.lay = c->lay;
+    a.max_bps = P.max_blocks_per_seq;
+    a.n_segs = 0;
+    int64_t units = 0;
+    while (i < segs.size() && a.n_segs < kMaxAppendSegs) {
+      const AppendSeg& g = *segs[i];
+      const int64_t u = tq3 ? (int64_t)((g.pos0 + g.n - 1) / 64 - g.pos0 / 64 + 1) : g.n;
+      if (units + u > (int64_t)INT32_MAX / 2 && a.n_segs > 0) break;
+      a.unit0[a.n_segs] = (int32_t)units;
+      a.seq[a.n_segs] = g.seq;
+      a.pos0[a.n_segs] = g.pos0;
+      a.n[a.n_segs] = g.n;
+      a.row0[a.n_segs] = g.src_row0;
+      units += u;
+      ++a.n_segs;
+      ++i;
+    }
+    a.unit0[a.n_segs] = (int32_t)units;
+    a.total_units = (int32_t)units;
+    if (tq3) {
+      const Codec& cd = c->core.codec();
+      a.signs = c->dsigns;
+      a.s_t = c->ds_t;
+      for (int j = 0; j < 7; ++j) a.thr[j] = cd.thresholds[j];
+      for (int j = 0; j < 8; ++j) a.lev16[j] = cd.levels16[j];
+      a.status = c->dstatus;
+    }
+    hipError_t e = launch_append(a, s);
+    if (e != hipSuccess) return hip_fail(c, e, "append launch");
+  }
+  c->core.commit_append(plan);
+  return KV_OK;
+}
+
+int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens) {
+  if (!c) return KV_EINVAL;
+  return c->core.rollback(seq_id, n_tokens, &c->err);
+}
+
+int kv_seq_free(kv_cache* c, int32_t seq_id) {
+  if (!c) return KV_EINVAL;
+  return c->core.free_seq(seq_id, &c->err);
+}
+
+int kv_encode(const kv_cache* cc, int64_t n_vecs, const float* src, int32_t is_key, void* dst, void* stream) {
+  kv_cache* c = const_cast<kv_cache*>(cc);
+  if (!c) return KV_EINVAL;
+  if (c->core.params().format != KV_TQ3) return set_err(c, KV_EINVAL, "kv_encode needs a KV_TQ3 handle");
+  if (n_vecs < 0) return set_err(c, KV_EINVAL, "n_vecs < 0");
+  if (n_vecs > 0 && (!src || !dst)) return set_err(c, KV_EINVAL, "null src / dst");
+  if (n_vecs > ((int64_t)1 << 33)) return set_err(c, KV_EINVAL, "n_vecs too large");
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  const Codec& cd = c->core.codec();
+  EncodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src = src;
+  a.dst = static_cast<uint8_t*>(dst);
+  a.n = n_vecs;
+  a.d = c->core.params().head_dim;
+  a.is_key = is_key ? 1 : 0;
+  a.signs = c->dsigns;
+  a.s_t = c->ds_t;
+  for (int j = 0; j < 7; ++j) a.thr[j] = cd.thresholds[j];
+  for (int j = 0; j < 8; ++j) a.lev16[j] = cd.levels16[j];
+  a.status = c->dstatus;
+  hipError_t e = launch_encode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(c, e, "encode launch");
+  return KV_OK;
+}
+
+int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                       int32_t num_q_heads, int32_t window, size_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  VerifyPlan vp;
+  int rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp, &const_cast<kv_cache*>(c)->err);
+  if (rc != KV_OK) return rc;
+  *out = vp.total;
+  return KV_OK;
+}
+
+int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const float* q,
+                     int32_t num_q_heads, float scale, float softcap, int32_t window, float* out, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  VerifyPlan vp;
+  rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp, &c->err);
+  if (rc != KV_OK) return rc;
+  if (!q || !out) return set_err(c, KV_EINVAL, "null q / out");
+  if (!std::isfinite(scale)) return set_err(c, KV_EINVAL, "scale must be finite");
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return set_err(c, KV_EINVAL, "softcap must be finite and >= 0");
+  if (ws_bytes < vp.total) return set_err(c, KV_ENOMEM, "workspace too small");
+  if (vp.total > 0 && (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign))
+    return set_err(c, KV_EINVAL, "workspace must be non-null and 256-byte aligned");
+  const CoreParams& P = c->core.params();
+  if (P.format == KV_TQ3) return set_err(c, KV_EINVAL, "KV_TQ3 attention not available in this build");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int g = num_q_heads / P.num_kv_heads;
+  int64_t qrow = 0;
+  for (const VerifyLaunch& L : vp.launches) {
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = c->pool;
+    a.table = c->dtable;
+    a.q = q;
+    a.out = out;
+    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace)) + L.slot0 * vp.slot_stride;
+    a.lay = c->lay;
+    a.hq = num_q_heads;
+    a.g = g;
+    a.max_bps = P.max_blocks_per_seq;
+    a.window = window;
+    a.scale = scale;
+    a.softcap = softcap;
+    a.inv_softcap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
+    a.n_seqs = L.count;
+    a.tiles_per_wg = L.tiles_per_wg;
+    a.total_tiles = L.total_tiles;
+    a.n_wg = L.n_wg;
+    a.slot_stride = (int32_t)vp.slot_stride;
+    a.rpad = vp.rpad;
+    a.force_partial = 0;
+    bool any_split = false;
+    for (int i = 0; i < L.count; ++i) {
+      const int sid = seq_ids[L.first + i];
+      int32_t len;
+      c->core.seq_len(sid, &len);
+      a.seq[i] = sid;
+      a.len[i] = len;
+      a.qrow0[i] = (int32_t)qrow;
+      a.nrows[i] = n_rows[L.first + i];
+      qrow += n_rows[L.first + i];
+      const int nt = (L.tile_base[i + 1] - L.tile_base[i]) / P.num_kv_heads;
+      for (int h = 0; h < P.num_kv_heads; ++h) {
+        const int first = L.tile_base[i] + h * nt;
+        if (first / L.tiles_per_wg != (first + nt - 1) / L.tiles_per_wg) any_split = true;
+      }
+    }
+    for (int i = 0; i <= L.count; ++i) a.tile_base[i] = L.tile_base[i];
+    hipError_t e = launch_attn(a, vp.nct, s);
+    if (e != hipSuccess) return hip_fail(c, e, "attention launch");
+    if (any_split) {
+      e = launch_merge(a, vp.nct, s);
+      if (e != hipSuccess) return hip_fail(c, e, "merge launch");
+    }
+  }
+  return KV_OK;
+}
+
+int kv_seq_len(const kv_cache* c, int32_t seq_id, int32_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  return c->core.seq_len(seq_id, out);
+}
+
+int kv_block_table(const kv_cache* c, int32_t seq_id, int32_t* out, int32_t cap, int32_t* n_owned) {
+  if (!c || !n_owned || cap < 0 || (cap > 0 && !out)) return KV_EINVAL;
+  int32_t owned;
+  int rc = c->core.owned(seq_id, &owned);
+  if (rc != KV_OK) return rc;
+  const int32_t* row = c->core.table_row(seq_id);
+  for (int i = 0; i < std::min(cap, owned); ++i) out[i] = row[i];
+  *n_owned = owned;
+  return KV_OK;
+}
+
+int kv_free_blocks(const kv_cache* c, int32_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  *out = c->core.free_count();
+  return KV_OK;
+}
+
+int kv_codec(const kv_cache* c, int8_t* signs, float* s_matrix, double* levels, double* levels16,
+             double* thresholds) {
+  if (!c) return KV_EINVAL;
+  if (c->core.params().format != KV_TQ3) return KV_EINVAL;
+  const Codec& cd = c->core.codec();
+  const int d = cd.d;
+  if (signs) std::memcpy(signs, cd.signs.data(), d);
+  if (s_matrix) std::memcpy(s_matrix, cd.s.data(), (size_t)d * d * 4);
+  if (levels) std::memcpy(levels, cd.levels, sizeof(cd.levels));
+  if (levels16) std::memcpy(levels16, cd.levels16, sizeof(cd.levels16));
+  if (thresholds) std::memcpy(thresholds, cd.thresholds, sizeof(cd.thresholds));
+  return KV_OK;
+}
+
+const char* kv_last_error(const kv_cache* c) { return c ? c->err.c_str() : "null handle"; }
+
+}  // extern "C"

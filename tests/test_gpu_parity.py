@@ -1,0 +1,231 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (written here, per the cache format): fp32 caches 1e-5 max abs
+error; bf16 caches 2e-3 max abs error.  Block tables, seq_len and stored
+bytes are compared bit for bit.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from parity import max_err, qoffsets, read_plain, require_gpu
+from speculative_verify_attention_amd import (KV_BF16, KV_EINVAL, KV_ENOMEM, KV_ENOSEQ, KV_ERANGE, KV_FP32, KVCache,
+                                              SvattnError, synth)
+from speculative_verify_attention_amd.runner import Runner
+
+pytestmark = pytest.mark.gpu
+
+TOL = {KV_FP32: 1e-5, KV_BF16: 2e-3}
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_check(wl, seqs=None, layers=None, scale_q=1.0, steps=(0,), check_steps=None):
+    r = Runner(wl, layers=layers, track=True)
+    r.fill()
+    worst = 0.0
+    for t in steps:
+        rows, q, outs = r.step(t, scale_q)
+        torch.cuda.synchronize()
+        if check_steps is None or t in check_steps:
+            for li, out in enumerate(outs):
+                e = max_err(r, rows, q, out, li, seqs if seqs is not None else range(wl.n_seqs))
+                worst = max(worst, e)
+    return r, worst
+
+
+# ---- the five workloads -----------------------------------------------------------
+
+
+def test_tiny_fp32():
+    banner("tiny fp32 256+5")
+    wl = synth.tiny()
+    _, err = run_and_check(wl)
+    assert err <= TOL[KV_FP32], err
+
+
+def test_tiny_append5_rollback3_equals_append2():
+    banner("tiny append-5/rollback-3 vs append-2")
+    wl = synth.tiny()
+    a, b = Runner(wl), Runner(wl)
+    a.fill()
+    b.fill()
+    k, v = synth.step_kv(wl, 0, 5, "cuda")
+    a.caches[0].append([0], [5], k, v)
+    a.caches[0].rollback(0, 3)
+    b.caches[0].append([0], [2], k[:2].contiguous(), v[:2].contiguous())
+    ca, cb = a.caches[0], b.caches[0]
+    assert ca.seq_len(0) == cb.seq_len(0) == 258
+    L = ca.seq_len(0)
+    assert ca.block_table(0)[: math.ceil(L / 256)] == cb.block_table(0)[: math.ceil(L / 256)]
+    ka, va = read_plain(ca, 0, L)
+    kb, vb = read_plain(cb, 0, L)
+    assert torch.equal(ka.view(torch.int32), kb.view(torch.int32))
+    assert torch.equal(va.view(torch.int32), vb.view(torch.int32))
+    q = synth.queries(wl, 0, 2, "cuda")
+    oa = ca.verify([0], [2], q, wl.hq, wl.scale)
+    ob = cb.verify([0], [2], q, wl.hq, wl.scale)
+    assert torch.equal(oa, ob)
+
+
+@pytest.mark.parametrize("fmt", [KV_FP32, KV_BF16])
+def test_pool_holds_appended_bits(fmt):
+    banner(f"stored bytes fmt={fmt}")
+    wl = synth.Workload("bytes", 8, 2, 128, fmt, [300, 513, 7], [3, 1, 5], seed=11, alloc_seed=3)
+    r = Runner(wl, track=True)
+    r.fill()
+    r.step(0)
+    torch.cuda.synchronize()
+    for s in range(wl.n_seqs):
+        L = r.caches[0].seq_len(s)
+        assert L == wl.prefill[s] + wl.rows[s]
+        k, v = read_plain(r.caches[0], s, L)
+        lk, lv = r.logical_kv(s)
+        assert np.array_equal(k.float().cpu().numpy(), lk)
+        assert np.array_equal(v.float().cpu().numpy(), lv)
+
+
+def test_qwen3_4b_reduced():
+    banner("qwen3-4b dense 3x1000")
+    wl = synth.qwen3_4b_dense(batch=3, ctx=1000)
+    _, err = run_and_check(wl)
+    assert err <= TOL[KV_BF16], err
+
+
+def test_qwen3_4b_full():
+    banner("qwen3-4b dense 16x4096 (bench launch shape)")
+    wl = synth.qwen3_4b_dense()
+    _, err = run_and_check(wl)
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+def test_gemma_interleaved_full():
+    banner("gemma 8x32768 window 512 + full, cap 50")
+    wl = synth.gemma_interleaved()
+    _, err = run_and_check(wl, layers=[(512, 50.0), (0, 50.0)])
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+def test_mixed_batch_steps():
+    banner("mixed batch 64 seqs, 20 steps with rollbacks, sampled sequences")
+    wl = synth.mixed_batch()
+    order = np.argsort(wl.prefill)
+    sample = sorted(set(order[:3].tolist() + order[-1:].tolist() + [7, 31]))
+    _, err = run_and_check(wl, seqs=sample, steps=range(20), check_steps={0, 19})
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+def test_bf16_long_context_sampled():
+    banner("bf16 4x100000, sampled sequence 1")
+    wl = synth.tq3_long(100000, fmt=KV_BF16)
+    _, err = run_and_check(wl, seqs=[1])
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+# ---- edge cases -----------------------------------------------------------------------
+
+
+EDGE = [
+    # name, hq, hkv, d, fmt, prefill, rows, window, cap, scale_q
+    ("plain_decode", 8, 2, 128, KV_BF16, [700, 64, 1], [1, 1, 1], 0, 0.0, 1.0),
+    ("max_rows", 8, 2, 64, KV_FP32, [300, 40], [8, 8], 0, 0.0, 1.0),
+    ("context_equals_rows", 4, 1, 64, KV_FP32, [0, 0], [5, 1], 0, 0.0, 1.0),
+    ("mha_g1", 4, 4, 128, KV_BF16, [333], [5], 0, 0.0, 1.0),
+    ("two_column_groups", 24, 2, 128, KV_BF16, [1000, 77], [5, 5], 0, 0.0, 1.0),
+    ("two_column_groups_fp32", 24, 2, 64, KV_FP32, [200, 5], [5, 2], 0, 0.0, 1.0),
+    ("window_1", 8, 2, 64, KV_FP32, [500], [5], 1, 0.0, 1.0),
+    ("window_ge_ctx", 8, 2, 128, KV_BF16, [400], [5], 100000, 0.0, 1.0),
+    ("window_ragged", 8, 1, 256, KV_BF16, [3000, 70], [5, 3], 100, 0.0, 1.0),
+    ("softcap_saturating", 8, 1, 256, KV_BF16, [900], [5], 0, 50.0, 20.0),
+    ("softcap_fp32", 8, 2, 64, KV_FP32, [600], [4], 0, 5.0, 3.0),
+    ("d256_fp32", 8, 2, 256, KV_FP32, [300], [5], 0, 0.0, 1.0),
+    ("d64_bf16", 16, 4, 64, KV_BF16, [5000, 1], [5, 1], 0, 0.0, 1.0),
+    ("many_seqs", 8, 2, 128, KV_BF16, [int(x) for x in np.linspace(1, 3000, 150)], [2] * 150, 0, 0.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge(case):
+    name, hq, hkv, d, fmt, prefill, rows, window, cap, scale_q = case
+    banner(f"edge {name}")
+    wl = synth.Workload(name, hq, hkv, d, fmt, prefill, rows, window=window, softcap=cap, seed=zlib.crc32(name.encode()) % 1000,
+                        alloc_seed=17)
+    _, err = run_and_check(wl, scale_q=scale_q)
+    assert err <= TOL[fmt], err
+
+
+def test_window_1_returns_own_value_exactly():
+    banner("window 1 exact")
+    wl = synth.Workload("w1", 8, 2, 64, KV_FP32, [260], [5], window=1, seed=5)
+    r = Runner(wl, track=True)
+    r.fill()
+    rows, q, (out,) = r.step(0)
+    k, v = r.logical_kv(0)
+    o = out.cpu().numpy()
+    for i in range(5):
+        for h in range(8):
+            assert np.array_equal(o[i, h], v[260 + i, h // 4])
+
+
+def test_deterministic():
+    banner("determinism")
+    wl = synth.qwen3_4b_dense(batch=4, ctx=2000)
+    r = Runner(wl)
+    r.fill()
+    rows, q, (o1,) = r.step(0)
+    o2 = r.verify(0, rows, q)
+    o3 = r.verify(0, rows, q)
+    assert torch.equal(o1, o2) and torch.equal(o2, o3)
+
+
+def test_errors_change_nothing():
+    banner("error returns")
+    wl = synth.Workload("err", 8, 2, 64, KV_BF16, [100, 3], [5, 5], seed=1)
+    r = Runner(wl)
+    r.fill()
+    c = r.caches[0]
+    q = synth.queries(wl, 0, 16, "cuda")
+    out = torch.zeros_like(q)
+    before = (c.seq_len(0), c.seq_len(1), c.block_table(0), c.free_blocks())
+
+    def code_of(fn):
+        with pytest.raises(SvattnError) as e:
+            fn()
+        return e.value.code
+
+    assert code_of(lambda: c.verify([0, 1], [5, 11], q, 8, 0.1, out=out)) == KV_EINVAL  # > KV_MAX_ROWS rows
+    assert code_of(lambda: c.verify([0, 1], [5, 5], q, 8, 0.1, out=out)) == KV_ERANGE  # 5 rows, 3 positions
+    assert code_of(lambda: c.verify([0, 9], [5, 2], q, 8, 0.1, out=out)) == KV_ENOSEQ
+    q7 = torch.zeros((16, 7, 64), device="cuda")
+    assert code_of(lambda: c.verify([0], [5], q7, 7, 0.1, out=torch.zeros_like(q7))) == KV_EINVAL  # 7 % 2 != 0
+    small_ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    assert code_of(lambda: c.verify([0], [5], q, 8, 0.1, out=out, workspace=small_ws)) == KV_ENOMEM
+    assert code_of(lambda: c.verify([0], [5], q, 8, float("nan"), out=out)) == KV_EINVAL
+    assert code_of(lambda: c.verify([0], [5], q, 8, 0.1, softcap=-1.0, out=out)) == KV_EINVAL
+    assert code_of(lambda: c.verify([0], [5], q, 8, 0.1, window=-3, out=out)) == KV_EINVAL
+    assert code_of(lambda: c.rollback(1, 4)) == KV_ERANGE
+    assert code_of(lambda: c.rollback(1, -1)) == KV_EINVAL
+    assert code_of(lambda: c.rollback(5, 1)) == KV_ENOSEQ
+    big = torch.zeros((10000, 2, 64), dtype=torch.bfloat16, device="cuda")
+    assert code_of(lambda: c.append([1], [10000], big, big)) in (KV_ENOMEM, KV_ERANGE)
+    assert code_of(lambda: c.append([0, 0], [1, 1], big, big)) == KV_EINVAL
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    assert (c.seq_len(0), c.seq_len(1), c.block_table(0), c.free_blocks()) == before
