@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: roll back the previous
+step's draft rows (host, O(1) per sequence), append the new rows into their
+blocks (quantize-on-append for compressed caches), and run the verify
+attention (partials + merge).  Steps rotate over enough independent layer
+caches (>= 1 GiB in all) that the 256 MB Infinity Cache cannot hold the
+working set, as successive layers of a model would.
+
+Reported: verified query-tokens/s (the metric's first half) as ``value``,
+effective KV GB/s and % of HBM peak, the attention kernel's roofline (its
+algorithmic bytes over its average duration, timed live with HIP events on
+the launch stream), and the fp64 CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified query-tokens/s + effective KV GB/s (% HBM peak), spec-verify attention"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "speculative_verify_attention_amd", "csrc", "attn.hip")
+
+
+def workloads():
+    from speculative_verify_attention_amd import synth
+
+    return {
+        "tiny": lambda: (synth.tiny(), None),
+        "qwen3_4b_dense": lambda: (synth.qwen3_4b_dense(), None),
+        "gemma_interleaved": lambda: (synth.gemma_interleaved(), [(512, 50.0), (0, 50.0)]),
+        "tq3_512": lambda: (synth.tq3_long(512), None),
+        "tq3_40000": lambda: (synth.tq3_long(40000), None),
+        "tq3_100000": lambda: (synth.tq3_long(100000), None),
+        "bf16_100000": lambda: (synth.tq3_long(100000, fmt=synth.KV_BF16), None),
+        "mixed_batch": lambda: (synth.mixed_batch(), None),
+    }
+
+
+def describe(name, wl, layers):
+    kv = {0: "fp32", 1: "bf16", 2: "tq3 (3-bit Lloyd-Max + QJL keys, 3-bit values)"}[wl.fmt]
+    lens = sorted(set(wl.prefill))
+    ctx = f"{lens[0]}" if len(lens) == 1 else f"{min(lens)}..{max(lens)} (log-uniform)"
+    lay = ", ".join(f"window={w or 'full'} cap={c or 'off'}" for w, c in layers)
+    return (f"{name}: {wl.n_seqs} seqs, context {ctx} + drafts, Hq={wl.hq} Hkv={wl.hkv} d={wl.d}, {kv} KV in "
+            f"256-token blocks, rows {'1..5 per seq' if wl.vary_rows else wl.rows[0]}, layers [{lay}]")
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        assert rc == 0, rc
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.dirname(ATTN_SRC))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(os.path.dirname(ATTN_SRC), f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, layers, budget_s=10.0):
+    """The fp64 oracle on this host: whole verify calls for single sequences
+    of the workload (all rows and heads), repeated until budget_s passes."""
+    import numpy as np
+    import torch
+
+    from oracle import attention as A
+    from speculative_verify_attention_amd import synth
+    from speculative_verify_attention_amd.runner import alg_bytes_per_call
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:
+        threads = 1
+    window, cap = max(layers, key=lambda x: x[0] == 0)  # the full-attention layer if any
+    s = int(np.argmin(wl.prefill))  # the shortest sequence keeps the sample bounded
+    L = wl.prefill[s]
+    n = wl.rows[s]
+    k, v = synth.prefill_kv(wl, s, 0, L, "cpu")
+    k2, v2 = synth.step_kv(wl, 0, n, "cpu")
+    k = torch.cat([k, k2]).float().numpy().astype(np.float64)
+    v = torch.cat([v, v2]).float().numpy().astype(np.float64)
+    q = synth.queries(wl, 0, n, "cpu").numpy().astype(np.float64)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        A.verify_attention(q, k, v, wl.scale, cap, window)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    byt = alg_bytes_per_call(wl, [n], [L + n], window) * calls
+    return {
+        "value": round(n * calls / el, 3),
+        "unit": "verified query-tokens/s",
+        "kv_gbs": round(byt / el / 1e9, 4),
+        "cores": threads,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"sequence {s} of the workload (context {L}+{n}, {n} rows x {wl.hq} heads), one verify call "
+                  f"repeated {calls} times in {el:.1f} s",
+    }
+
+
+def run(args, name):
+    import torch
+
+    from speculative_verify_attention_amd import synth
+    from speculative_verify_attention_amd.runner import Runner, alg_bytes_per_call
+
+    wl, layers = workloads()[name]()
+    layers = layers or [(wl.window, wl.softcap)]
+    total_steps = args.warmup + args.steps
+    wl.steps = total_steps  # room in the tables for every step's growth
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    # bytes one layer's cache holds at verify time (stored format)
+    per_layer = sum(alg_bytes_per_call(wl, [1], [L + 8], 0) for L in wl.prefill)
+    reps = max(1, math.ceil((1 << 30) / max(1, per_layer * len(layers))))
+    runners = []
+    for _ in range(reps):
+        r = Runner(wl, layers=layers, device=dev)
+        r.fill()
+        runners.append(r)
+    # the steps' plans and inputs, generated before timing
+    varying = wl.vary_rows or wl.rollback_max
+    n_plans = 20 if varying else 1
+    plans = [synth.step_plan(wl, t) for t in range(n_plans)]
+    inputs = []
+    for t, (rb, rows) in enumerate(plans):
+        k, v = synth.step_kv(wl, t, sum(rows), dev)
+        q = synth.queries(wl, t, sum(rows), dev)
+        inputs.append((k, v, q, torch.empty_like(q)))
+    seqs = list(range(wl.n_seqs))
+    # one workspace per (replica, layer): the partial-slot count is bounded by
+    # the workgroup target plus the (sequence, kv head) pairs, whatever the lengths
+    ws_need = max(runners[0].caches[li].workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq, layers[li][0])
+                  for li in range(len(layers)))
+    ws = [[torch.empty(2 * ws_need, dtype=torch.uint8, device=dev) for _ in layers] for _ in range(reps)]
+    hip = Hip()
+    dom = max(range(len(layers)), key=lambda i: layers[i][0] == 0)  # dominant layer: full attention
+    ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    lens = [list(wl.prefill) for _ in range(reps)]  # host-side mirror of seq_len per replica
+    last_rows = [None] * reps
+    step_bytes = []
+
+    def step(i, timed_idx):
+        rep = i % reps
+        r = runners[rep]
+        t = i % n_plans
+        rb, rows = plans[t]
+        k, v, q, out = inputs[t]
+        if varying:
+            back = list(rb)
+        else:  # all drafts of this layer's previous step are rejected: the cache returns to its prefill
+            back = list(last_rows[rep]) if last_rows[rep] is not None else [0] * wl.n_seqs
+        if any(back):
+            for c in r.caches:
+                c.rollback_batch(seqs, back)
+        for c in r.caches:
+            c.append(seqs, rows, k, v)
+        lens[rep] = [L - b + n for L, b, n in zip(lens[rep], back, rows)]
+        for li, c in enumerate(r.caches):
+            if li == dom and timed_idx is not None:
+                c.trace_events(*ev[timed_idx])
+            c.verify(seqs, rows, q, wl.hq, wl.scale, layers[li][1], layers[li][0], out=out, workspace=ws[rep][li])
+            if li == dom and timed_idx is not None:
+                c.trace_events(None, None)
+        last_rows[rep] = rows
+        if timed_idx is not None:
+            step_bytes.append([alg_bytes_per_call(wl, rows, lens[rep], w) for w, _ in layers])
+        return rows
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    tok = 0
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        tok += sum(step(args.warmup + j, j))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # sanity: the host mirror of the lengths matches the library's
+    for rep in range(reps):
+        assert lens[rep] == [runners[rep].caches[0].seq_len(s) for s in seqs]
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    dom_bytes_avg = sum(b[dom] for b in step_bytes) / len(step_bytes)
+    byt = sum(sum(b) for b in step_bytes)
+    ms_per_step = el * 1e3 / args.steps
+    value = tok / el
+    kv_gbs = byt / el / 1e9
+    achieved = dom_bytes_avg / (kern_avg * 1e-3) / 1e9
+    traffic = load_traffic(name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "verified query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "f32", 1: "bf16", 2: "f16"}[wl.fmt],
+        "data": "synthetic",
+        "config": {"workload": describe(name, wl, layers), "layer_replicas": reps,
+                   "step": "rollback previous drafts + append new rows + verify attention (partials + merge)"},
+        "effective_kv_gbs": round(kv_gbs, 2),
+        "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": round(dom_bytes_avg),
+            "avg_launch_ms": round(kern_avg, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, layers)
+    return res
+
+
+def copy_probe(nbytes=1 << 30):
+    """A plain device-to-device copy of known size (for scaling the HBM
+    byte counters)."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB plain copy first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+    res = run(args, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

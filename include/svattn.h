@@ -86,15 +86,24 @@ typedef struct {
  * by the library's metadata: the device block table and, for KV_TQ3, the
  * codec constants).  p->pool and p->pool_bytes are ignored.
  *
- * Block layout (per block, per kv head h, d = head_dim; all offsets are in
- * the block's region, heads stored one after another):
- *  KV_FP32 / KV_BF16 (e = 4 or 2 bytes): K as [256 tokens][d]; V as
- *    [4 sub-tiles of 64 tokens][d][64 tokens] (token-minor inside a sub-tile).
- *  KV_TQ3: K codes as [256][d/2] bytes, dimension i in nibble i (low nibble
- *    first) holding code | sign_bit << 3; K norms n16 as [256] fp16; K
- *    residual norms g16 as [256] fp16; V codes as [4][d][24 bytes], the 24
- *    bytes holding 64 tokens' 3-bit codes, token t at bits 3t..3t+2
- *    (little-endian bit order); V norms as [256] fp16.
+ * Block layout.  A block holds 256 token positions of every kv head: first
+ * each head's K region in head order, then each head's V region.  d =
+ * head_dim; m = token within a 32-token sub-tile; a region is 8 sub-tiles.
+ *  KV_BF16 (2-byte elements), per sub-tile:
+ *    K as [d/16][2][32][8]:       element (kk, h, m, e) = K[m][16kk + 8h + e]
+ *    V as [2][d/32][2][32][8]:    element (v, dt, h, r, e) =
+ *                                 V[16v + 8(e>>2) + 4h + (e&3)][32dt + r]
+ *  KV_FP32 (4-byte elements), per sub-tile:
+ *    K as [d/8][2][32][4]:        element (kq, h, m, e) = K[m][(d/2)h + 4kq + e]
+ *    V as [4][d/32][2][32][4]:    element (uq, dt, h, r, e) = V[8uq + 4h + e][32dt + r]
+ *  (this order makes every wavefront-wide load of the attention kernel read
+ *  1 KiB of contiguous memory straight into its matrix-core operands).
+ *  KV_TQ3 (per kv head, heads one after another inside each field): K codes
+ *    as [256][d/2] bytes, dimension i in nibble i (low nibble first) holding
+ *    code | sign_bit << 3; K norms n16 as [256] fp16; K residual norms g16 as
+ *    [256] fp16; V codes as [4][d][24 bytes], the 24 bytes holding 64 tokens'
+ *    3-bit codes, token t at bits 3t..3t+2 (little-endian bit order); V norms
+ *    as [256] fp16.
  */
 int kv_pool_bytes(const kv_params* p, size_t* out);
 
@@ -134,6 +143,13 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
  * Errors: KV_ENOSEQ, KV_EINVAL (n_tokens < 0), KV_ERANGE (n_tokens > seq_len).
  */
 int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens);
+
+/*
+ * kv_rollback for several sequences in one call, all-or-nothing: every entry
+ * is validated first (errors as kv_rollback; a repeated id is KV_EINVAL) and
+ * nothing changes unless all are valid.  seq_ids, n_tokens: host arrays.
+ */
+int kv_rollback_batch(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens);
 
 /* Release every block of a sequence (pushed back onto the front of the free
  * list, first-owned block first) and reset its length to 0.  The caller must
@@ -194,6 +210,15 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
 int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                      const float* q, int32_t num_q_heads, float scale, float softcap,
                      int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Tracing: while set, every spec_verify_attn call records event `before` on
+ * its stream just before its first attention-partial kernel and `after` just
+ * after its last one (hipEvent_t handles passed as void*, owned by the
+ * caller), so that hipEventElapsedTime gives the partial kernels' time
+ * without the merge.  Passing NULL for both stops the recording.
+ */
+int kv_trace_events(kv_cache* c, void* before, void* after);
 
 /* ---- introspection (host only; never touches the device) ---- */
 

@@ -36,6 +36,8 @@ from ._binding import (  # noqa: F401
     kv_pool_bytes,
     kv_record_bytes,
     kv_rollback,
+    kv_rollback_batch,
+    kv_trace_events,
     kv_seq_free,
     kv_seq_len,
     kv_workspace_bytes,

@@ -73,6 +73,8 @@ _SIGS = {
     "kv_destroy": [_p],
     "kv_append": [_p, _i32, _i32p, _i32p, _p, _p, _p],
     "kv_rollback": [_p, _i32, _i32],
+    "kv_rollback_batch": [_p, _i32, _i32p, _i32p],
+    "kv_trace_events": [_p, _p, _p],
     "kv_seq_free": [_p, _i32],
     "kv_encode": [_p, _i64, _p, _i32, _p, _p],
     "kv_record_bytes": [_i32, _i32, _i32p],
@@ -181,6 +183,15 @@ def kv_append(h, seq_ids, n_new, k, v, stream=None):
 
 def kv_rollback(h, seq_id, n_tokens):
     return lib().kv_rollback(h, seq_id, n_tokens)
+
+
+def kv_rollback_batch(h, seq_ids, n_tokens):
+    return lib().kv_rollback_batch(h, len(seq_ids), _arr(seq_ids), _arr(n_tokens))
+
+
+def kv_trace_events(h, before, after):
+    """before/after: raw hipEvent_t handles (ints) or None."""
+    return lib().kv_trace_events(h, ctypes.c_void_p(before or 0), ctypes.c_void_p(after or 0))
 
 
 def kv_seq_free(h, seq_id):
@@ -297,6 +308,12 @@ class KVCache:
 
     def rollback(self, seq_id, n_tokens):
         return _check(kv_rollback(self.handle, seq_id, n_tokens), self.handle)
+
+    def rollback_batch(self, seq_ids, n_tokens):
+        return _check(kv_rollback_batch(self.handle, seq_ids, n_tokens), self.handle)
+
+    def trace_events(self, before, after):
+        return _check(kv_trace_events(self.handle, before, after), self.handle)
 
     def seq_free(self, seq_id):
         return _check(kv_seq_free(self.handle, seq_id), self.handle)

@@ -226,7 +226,7 @@ __device__ inline void store_half(uint8_t* p, uint16_t h) {
 
 // ---- plain slice-update ----------------------------------------------------------
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
   const int unit = blockIdx.x;  // one source row
   const int h = blockIdx.y;
@@ -238,13 +238,13 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (pos >> 8)];
   const int slot = pos & 255;
   uint8_t* base = a.pool + (int64_t)block * a.lay.block_bytes;
-  T* kdst = reinterpret_cast<T*>(base + a.lay.k_off) + ((int64_t)h * 256 + slot) * d;
-  T* vdst = reinterpret_cast<T*>(base + a.lay.v_off) + ((int64_t)h * 4 + (slot >> 6)) * d * 64 + (slot & 63);
+  T* kdst = reinterpret_cast<T*>(base + a.lay.k_off) + (int64_t)h * 256 * d;
+  T* vdst = reinterpret_cast<T*>(base + a.lay.v_off) + (int64_t)h * 256 * d;
   const T* ksrc = reinterpret_cast<const T*>(a.k) + (src_row * a.lay.hkv + h) * d;
   const T* vsrc = reinterpret_cast<const T*>(a.v) + (src_row * a.lay.hkv + h) * d;
   for (int e = threadIdx.x; e < d; e += 64) {
-    kdst[e] = ksrc[e];
-    vdst[(int64_t)e * 64] = vsrc[e];
+    kdst[plain_k_index(FMT, d, slot, e)] = ksrc[e];
+    vdst[plain_v_index(FMT, d, slot, e)] = vsrc[e];
   }
 }
 
@@ -322,9 +322,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.total_units <= 0) return hipSuccess;
   dim3 grid(a.total_units, a.lay.hkv);
   if (a.lay.fmt == 0) {
-    hipLaunchKernelGGL(append_plain_kernel<float>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((append_plain_kernel<float, 0>), grid, dim3(64), 0, s, a);
   } else if (a.lay.fmt == 1) {
-    hipLaunchKernelGGL(append_plain_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((append_plain_kernel<uint16_t, 1>), grid, dim3(64), 0, s, a);
   } else {
     switch (a.lay.d) {
       case 64:

@@ -39,158 +39,211 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define NEG_INF (-__builtin_inff())
 
-// Key (0..63) of the tile held by MFMA row m (0..31) of QK sub-tile st.
-__device__ __forceinline__ int key_of_row(int st, int m) {
-  return 32 * st + 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
-}
-// Key (0..63) of score register r (0..15) of sub-tile st in half-wave hh.
-__device__ __forceinline__ int key_of_reg(int st, int r, int hh) {
-  return 32 * st + 16 * (r >> 3) + 8 * hh + (r & 7);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int FMT>
-struct Elem;
-template <>
-struct Elem<0> {
-  using T = float;
-  static constexpr int bytes = 4;
-};
-template <>
-struct Elem<1> {
-  using T = uint16_t;
-  static constexpr int bytes = 2;
-};
+// tanh without branches, for the soft cap: an odd Taylor polynomial below
+// |x| = 0.55 (truncation below 2e-7 relative there) and 1 - 2 / (e^{2|x|} + 1)
+// above, where the subtraction loses no more than a few ulp.
+__device__ __forceinline__ float tanh_nb(float x) {
+  const float ax = fabsf(x);
+  const float x2 = x * x;
+  float p = 929569.0f / 638512875.0f;
+  p = fmaf(p, x2, -21844.0f / 6081075.0f);
+  p = fmaf(p, x2, 1382.0f / 155925.0f);
+  p = fmaf(p, x2, -62.0f / 2835.0f);
+  p = fmaf(p, x2, 17.0f / 315.0f);
+  p = fmaf(p, x2, -2.0f / 15.0f);
+  p = fmaf(p, x2, 1.0f / 3.0f);
+  const float small = fmaf(-x * x2, p, x);
+  const float e = fast_exp2(ax * 2.8853900817779268f);  // e^{2|x|}
+  const float big = copysignf(1.0f - 2.0f / (e + 1.0f), x);
+  return ax < 0.55f ? small : big;
+}
 
-// Per-lane state of one column of the online softmax.
+// ---- per-format traits ---------------------------------------------------------------
+//
+// A tile is NSUB sub-tiles of 32 keys.  A sub-tile's K and V occupy LK and LV
+// wave-wide 1 KiB loads (lane l reads 16 bytes at 16 l), laid out so the
+// registers each lane receives are exactly its MFMA operand fragments.
+
+template <int FMT, int D>
+struct Tr;
 template <int D>
-struct ColState {
-  static constexpr int NDT = D / 32;
-  float m;  // running max (log2 units), same in both half-waves
-  float l;  // running sum of this lane's keys
-  f32x16_t acc[NDT];
+struct Tr<1, D> {  // bf16: v_mfma_f32_32x32x16_bf16
+  static constexpr int NSUB = 128 / D > 1 ? 128 / D : 1;
+  static constexpr int LK = D / 16;  // k-steps of QK
+  static constexpr int LV = D / 16;  // 2 PV k-steps x D/32 output tiles
+};
+template <int D>
+struct Tr<0, D> {  // fp32: v_mfma_f32_32x32x2f32
+  static constexpr int NSUB = 1;
+  static constexpr int LK = D / 8;  // groups of 4 QK k-steps
+  static constexpr int LV = D / 8;  // 4 groups of 4 PV k-steps x D/32 output tiles
 };
 
-// ---- QK and PV for the plain formats -------------------------------------------
+// One tile of raw operand registers.
+template <int FMT, int D>
+struct TileRegs {
+  using T = Tr<FMT, D>;
+  u32x4_t k[T::NSUB][T::LK];
+  u32x4_t v[T::NSUB][T::LV];
+};
 
-// Query operand of one lane (column c, half hh).
+template <int FMT, int D>
+__device__ __forceinline__ void load_tile(TileRegs<FMT, D>& b, const uint8_t* __restrict__ kbase,
+                                          const uint8_t* __restrict__ vbase, int lane) {
+  using T = Tr<FMT, D>;
+  constexpr int SUB_BYTES = 32 * D * (FMT == 1 ? 2 : 4);
+#pragma unroll
+  for (int st = 0; st < T::NSUB; ++st) {
+#pragma unroll
+    for (int j = 0; j < T::LK; ++j)
+      b.k[st][j] = *reinterpret_cast<const u32x4_t*>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < T::LV; ++j)
+      b.v[st][j] = *reinterpret_cast<const u32x4_t*>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
+  }
+}
+
+// Query operand of one lane (column c, half-wave hh).
 template <int FMT, int D>
 struct QOperand;
 
 template <int D>
-struct QOperand<1, D> {  // bf16: k-step kk holds dims 16kk + 8hh .. +8
+struct QOperand<1, D> {  // k-step kk holds dims 16kk + 8hh .. +8
   bf16x8_t v[D / 16];
-  __device__ void load(const float* q, bool ok, int hh) {
+  __device__ __forceinline__ void load(const float* q, int hh) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[kk][e] = (__bf16)(ok ? q[16 * kk + 8 * hh + e] : 0.0f);
-    }
-  }
-};
-
-template <int D>
-struct QOperand<0, D> {  // fp32: k-step kk holds dim (D/2)*hh + kk
-  float v[D / 2];
-  __device__ void load(const float* q, bool ok, int hh) {
-#pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) v[kk] = ok ? q[(D / 2) * hh + kk] : 0.0f;
-  }
-};
-
-// S^T for sub-tile st of the tile at kt (K rows [64][D]).
-template <int D>
-__device__ __forceinline__ f32x16_t qk_subtile(const QOperand<1, D>& q, const uint16_t* __restrict__ kt, int st,
-                                               int lane) {
-  const int m = lane & 31, ha = lane >> 5;
-  const uint16_t* row = kt + key_of_row(st, m) * D + 8 * ha;
-  bf16x8_t kop[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) kop[kk] = *reinterpret_cast<const bf16x8_t*>(row + 16 * kk);
-  f32x16_t s = {};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], q.v[kk], s, 0, 0, 0);
-  return s;
-}
-
-template <int D>
-__device__ __forceinline__ f32x16_t qk_subtile(const QOperand<0, D>& q, const float* __restrict__ kt, int st,
-                                               int lane) {
-  const int m = lane & 31, ha = lane >> 5;
-  const float* row = kt + key_of_row(st, m) * D + (D / 2) * ha;
-  f32x16_t s = {};
-#pragma unroll
-  for (int kk = 0; kk < D / 2; kk += 4) {
-    f32x4_t k4 = *reinterpret_cast<const f32x4_t*>(row + kk);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4[e], q.v[kk + e], s, 0, 0, 0);
-  }
-  return s;
-}
-
-// O^T += V^T P^T for a 64-key tile; vt = V sub-tile [D][64]; p = probabilities
-// in score-register order; nvalid = keys of the tile below seq_len (64 if all).
-template <int D>
-__device__ __forceinline__ void pv_tile(ColState<D>& st, const uint16_t* __restrict__ vt, const float (&p)[2][16],
-                                        int lane, int nvalid) {
-  const int dr = lane & 31, ha = lane >> 5;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    // P = hi + lo, both bf16: the residual of a float after rounding to bf16
-    // is exact in fp32, so hi + lo carries P to about 2^-17 relative, and the
-    // product with the bf16 values is accumulated in fp32 by the MFMA.
-    bf16x8_t phi, plo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = p[u >> 1][8 * (u & 1) + e];
-      const __bf16 h = (__bf16)x;
-      phi[e] = h;
-      plo[e] = (__bf16)(x - (float)h);
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const uint16_t* src = vt + (32 * dt + dr) * 64 + 16 * u + 8 * ha;
-      u16x8_t raw = *reinterpret_cast<const u16x8_t*>(src);
-      if (nvalid < 64) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (16 * u + 8 * ha + e >= nvalid) raw[e] = 0;
-      }
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, raw);
-      st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, st.acc[dt], 0, 0, 0);
-      st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo, st.acc[dt], 0, 0, 0);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void pv_tile(ColState<D>& st, const float* __restrict__ vt, const float (&p)[2][16],
-                                        int lane, int nvalid) {
-  const int dr = lane & 31, ha = lane >> 5;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const float* rowp = vt + (32 * dt + dr) * 64;
-#pragma unroll
-    for (int u4 = 0; u4 < 32; u4 += 4) {
-      // keys of u = u4..u4+3 for half ha: 32(u>>4) + 16((u>>3)&1) + 8ha + (u&7)
-      const int kbase = 32 * (u4 >> 4) + 16 * ((u4 >> 3) & 1) + 8 * ha + (u4 & 7);
-      f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(rowp + kbase);
-      if (nvalid < 64) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (kbase + e >= nvalid) v4[e] = 0.0f;
-      }
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int u = u4 + e;
-        st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v4[e], p[u >> 4][u & 15], st.acc[dt], 0, 0, 0);
+        v[kk][e] = (__bf16)a[e];
+        v[kk][4 + e] = (__bf16)b[e];
       }
     }
   }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) v[kk] = bf16x8_t{};
+  }
+};
+
+template <int D>
+struct QOperand<0, D> {  // k-step kk holds dim (D/2) hh + kk
+  float v[D / 2];
+  __device__ __forceinline__ void load(const float* q, int hh) {
+#pragma unroll
+    for (int kk = 0; kk < D / 2; kk += 4) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + (D / 2) * hh + kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[kk + e] = a[e];
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) v[kk] = 0.0f;
+  }
+};
+
+// S^T of sub-tile st: lane (column c, half hh) gets the scores of keys
+// 8(r>>2) + 4hh + (r&3), r = 0..15.
+template <int D>
+__device__ __forceinline__ f32x16_t qk_sub(const QOperand<1, D>& q, const TileRegs<1, D>& b, int st) {
+  f32x16_t s = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.k[st][kk]), q.v[kk], s, 0, 0, 0);
+  return s;
+}
+template <int D>
+__device__ __forceinline__ f32x16_t qk_sub(const QOperand<0, D>& q, const TileRegs<0, D>& b, int st) {
+  f32x16_t s = {};
+#pragma unroll
+  for (int kq = 0; kq < D / 8; ++kq) {
+    const f32x4_t k4 = __builtin_bit_cast(f32x4_t, b.k[st][kq]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k4[e], q.v[4 * kq + e], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// Zero the V fragments of keys at or beyond nvalid (only in the last tile of a
+// sequence, where never-written slots may hold arbitrary bits).
+template <int D>
+__device__ __forceinline__ void mask_v(TileRegs<1, D>& b, int nvalid, int ha) {
+#pragma unroll
+  for (int st = 0; st < Tr<1, D>::NSUB; ++st)
+#pragma unroll
+    for (int j = 0; j < Tr<1, D>::LV; ++j) {
+      const int v = j / (D / 32);
+      u16x8_t x = __builtin_bit_cast(u16x8_t, b.v[st][j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (32 * st + 16 * v + 8 * (e >> 2) + 4 * ha + (e & 3) >= nvalid) x[e] = 0;
+      b.v[st][j] = __builtin_bit_cast(u32x4_t, x);
+    }
+}
+template <int D>
+__device__ __forceinline__ void mask_v(TileRegs<0, D>& b, int nvalid, int ha) {
+#pragma unroll
+  for (int st = 0; st < Tr<0, D>::NSUB; ++st)
+#pragma unroll
+    for (int j = 0; j < Tr<0, D>::LV; ++j) {
+      const int uq = j / (D / 32);
+      f32x4_t x = __builtin_bit_cast(f32x4_t, b.v[st][j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (32 * st + 8 * uq + 4 * ha + e >= nvalid) x[e] = 0.0f;
+      b.v[st][j] = __builtin_bit_cast(u32x4_t, x);
+    }
+}
+
+// O^T += V^T P^T for one tile; p holds the probabilities in score-register
+// order.  bf16: P = hi + lo (two bf16 parts; the residual of a float after
+// rounding to bf16 is exact in fp32), so the product keeps P to ~2^-17.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const TileRegs<1, D>& b,
+                                        const float (&p)[Tr<1, D>::NSUB][16]) {
+#pragma unroll
+  for (int st = 0; st < Tr<1, D>::NSUB; ++st)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      bf16x8_t phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = p[st][8 * v + e];
+        const __bf16 h = (__bf16)x;
+        phi[e] = h;
+        plo[e] = (__bf16)(x - (float)h);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, b.v[st][v * (D / 32) + dt]);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo, acc[dt], 0, 0, 0);
+      }
+    }
+}
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const TileRegs<0, D>& b,
+                                        const float (&p)[Tr<0, D>::NSUB][16]) {
+#pragma unroll
+  for (int st = 0; st < Tr<0, D>::NSUB; ++st)
+#pragma unroll
+    for (int uq = 0; uq < 4; ++uq)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const f32x4_t v4 = __builtin_bit_cast(f32x4_t, b.v[st][uq * (D / 32) + dt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v4[e], p[st][4 * uq + e], acc[dt], 0, 0, 0);
+      }
 }
 
 // ---- the partial kernel ----------------------------------------------------------
@@ -207,11 +260,85 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int n, int f) {
   return lo;
 }
 
-template <int FMT, int D, int NCT>
+// Online-softmax state of one lane: column c's running reference max m (log2
+// units, equal in both half-waves), this lane's partial sum l, and its part
+// of the column's O^T accumulator.
+template <int D>
+struct ColState {
+  float m, l;
+  f32x16_t acc[D / 32];
+};
+
+template <int FMT, int D, bool CAP>
+__device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& b, const QOperand<FMT, D>& q,
+                                             const AttnArgs& a, int key0, int L, int n, int ppos, int lane) {
+  constexpr int NSUB = Tr<FMT, D>::NSUB;
+  constexpr int TK = 32 * NSUB;
+  const int hh = lane >> 5;
+  float p[NSUB][16];
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st) {
+    const f32x16_t s = qk_sub<D>(q, b, st);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r] * a.scale;
+      if constexpr (CAP) x = a.softcap * tanh_nb(x * a.inv_softcap);
+      p[st][r] = x * 1.4426950408889634f;  // log2(e): the softmax runs on exp2
+    }
+  }
+  // keys every row sees need no mask: all of the tile lies at or before the
+  // first row's position and inside the last row's window
+  const bool full = key0 + TK <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
+  if (!full) {
+    if (key0 + TK > L) mask_v<D>(b, L - key0, hh);
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kp = key0 + 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool vis = kp <= ppos && (a.window == 0 || ppos - kp < a.window);
+        p[st][r] = vis ? p[st][r] : NEG_INF;
+      }
+  }
+  float mt = NEG_INF;
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // move the reference only when the tile max exceeds it by more than 2^8,
+  // so probabilities stay below 256 and rescales are rare
+  const bool up = mt > cs.m + 8.0f;
+  if (__builtin_amdgcn_ballot_w64(up)) {
+    // lanes that move: alpha = 2^(m_old - m_new), 0 when nothing was seen yet;
+    // lanes that stay keep alpha = 1 (their m may still be -inf)
+    const float alpha = up ? fast_exp2(cs.m - mt) : 1.0f;
+    cs.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) cs.acc[dt] *= alpha;
+    cs.m = up ? mt : cs.m;
+  }
+  const float m_use = cs.m == NEG_INF ? 0.0f : cs.m;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(p[st][r] - m_use);
+      p[st][r] = e;
+      lsum += e;
+    }
+  cs.l += lsum;
+  pv_tile<D>(cs.acc, b, p);
+}
+
+template <int FMT, int D, int NCT, bool CAP>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  using T = typename Elem<FMT>::T;
   constexpr int TL = 4 / NCT;  // token lanes
   constexpr int NDT = D / 32;
+  constexpr int TK = 32 * Tr<FMT, D>::NSUB;
+  constexpr int E = FMT == 1 ? 2 : 4;
+  constexpr bool DB = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4 <= 64;  // double-buffer
   constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
   __shared__ float cbuf[NCT * (TL / 2) * CSTRIDE];
 
@@ -228,8 +355,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int s = find_seq(a.tile_base, a.n_seqs, f);
     const int L = a.len[s], n = a.nrows[s];
     const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
-    const int tlo = klo / kTileKeys;
-    const int nt = (L + kTileKeys - 1) / kTileKeys - tlo;
+    const int tlo = klo / TK;
+    const int nt = (L + TK - 1) / TK - tlo;
     const int rel = f - a.tile_base[s];
     const int h = rel / nt;
     const int pair_first = a.tile_base[s] + h * nt;
@@ -242,7 +369,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int ppos = L - n + row_i;  // position of this column's query row
 
     QOperand<FMT, D> qop;
-    qop.load(a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D, col_ok, hh);
+    if (col_ok)
+      qop.load(a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D, hh);
+    else
+      qop.zero();
 
     ColState<D> cs;
     cs.m = NEG_INF;
@@ -251,51 +381,45 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
 
     const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
-    for (int t = t_begin + tl; t < t_end; t += TL) {
-      const int key0 = (tlo + t) * kTileKeys;
-      const int blk = trow[key0 >> 8];
-      const uint8_t* bbase = a.pool + (int64_t)blk * a.lay.block_bytes;
-      const T* kt = reinterpret_cast<const T*>(bbase + a.lay.k_off) + ((int64_t)h * 256 + (key0 & 255)) * D;
-      const T* vt = reinterpret_cast<const T*>(bbase + a.lay.v_off) + ((int64_t)h * 4 + ((key0 & 255) >> 6)) * D * 64;
-
-      float p[2][16];
-      f32x16_t s0 = qk_subtile<D>(qop, kt, 0, lane);
-      f32x16_t s1 = qk_subtile<D>(qop, kt, 1, lane);
-      float mt = NEG_INF;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = st == 0 ? s0[r] : s1[r];
-          float sc = x * a.scale;
-          if (a.softcap > 0.0f) sc = a.softcap * tanhf(sc * a.inv_softcap);
-          sc *= 1.4426950408889634f;  // log2(e): the softmax runs on exp2
-          const int kp = key0 + key_of_reg(st, r, hh);
-          const bool vis = col_ok && kp <= ppos && (a.window == 0 || ppos - kp < a.window);
-          sc = vis ? sc : NEG_INF;
-          p[st][r] = sc;
-          mt = fmaxf(mt, sc);
+    const int64_t head_off = (int64_t)h * 256 * D * E;
+    auto bases = [&](int t, const uint8_t*& kb, const uint8_t*& vb) {
+      const int key0 = (tlo + t) * TK;
+      const uint8_t* blk = a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + head_off + (key0 & 255) * D * E;
+      kb = blk + a.lay.k_off;
+      vb = blk + a.lay.v_off;
+    };
+    const int cnt = t_begin + tl < t_end ? (t_end - t_begin - tl + TL - 1) / TL : 0;
+    TileRegs<FMT, D> b0;
+    if constexpr (DB) {
+      TileRegs<FMT, D> b1;
+      const uint8_t *kb, *vb;
+      if (cnt > 0) {
+        bases(t_begin + tl, kb, vb);
+        load_tile<FMT, D>(b0, kb, vb, lane);
+      }
+      for (int i = 0; i < cnt; i += 2) {
+        const int t0 = t_begin + tl + i * TL;
+        if (i + 1 < cnt) {
+          bases(t0 + TL, kb, vb);
+          load_tile<FMT, D>(b1, kb, vb, lane);
+        }
+        process_tile<FMT, D, CAP>(cs, b0, qop, a, (tlo + t0) * TK, L, n, ppos, lane);
+        if (i + 1 < cnt) {
+          if (i + 2 < cnt) {
+            bases(t0 + 2 * TL, kb, vb);
+            load_tile<FMT, D>(b0, kb, vb, lane);
+          }
+          process_tile<FMT, D, CAP>(cs, b1, qop, a, (tlo + t0 + TL) * TK, L, n, ppos, lane);
         }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(cs.m, mt);
-      const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-      const float alpha = fast_exp2(cs.m - m_use);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = fast_exp2(p[st][r] - m_use);
-          p[st][r] = e;
-          lsum += e;
-        }
+    } else {
+      for (int i = 0; i < cnt; ++i) {
+        const int t0 = t_begin + tl + i * TL;
+        const uint8_t *kb, *vb;
+        bases(t0, kb, vb);
+        load_tile<FMT, D>(b0, kb, vb, lane);
+        process_tile<FMT, D, CAP>(cs, b0, qop, a, (tlo + t0) * TK, L, n, ppos, lane);
       }
-      cs.l = cs.l * alpha + lsum;
-      cs.m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] *= alpha;
-      pv_tile<D>(cs, vt, p, lane, min(64, L - key0));
     }
 
     // ---- combine the token lanes of each column group through LDS ----
@@ -376,8 +500,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int s = pair / hkv, h = pair - s * hkv;
   const int L = a.len[s], n = a.nrows[s];
   const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
-  const int tlo = klo / kTileKeys;
-  const int nt = (L + kTileKeys - 1) / kTileKeys - tlo;
+  const int tlo = klo / a.tile_keys;
+  const int nt = (L + a.tile_keys - 1) / a.tile_keys - tlo;
   const int pair_first = a.tile_base[s] + h * nt;
   const int wg_lo = pair_first / a.tiles_per_wg;
   const int wg_hi = (pair_first + nt - 1) / a.tiles_per_wg;
@@ -408,10 +532,15 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 
 template <int FMT, int D>
 static hipError_t launch_attn_fd(const AttnArgs& a, int nct, hipStream_t s) {
-  if (nct == 1)
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 1>), dim3(a.n_wg), dim3(256), 0, s, a);
+  const bool cap = a.softcap > 0.0f;
+  if (nct == 1 && !cap)
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, false>), dim3(a.n_wg), dim3(256), 0, s, a);
+  else if (nct == 1)
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, true>), dim3(a.n_wg), dim3(256), 0, s, a);
+  else if (!cap)
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, false>), dim3(a.n_wg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 2>), dim3(a.n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, true>), dim3(a.n_wg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -12,10 +12,16 @@ namespace svattn {
 
 // ---- pool layout -------------------------------------------------------------
 //
-// One block holds 256 token positions of every kv head.
-//  FP32/BF16 (e = element bytes):
-//    K: [hkv][256][d]                        at 0
-//    V: [hkv][4][d][64]                      at hkv*256*d*e
+// One block holds 256 token positions of every kv head; inside a block each
+// head's K region is followed by the other heads' K regions, then the V
+// regions.  The plain formats store each 32-token sub-tile in the order the
+// attention kernel's MFMA operands consume it, so that every wave-wide load
+// reads 1 KiB of contiguous memory (d = head_dim, sub-tile tokens m = 0..31):
+//  BF16 K sub-tile: [d/16][2][32][8]: (kk, h, m, e) = K[m][16kk + 8h + e]
+//  BF16 V sub-tile: [2][d/32][2][32][8]:
+//                   (v, dt, h, r, e) = V[16v + 8(e>>2) + 4h + (e&3)][32dt + r]
+//  FP32 K sub-tile: [d/8][2][32][4]: (kq, h, m, e) = K[m][(d/2)h + 4kq + e]
+//  FP32 V sub-tile: [4][d/32][2][32][4]: (uq, dt, h, r, e) = V[8uq + 4h + e][32dt + r]
 //  TQ3:
 //    K codes  [hkv][256][d/2]  (nibble = code | sign << 3, dim i in nibble i)
 //    K n16    [hkv][256]  fp16
@@ -29,6 +35,29 @@ struct PoolLayout {
   int64_t kc_off, kn_off, kg_off;  // TQ3
   int64_t vc_off, vn_off;          // TQ3
 };
+
+// Element offset of (token slot j in 0..255, dimension d) inside one head's
+// K or V region of a block, for the plain formats.
+__host__ __device__ inline int64_t plain_k_index(int fmt, int D, int j, int d) {
+  const int64_t sb = j >> 5, m = j & 31;
+  if (fmt == 1) return sb * 32 * D + (((d >> 4) * 2 + ((d >> 3) & 1)) * 32 + m) * 8 + (d & 7);
+  const int h = d / (D / 2), r = d % (D / 2);
+  return sb * 32 * D + (((r >> 2) * 2 + h) * 32 + m) * 4 + (r & 3);
+}
+__host__ __device__ inline int64_t plain_v_index(int fmt, int D, int j, int d) {
+  const int64_t sb = j >> 5;
+  const int t = j & 31, dt = d >> 5, dr = d & 31;
+  if (fmt == 1) {
+    const int v = t >> 4, rest = t & 15, h = (rest >> 2) & 1, e = 4 * (rest >> 3) + (rest & 3);
+    return sb * 32 * D + (((v * (D / 32) + dt) * 2 + h) * 32 + dr) * 8 + e;
+  }
+  const int uq = t >> 3, h = (t >> 2) & 1, e = t & 3;
+  return sb * 32 * D + (((uq * (D / 32) + dt) * 2 + h) * 32 + dr) * 4 + e;
+}
+
+// Keys per attention tile (one wavefront iteration): 16 KiB of bf16 K and V
+// at d <= 128, one 32-key sub-tile otherwise.
+constexpr int tile_keys(int fmt, int d) { return fmt == 1 ? 32 * (128 / d > 1 ? 128 / d : 1) : fmt == 0 ? 32 : 64; }
 
 PoolLayout make_layout(int fmt, int hkv, int d);
 
@@ -83,7 +112,6 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
 // ---- verify attention ------------------------------------------------------------
 constexpr int kMaxAttnSeqs = 128;
-constexpr int kTileKeys = 64;  // keys per wave iteration
 
 struct AttnArgs {
   const uint8_t* pool;
@@ -106,7 +134,7 @@ struct AttnArgs {
   int32_t slot_stride;    // floats per partial slot
   int32_t rpad;           // padded rows per slot (32 * NCT)
   int32_t force_partial;  // 1: every pair goes through the merge
-  int32_t pad0;
+  int32_t tile_keys;      // keys per tile (tile_keys(fmt, d))
   uint16_t lev16_bits[8];
   int32_t seq[kMaxAttnSeqs];
   int32_t len[kMaxAttnSeqs];

@@ -29,6 +29,7 @@ struct kv_cache {
   std::vector<int8_t> h_signs;
   std::vector<float> h_s_t;
   std::vector<uint32_t> h_zero;
+  hipEvent_t trace_before = nullptr, trace_after = nullptr;
   std::string err;
 };
 
@@ -143,7 +144,8 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
       c->core.seq_len(seq_ids[first + i], &len);
       const int n = n_rows[first + i];
       const int klo = window > 0 ? std::max(0, len - n - window + 1) : 0;
-      const int nt = (len + kTileKeys - 1) / kTileKeys - klo / kTileKeys;
+      const int tk = tile_keys(P.format, P.head_dim);
+      const int nt = (len + tk - 1) / tk - klo / tk;
       L.tile_base[i + 1] = L.tile_base[i] + nt * P.num_kv_heads;
     }
     L.total_tiles = L.tile_base[L.count];
@@ -315,6 +317,32 @@ int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens) {
   return c->core.rollback(seq_id, n_tokens, &c->err);
 }
 
+int kv_rollback_batch(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens) {
+  if (!c) return KV_EINVAL;
+  if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_tokens))) return set_err(c, KV_EINVAL, "bad arrays");
+  std::vector<char> seen(c->core.params().max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    if (!c->core.valid_seq(s)) return set_err(c, KV_ENOSEQ, "sequence id out of range");
+    if (seen[s]) return set_err(c, KV_EINVAL, "sequence id repeated");
+    seen[s] = 1;
+    if (n_tokens[i] < 0) return set_err(c, KV_EINVAL, "rollback count < 0");
+    int32_t len;
+    c->core.seq_len(s, &len);
+    if (n_tokens[i] > len) return set_err(c, KV_ERANGE, "rollback beyond seq_len");
+  }
+  for (int i = 0; i < n_seqs; ++i) c->core.rollback(seq_ids[i], n_tokens[i], &c->err);
+  return KV_OK;
+}
+
+int kv_trace_events(kv_cache* c, void* before, void* after) {
+  if (!c) return KV_EINVAL;
+  if ((before == nullptr) != (after == nullptr)) return set_err(c, KV_EINVAL, "set both events or neither");
+  c->trace_before = static_cast<hipEvent_t>(before);
+  c->trace_after = static_cast<hipEvent_t>(after);
+  return KV_OK;
+}
+
 int kv_seq_free(kv_cache* c, int32_t seq_id) {
   if (!c) return KV_EINVAL;
   return c->core.free_seq(seq_id, &c->err);
@@ -377,8 +405,11 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int g = num_q_heads / P.num_kv_heads;
   int64_t qrow = 0;
-  for (const VerifyLaunch& L : vp.launches) {
-    AttnArgs a;
+  std::vector<AttnArgs> args(vp.launches.size());
+  std::vector<char> split(vp.launches.size(), 0);
+  for (size_t li = 0; li < vp.launches.size(); ++li) {
+    const VerifyLaunch& L = vp.launches[li];
+    AttnArgs& a = args[li];
     std::memset(&a, 0, sizeof(a));
     a.pool = c->pool;
     a.table = c->dtable;
@@ -400,6 +431,7 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.slot_stride = (int32_t)vp.slot_stride;
     a.rpad = vp.rpad;
     a.force_partial = 0;
+    a.tile_keys = tile_keys(P.format, P.head_dim);
     bool any_split = false;
     for (int i = 0; i < L.count; ++i) {
       const int sid = seq_ids[L.first + i];
@@ -417,12 +449,17 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
       }
     }
     for (int i = 0; i <= L.count; ++i) a.tile_base[i] = L.tile_base[i];
-    hipError_t e = launch_attn(a, vp.nct, s);
-    if (e != hipSuccess) return hip_fail(c, e, "attention launch");
-    if (any_split) {
-      e = launch_merge(a, vp.nct, s);
-      if (e != hipSuccess) return hip_fail(c, e, "merge launch");
-    }
+    split[li] = any_split ? 1 : 0;
+  }
+  hipError_t e = hipSuccess;
+  if (c->trace_before) e = hipEventRecord(c->trace_before, s);
+  for (size_t li = 0; li < args.size() && e == hipSuccess; ++li) e = launch_attn(args[li], vp.nct, s);
+  if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, s);
+  if (e != hipSuccess) return hip_fail(c, e, "attention launch");
+  for (size_t li = 0; li < args.size(); ++li) {
+    if (!split[li]) continue;
+    e = launch_merge(args[li], vp.nct, s);
+    if (e != hipSuccess) return hip_fail(c, e, "merge launch");
   }
   return KV_OK;
 }

@@ -52,12 +52,14 @@ class Runner:
         return synth.step_plan(self.wl, step)
 
     def rollback(self, rb):
-        for s, r in enumerate(rb):
-            if r:
-                for c in self.caches:
-                    c.rollback(s, r)
-                if self.track:
-                    self.prov[s] = self.prov[s][: len(self.prov[s]) - r]
+        if not any(rb):
+            return
+        seqs = [s for s, r in enumerate(rb) if r]
+        for c in self.caches:
+            c.rollback_batch(seqs, [rb[s] for s in seqs])
+        if self.track:
+            for s in seqs:
+                self.prov[s] = self.prov[s][: len(self.prov[s]) - rb[s]]
 
     def append_rows(self, step, rows):
         wl = self.wl

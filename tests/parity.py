@@ -46,9 +46,25 @@ def max_err(runner, rows, q, out, layer, seqs):
     return worst
 
 
+def unswizzle_subtiles(raw, fmt, D, kind):
+    """Undo the documented sub-tile order of a plain-format K or V region:
+    raw [n_sub, 32 * D] -> [n_sub * 32 tokens, D]."""
+    n = raw.shape[0]
+    if fmt == 1 and kind == "k":  # (kk, h, m, e) = K[m][16kk + 8h + e]
+        t = raw.reshape(n, D // 16, 2, 32, 8).permute(0, 3, 1, 2, 4)
+    elif fmt == 1:  # (v, dt, h, r, e1, e0) = V[16v + 8e1 + 4h + e0][32dt + r]
+        t = raw.reshape(n, 2, D // 32, 2, 32, 2, 4).permute(0, 1, 5, 3, 6, 2, 4)
+    elif kind == "k":  # (kq, h, m, e) = K[m][(D/2)h + 4kq + e]
+        t = raw.reshape(n, D // 8, 2, 32, 4).permute(0, 3, 2, 1, 4)
+    else:  # (uq, dt, h, r, e) = V[8uq + 4h + e][32dt + r]
+        t = raw.reshape(n, 4, D // 32, 2, 32, 4).permute(0, 1, 3, 5, 2, 4)
+    return t.reshape(n * 32, D)
+
+
 def read_plain(cache, s, L):
-    """K, V [L, hkv, d] of sequence s read from an fp32/bf16 pool via the
-    documented layout (K [hkv][256][d]; V [hkv][4][d][64] per block)."""
+    """K, V [L, hkv, d] of sequence s read from an fp32/bf16 pool through the
+    documented layout (per block: every head's K region, then every head's V
+    region; each region is 8 sub-tiles of 32 tokens in MFMA operand order)."""
     import torch
 
     hkv, d = cache.num_kv_heads, cache.head_dim
@@ -60,8 +76,8 @@ def read_plain(cache, s, L):
     ks, vs = [], []
     for b in range(math.ceil(L / 256)):
         base = table[b] * bb
-        kb = cache.pool[base: base + half].view(dt).reshape(hkv, 256, d).permute(1, 0, 2)
-        vb = cache.pool[base + half: base + bb].view(dt).reshape(hkv, 4, d, 64).permute(1, 3, 0, 2)
-        ks.append(kb)
-        vs.append(vb.reshape(256, hkv, d))
+        kb = cache.pool[base: base + half].view(dt).reshape(hkv, 8, 32 * d)
+        vb = cache.pool[base + half: base + bb].view(dt).reshape(hkv, 8, 32 * d)
+        ks.append(torch.stack([unswizzle_subtiles(kb[h], cache.fmt, d, "k") for h in range(hkv)], dim=1))
+        vs.append(torch.stack([unswizzle_subtiles(vb[h], cache.fmt, d, "v") for h in range(hkv)], dim=1))
     return torch.cat(ks)[:L], torch.cat(vs)[:L]
