@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsvattn.so")
+# SVATTN_LIB may name another build of the same library (e.g. a variant
+# being measured); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("SVATTN_LIB") or os.path.join(PKG, "libsvattn.so")
 CORE_LIB_PATH = os.path.join(PKG, "libsvattn_core.so")
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_ERANGE, KV_ENOSEQ, KV_EDEVICE = 0, -1, -2, -3, -4, -5

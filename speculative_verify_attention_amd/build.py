@@ -50,10 +50,10 @@ def _run(cmd):
     return r.stdout
 
 
-def _compile_hip(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile_hip(src, defines=(), tag=""):
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    _run([HIPCC, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    _run([HIPCC, *HIP_FLAGS, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
@@ -66,15 +66,18 @@ def build_core():
     return CORE_LIB
 
 
-def build_hip(jobs=None):
+def build_hip(jobs=None, out=LIB, defines=()):
+    """Compile libsvattn.so; `defines` (NAME=VALUE) and `out` build a variant
+    elsewhere without touching the in-tree library."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(4, os.cpu_count() or 1)
+    tag = "" if not defines else "." + "_".join(d.replace("=", "") for d in defines)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile_hip, HIP_SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile_hip(s, defines, tag), HIP_SOURCES))
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def build():

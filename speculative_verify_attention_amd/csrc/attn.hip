@@ -43,6 +43,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define NEG_INF (-__builtin_inff())
 
+// Depth of the register ring of 16 KiB tiles (tiles in flight + 1), and the
+// waves per SIMD the bf16 kernels at d <= 128 are compiled for.
+#ifndef SVATTN_NBUF
+#define SVATTN_NBUF 2
+#endif
+#ifndef SVATTN_BF16_WAVES
+#define SVATTN_BF16_WAVES 1
+#endif
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh without branches, for the soft cap: an odd Taylor polynomial below
@@ -114,23 +123,27 @@ template <int FMT, int D>
 struct QOperand;
 
 template <int D>
-struct QOperand<1, D> {  // k-step kk holds dims 16kk + 8hh .. +8
-  bf16x8_t v[D / 16];
-  __device__ __forceinline__ void load(const float* q, int hh) {
+struct QOperand<1, D> {
+  // bf16: the fragments live in LDS, shared by the workgroup's token lanes:
+  // k-step kk of lane (c, hh) = dims 16kk + 8hh .. +8 at lds[kk * 64 + lane].
+  const u32x4_t* lds;
+  // Written by one wave per column group.
+  __device__ __forceinline__ static void store(u32x4_t* dst, const float* q, bool ok, int lane) {
+    const int hh = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
+      bf16x8_t v{};
+      if (ok) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[kk][e] = (__bf16)a[e];
-        v[kk][4 + e] = (__bf16)b[e];
+        for (int e = 0; e < 4; ++e) {
+          v[e] = (__bf16)a[e];
+          v[4 + e] = (__bf16)b[e];
+        }
       }
+      dst[kk * 64 + lane] = __builtin_bit_cast(u32x4_t, v);
     }
-  }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) v[kk] = bf16x8_t{};
   }
 };
 
@@ -155,10 +168,12 @@ struct QOperand<0, D> {  // k-step kk holds dim (D/2) hh + kk
 // 8(r>>2) + 4hh + (r&3), r = 0..15.
 template <int D>
 __device__ __forceinline__ f32x16_t qk_sub(const QOperand<1, D>& q, const TileRegs<1, D>& b, int st) {
+  const int lane = threadIdx.x & 63;
   f32x16_t s = {};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.k[st][kk]), q.v[kk], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.k[st][kk]),
+                                                __builtin_bit_cast(bf16x8_t, q.lds[kk * 64 + lane]), s, 0, 0, 0);
   return s;
 }
 template <int D>
@@ -332,200 +347,225 @@ __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& 
   pv_tile<D>(cs.acc, b, p);
 }
 
+// Chunk of workgroup w: sequence index s, kv head h, tiles [t_begin, t_end)
+// of the pair, out of nt, split into k chunks.
+struct Chunk {
+  int s, h, k, nt, tlo, t_begin, t_end;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
+  Chunk c;
+  c.s = find_seq(a.wg_base, a.n_seqs, w);
+  c.k = a.ksplit[c.s];
+  const int local = w - a.wg_base[c.s];
+  c.h = local / c.k;
+  const int part = local - c.h * c.k;
+  const int L = a.len[c.s], n = a.nrows[c.s];
+  const int tk = a.tile_keys;
+  const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
+  c.tlo = klo / tk;
+  c.nt = (L + tk - 1) / tk - c.tlo;
+  const int cs = (c.nt + c.k - 1) / c.k;
+  c.t_begin = part * cs;
+  c.t_end = min(c.nt, c.t_begin + cs);
+  return c;
+}
+
 template <int FMT, int D, int NCT, bool CAP>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1) void attn_kernel(AttnArgs a) {
   constexpr int TL = 4 / NCT;  // token lanes
   constexpr int NDT = D / 32;
   constexpr int TK = 32 * Tr<FMT, D>::NSUB;
   constexpr int E = FMT == 1 ? 2 : 4;
-  constexpr bool DB = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4 <= 64;  // double-buffer
+  // registers per tile buffer decide how many tiles are kept in flight
+  constexpr int TILE_REGS = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4;
+  constexpr int NBUF = TILE_REGS <= 64 ? SVATTN_NBUF : 1;
   constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
   __shared__ float cbuf[NCT * (TL / 2) * CSTRIDE];
+  __shared__ u32x4_t qlds[FMT == 1 ? NCT * (D / 16) * 64 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ct = wave % NCT, tl = wave / NCT;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
   const int w = blockIdx.x;
-  const int hkv = a.lay.hkv;
-  int f = w * a.tiles_per_wg;
-  const int fend = min(f + a.tiles_per_wg, a.total_tiles);
+  const Chunk ch = chunk_of(a, w);
+  const int s = ch.s, h = ch.h, tlo = ch.tlo;
+  const int L = a.len[s], n = a.nrows[s];
+  const int R = n * a.g;
+  const bool col_ok = c < R;
+  const int row_i = col_ok ? c / a.g : 0;
+  const int head_j = col_ok ? c - row_i * a.g : 0;
+  const int ppos = L - n + row_i;  // position of this column's query row
 
-  while (f < fend) {
-    const int s = find_seq(a.tile_base, a.n_seqs, f);
-    const int L = a.len[s], n = a.nrows[s];
-    const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
-    const int tlo = klo / TK;
-    const int nt = (L + TK - 1) / TK - tlo;
-    const int rel = f - a.tile_base[s];
-    const int h = rel / nt;
-    const int pair_first = a.tile_base[s] + h * nt;
-    const int seg_end = min(fend, pair_first + nt);
-    const int t_begin = f - pair_first, t_end = seg_end - pair_first;
-    const int R = n * a.g;
-    const bool col_ok = c < R;
-    const int row_i = col_ok ? c / a.g : 0;
-    const int head_j = col_ok ? c - row_i * a.g : 0;
-    const int ppos = L - n + row_i;  // position of this column's query row
+  const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
+  const int64_t head_off = (int64_t)h * 256 * D * E;
+  auto bases = [&](int t, const uint8_t*& kb, const uint8_t*& vb) {
+    const int key0 = (tlo + t) * TK;
+    const uint8_t* blk = a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + head_off + (key0 & 255) * D * E;
+    kb = blk + a.lay.k_off;
+    vb = blk + a.lay.v_off;
+  };
+  const int t_first = ch.t_begin + tl;
+  const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
 
-    QOperand<FMT, D> qop;
+  // First tiles' loads go out before anything else waits on memory.
+  // NBUF-deep register ring: tiles i+1 .. i+NBUF-1 are in flight while tile i
+  // is computed; the loop is unrolled NBUF times so buffer indices are
+  // compile-time constants.
+  TileRegs<FMT, D> buf[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) {
+    if (j < cnt) {
+      const uint8_t *kb, *vb;
+      bases(t_first + j * TL, kb, vb);
+      load_tile<FMT, D>(buf[j], kb, vb, lane);
+    }
+  }
+
+  const float* qsrc = a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+  QOperand<FMT, D> qop;
+  if constexpr (FMT == 1) {
+    if (tl == 0) QOperand<1, D>::store(qlds + ct * (D / 16) * 64, qsrc, col_ok, lane);
+    __syncthreads();
+    qop.lds = qlds + ct * (D / 16) * 64;
+  } else {
     if (col_ok)
-      qop.load(a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D, hh);
+      qop.load(qsrc, hh);
     else
       qop.zero();
+  }
 
-    ColState<D> cs;
-    cs.m = NEG_INF;
-    cs.l = 0.0f;
+  ColState<D> cs;
+  cs.m = NEG_INF;
+  cs.l = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
+  for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
 
-    const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
-    const int64_t head_off = (int64_t)h * 256 * D * E;
-    auto bases = [&](int t, const uint8_t*& kb, const uint8_t*& vb) {
-      const int key0 = (tlo + t) * TK;
-      const uint8_t* blk = a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + head_off + (key0 & 255) * D * E;
-      kb = blk + a.lay.k_off;
-      vb = blk + a.lay.v_off;
-    };
-    const int cnt = t_begin + tl < t_end ? (t_end - t_begin - tl + TL - 1) / TL : 0;
-    TileRegs<FMT, D> b0;
-    if constexpr (DB) {
-      TileRegs<FMT, D> b1;
-      const uint8_t *kb, *vb;
-      if (cnt > 0) {
-        bases(t_begin + tl, kb, vb);
-        load_tile<FMT, D>(b0, kb, vb, lane);
-      }
-      for (int i = 0; i < cnt; i += 2) {
-        const int t0 = t_begin + tl + i * TL;
-        if (i + 1 < cnt) {
-          bases(t0 + TL, kb, vb);
-          load_tile<FMT, D>(b1, kb, vb, lane);
+  for (int i = 0; i < cnt; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int k = i + u;
+      if (k < cnt) {
+        if (k + NBUF - 1 < cnt) {
+          const uint8_t *kb, *vb;
+          bases(t_first + (k + NBUF - 1) * TL, kb, vb);
+          load_tile<FMT, D>(buf[(u + NBUF - 1) % NBUF], kb, vb, lane);
         }
-        process_tile<FMT, D, CAP>(cs, b0, qop, a, (tlo + t0) * TK, L, n, ppos, lane);
-        if (i + 1 < cnt) {
-          if (i + 2 < cnt) {
-            bases(t0 + 2 * TL, kb, vb);
-            load_tile<FMT, D>(b0, kb, vb, lane);
-          }
-          process_tile<FMT, D, CAP>(cs, b1, qop, a, (tlo + t0 + TL) * TK, L, n, ppos, lane);
-        }
+        process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane);
       }
+    }
+  }
+
+  // ---- combine the token lanes of each column group through LDS ----
+  cs.l += __shfl_xor(cs.l, 32);
+#pragma unroll
+  for (int half = TL / 2; half >= 1; half >>= 1) {
+    if (tl >= half && tl < 2 * half) {
+      float* slot = cbuf + (ct * (TL / 2) + (tl - half)) * CSTRIDE;
+      if (hh == 0) {
+        slot[col] = cs.m;
+        slot[32 + col] = cs.l;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
+    }
+    __syncthreads();
+    if (tl < half) {
+      const float* slot = cbuf + (ct * (TL / 2) + tl) * CSTRIDE;
+      const float mp = slot[col], lp = slot[32 + col];
+      const float mm = fmaxf(cs.m, mp);
+      const float mu = mm == NEG_INF ? 0.0f : mm;
+      const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
+      cs.l = cs.l * fs + lp * fp;
+      cs.m = mm;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
+    }
+    if (half > 1) __syncthreads();
+  }
+
+  if (tl == 0 && col_ok) {
+    if (ch.k == 1 && !a.force_partial) {
+      const float inv = 1.0f / cs.l;
+      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t v = {cs.acc[dt][4 * j] * inv, cs.acc[dt][4 * j + 1] * inv, cs.acc[dt][4 * j + 2] * inv,
+                       cs.acc[dt][4 * j + 3] * inv};
+          *reinterpret_cast<f32x4_t*>(o + 32 * dt + 8 * j + 4 * hh) = v;
+        }
     } else {
-      for (int i = 0; i < cnt; ++i) {
-        const int t0 = t_begin + tl + i * TL;
-        const uint8_t *kb, *vb;
-        bases(t0, kb, vb);
-        load_tile<FMT, D>(b0, kb, vb, lane);
-        process_tile<FMT, D, CAP>(cs, b0, qop, a, (tlo + t0) * TK, L, n, ppos, lane);
+      float* slot = a.part + (int64_t)w * a.slot_stride;
+      if (hh == 0) {
+        slot[c] = cs.m;
+        slot[a.rpad + c] = cs.l;
       }
-    }
-
-    // ---- combine the token lanes of each column group through LDS ----
-    cs.l += __shfl_xor(cs.l, 32);
+      float* acc = slot + 2 * a.rpad + (int64_t)c * D;
 #pragma unroll
-    for (int half = TL / 2; half >= 1; half >>= 1) {
-      if (tl >= half && tl < 2 * half) {
-        float* slot = cbuf + (ct * (TL / 2) + (tl - half)) * CSTRIDE;
-        if (hh == 0) {
-          slot[col] = cs.m;
-          slot[32 + col] = cs.l;
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t v = {cs.acc[dt][4 * j], cs.acc[dt][4 * j + 1], cs.acc[dt][4 * j + 2], cs.acc[dt][4 * j + 3]};
+          *reinterpret_cast<f32x4_t*>(acc + 32 * dt + 8 * j + 4 * hh) = v;
         }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
-      }
-      __syncthreads();
-      if (tl < half) {
-        const float* slot = cbuf + (ct * (TL / 2) + tl) * CSTRIDE;
-        const float mp = slot[col], lp = slot[32 + col];
-        const float mm = fmaxf(cs.m, mp);
-        const float mu = mm == NEG_INF ? 0.0f : mm;
-        const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
-        cs.l = cs.l * fs + lp * fp;
-        cs.m = mm;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
-      }
-      __syncthreads();
     }
-
-    if (tl == 0 && col_ok) {
-      const int wg_lo = pair_first / a.tiles_per_wg;
-      const int wg_hi = (pair_first + nt - 1) / a.tiles_per_wg;
-      if (wg_lo == wg_hi && !a.force_partial) {
-        const float inv = 1.0f / cs.l;
-        float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4_t v = {cs.acc[dt][4 * j] * inv, cs.acc[dt][4 * j + 1] * inv, cs.acc[dt][4 * j + 2] * inv,
-                         cs.acc[dt][4 * j + 3] * inv};
-            *reinterpret_cast<f32x4_t*>(o + 32 * dt + 8 * j + 4 * hh) = v;
-          }
-      } else {
-        const int pair = s * hkv + h;
-        float* slot = a.part + (int64_t)(w + pair) * a.slot_stride;
-        if (hh == 0) {
-          slot[c] = cs.m;
-          slot[a.rpad + c] = cs.l;
-        }
-        float* acc = slot + 2 * a.rpad + (int64_t)c * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4_t v = {cs.acc[dt][4 * j], cs.acc[dt][4 * j + 1], cs.acc[dt][4 * j + 2], cs.acc[dt][4 * j + 3]};
-            *reinterpret_cast<f32x4_t*>(acc + 32 * dt + 8 * j + 4 * hh) = v;
-          }
-      }
-    }
-    f = seg_end;
   }
 }
 
 // ---- merge of split partials -------------------------------------------------------
 
-// One workgroup per (sequence, kv head).  Pairs that one workgroup covered
-// whole were finished by the partial kernel and are skipped.
+// One wavefront per (sequence, kv head, query column).  Pairs that a single
+// workgroup covered whole were finished by the partial kernel and are
+// skipped.  The partials' maxima and sums are reduced across the wave; each
+// lane then accumulates D/64 output dimensions over the partials.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
+  constexpr int EL = D / 64;
   const int hkv = a.lay.hkv;
-  const int pair = blockIdx.x;
+  const int rmax = a.rpad;
+  const int pair = blockIdx.x / rmax, c = blockIdx.x - pair * rmax;
   const int s = pair / hkv, h = pair - s * hkv;
-  const int L = a.len[s], n = a.nrows[s];
-  const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
-  const int tlo = klo / a.tile_keys;
-  const int nt = (L + a.tile_keys - 1) / a.tile_keys - tlo;
-  const int pair_first = a.tile_base[s] + h * nt;
-  const int wg_lo = pair_first / a.tiles_per_wg;
-  const int wg_hi = (pair_first + nt - 1) / a.tiles_per_wg;
-  if (wg_lo == wg_hi && !a.force_partial) return;
+  const int n = a.nrows[s];
   const int R = n * a.g;
-  for (int idx = threadIdx.x; idx < R * (D / 4); idx += 256) {
-    const int c = idx / (D / 4), d4 = idx - c * (D / 4);
-    float M = NEG_INF;
-    for (int w = wg_lo; w <= wg_hi; ++w) M = fmaxf(M, a.part[(int64_t)(w + pair) * a.slot_stride + c]);
-    const float mu = M == NEG_INF ? 0.0f : M;
-    float lsum = 0.0f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w = wg_lo; w <= wg_hi; ++w) {
-      const float* slot = a.part + (int64_t)(w + pair) * a.slot_stride;
-      const float f = fast_exp2(slot[c] - mu);
-      lsum += slot[a.rpad + c] * f;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(slot + 2 * a.rpad + (int64_t)c * D + 4 * d4);
-      acc += v * f;
-    }
-    const float inv = 1.0f / lsum;
-    const int row_i = c / a.g, head_j = c - row_i * a.g;
-    float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D + 4 * d4;
-    *reinterpret_cast<f32x4_t*>(o) = acc * inv;
+  const int k = a.ksplit[s];
+  if (c >= R || (k == 1 && !a.force_partial)) return;
+  const int w0 = a.wg_base[s] + h * k;  // the pair's chunks are workgroups w0 .. w0+k-1
+  const int lane = threadIdx.x;
+  const float* base = a.part + (int64_t)w0 * a.slot_stride;
+  float M = NEG_INF;
+  for (int j = lane; j < k; j += 64) M = fmaxf(M, base[(int64_t)j * a.slot_stride + c]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float mu = M == NEG_INF ? 0.0f : M;
+  float lsum = 0.0f;
+  for (int j = lane; j < k; j += 64) {
+    const float* slot = base + (int64_t)j * a.slot_stride;
+    lsum += slot[a.rpad + c] * fast_exp2(slot[c] - mu);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+  float acc[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const float* slot = base + (int64_t)j * a.slot_stride;
+    const float f = fast_exp2(slot[c] - mu);
+    const float* src = slot + 2 * a.rpad + (int64_t)c * D + lane * EL;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] += src[e] * f;
+  }
+  const float inv = 1.0f / lsum;
+  const int row_i = c / a.g, head_j = c - row_i * a.g;
+  float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) o[e] = acc[e] * inv;
 }
 
 // ---- launchers ----------------------------------------------------------------------
@@ -562,15 +602,15 @@ hipError_t launch_attn(const AttnArgs& a, int nct, hipStream_t s) {
 
 hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s) {
   (void)nct;
-  const int pairs = a.n_seqs * a.lay.hkv;
-  if (pairs <= 0) return hipSuccess;
+  const int blocks = a.n_seqs * a.lay.hkv * a.rpad;
+  if (blocks <= 0) return hipSuccess;
   const int d = a.lay.d;
   if (d == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(pairs), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(64), 0, s, a);
   else if (d == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(pairs), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, s, a);
   else if (d == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, dim3(pairs), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<256>, dim3(blocks), dim3(64), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -113,11 +113,16 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 // ---- verify attention ------------------------------------------------------------
 constexpr int kMaxAttnSeqs = 128;
 
+// A call's work is cut into chunks of consecutive tiles of one (sequence, kv
+// head) pair; workgroup w takes one chunk.  Sequence i's pairs are split into
+// ksplit[i] chunks each, and its workgroups are wg_base[i] .. wg_base[i+1]-1
+// (kv head major).  A pair split into more than one chunk leaves one partial
+// slot per chunk (slot index = workgroup index) for the merge.
 struct AttnArgs {
   const uint8_t* pool;
   const int32_t* table;
-  const float* q;    // [rows][hq][d] (TQ3: q' and q'' in the workspace instead)
-  const float* q2;   // TQ3: q'' (S Pi q)
+  const float* q;    // [rows][hq][d] (TQ3: q' = Pi q)
+  const float* q2;   // TQ3: q'' = S Pi q
   float* out;        // [rows][hq][d]
   float* part;       // partial slots
   PoolLayout lay;
@@ -128,8 +133,6 @@ struct AttnArgs {
   float qjl_coef;    // TQ3: sqrt(pi/2) / d
   float inv_sqrt_d;  // TQ3
   int32_t n_seqs;
-  int32_t tiles_per_wg;
-  int32_t total_tiles;
   int32_t n_wg;
   int32_t slot_stride;    // floats per partial slot
   int32_t rpad;           // padded rows per slot (32 * NCT)
@@ -140,7 +143,8 @@ struct AttnArgs {
   int32_t len[kMaxAttnSeqs];
   int32_t qrow0[kMaxAttnSeqs];
   int32_t nrows[kMaxAttnSeqs];
-  int32_t tile_base[kMaxAttnSeqs + 1];  // prefix over sequences of hkv * tiles
+  int32_t ksplit[kMaxAttnSeqs];
+  int32_t wg_base[kMaxAttnSeqs + 1];
 };
 
 struct QPrepArgs {

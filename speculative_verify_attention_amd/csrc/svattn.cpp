@@ -36,6 +36,15 @@ struct kv_cache {
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// Workgroups a verify call is split into (one round on 256 compute units at
+// one workgroup per CU); build-time constants so variants can be measured.
+#ifndef SVATTN_WG_PER_CALL
+#define SVATTN_WG_PER_CALL 256
+#endif
+#ifndef SVATTN_WG_PER_CALL_D256
+#define SVATTN_WG_PER_CALL_D256 256
+#endif
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MetaLayout {
@@ -93,13 +102,15 @@ CoreParams core_params(const kv_params& p) {
 
 struct VerifyLaunch {
   int first, count;  // sequences [first, first+count) of the call
-  int total_tiles, tiles_per_wg, n_wg, n_pairs;
+  int n_wg;
   int64_t slot0;     // first partial slot of this launch
-  std::vector<int32_t> tile_base;
+  std::vector<int32_t> ksplit, wg_base;
 };
 
 struct VerifyPlan {
   int nct = 1, rpad = 32;
+  std::vector<int> order;      // call index of the i-th sequence handed to the kernels
+  std::vector<int32_t> qrow0;  // first query/output row of each call index
   int64_t slot_stride = 0, slots = 0, rows = 0;
   size_t part_bytes = 0, q_bytes = 0, total = 0;
   std::vector<VerifyLaunch> launches;
@@ -133,27 +144,50 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
   vp->rpad = 32 * vp->nct;
   vp->slot_stride = (int64_t)vp->rpad * (2 + P.head_dim);
   const int TL = 4 / vp->nct;
-  const int target_wg = P.head_dim > 128 ? 256 : 512;
+  const int target_wg = P.head_dim > 128 ? SVATTN_WG_PER_CALL_D256 : SVATTN_WG_PER_CALL;
+  // tiles of each (sequence, kv head) pair over the whole call
+  const int tk = tile_keys(P.format, P.head_dim);
+  std::vector<int> nt(n_seqs);
+  int64_t total_tiles = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    int32_t len;
+    c->core.seq_len(seq_ids[i], &len);
+    const int klo = window > 0 ? std::max(0, len - n_rows[i] - window + 1) : 0;
+    nt[i] = (len + tk - 1) / tk - klo / tk;
+    total_tiles += (int64_t)nt[i] * P.num_kv_heads;
+  }
+  // Uniform batches: one round of workgroups (one per CU).  Ragged batches
+  // (lengths far apart): four times as many, smaller chunks, so the dispatcher
+  // can even out the mix of long and short pairs.
+  const int nt_max = *std::max_element(nt.begin(), nt.end());
+  const int nt_min = *std::min_element(nt.begin(), nt.end());
+  const int64_t target = 4 * (int64_t)nt_min >= 3 * (int64_t)nt_max ? target_wg : 4 * (int64_t)target_wg;
+  // chunks of at most ~total / target tiles, never fewer than one per token lane
+  const int64_t per_wg = std::max<int64_t>(TL, (total_tiles + target - 1) / target);
+  // Sequences go to the kernel longest first (workgroups are dispatched in
+  // index order, so the big chunks start first and the short ones fill in).
+  vp->order.resize(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) vp->order[i] = i;
+  std::stable_sort(vp->order.begin(), vp->order.end(), [&](int x, int y) { return nt[x] > nt[y]; });
+  vp->qrow0.assign(n_seqs, 0);
+  for (int i = 1; i < n_seqs; ++i) vp->qrow0[i] = vp->qrow0[i - 1] + n_rows[i - 1];
   for (int first = 0; first < n_seqs; first += kMaxAttnSeqs) {
     VerifyLaunch L;
     L.first = first;
     L.count = std::min(kMaxAttnSeqs, n_seqs - first);
-    L.tile_base.assign(L.count + 1, 0);
+    L.ksplit.assign(L.count, 1);
+    L.wg_base.assign(L.count + 1, 0);
     for (int i = 0; i < L.count; ++i) {
-      int32_t len;
-      c->core.seq_len(seq_ids[first + i], &len);
-      const int n = n_rows[first + i];
-      const int klo = window > 0 ? std::max(0, len - n - window + 1) : 0;
-      const int tk = tile_keys(P.format, P.head_dim);
-      const int nt = (len + tk - 1) / tk - klo / tk;
-      L.tile_base[i + 1] = L.tile_base[i] + nt * P.num_kv_heads;
+      const int tiles = nt[vp->order[first + i]];
+      int k = (int)std::max<int64_t>(1, (tiles + per_wg - 1) / per_wg);
+      const int cs = (tiles + k - 1) / k;
+      k = (tiles + cs - 1) / cs;  // no empty chunk
+      L.ksplit[i] = k;
+      L.wg_base[i + 1] = L.wg_base[i] + k * P.num_kv_heads;
     }
-    L.total_tiles = L.tile_base[L.count];
-    L.tiles_per_wg = std::max(TL, (L.total_tiles + target_wg - 1) / target_wg);
-    L.n_wg = (L.total_tiles + L.tiles_per_wg - 1) / L.tiles_per_wg;
-    L.n_pairs = L.count * P.num_kv_heads;
+    L.n_wg = L.wg_base[L.count];
     L.slot0 = vp->slots;
-    vp->slots += L.n_wg + L.n_pairs;
+    vp->slots += L.n_wg;
     vp->launches.push_back(std::move(L));
   }
   vp->part_bytes = align_up((size_t)vp->slots * vp->slot_stride * 4);
@@ -404,7 +438,6 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   if (P.format == KV_TQ3) return set_err(c, KV_EINVAL, "KV_TQ3 attention not available in this build");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int g = num_q_heads / P.num_kv_heads;
-  int64_t qrow = 0;
   std::vector<AttnArgs> args(vp.launches.size());
   std::vector<char> split(vp.launches.size(), 0);
   for (size_t li = 0; li < vp.launches.size(); ++li) {
@@ -425,8 +458,6 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.softcap = softcap;
     a.inv_softcap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
     a.n_seqs = L.count;
-    a.tiles_per_wg = L.tiles_per_wg;
-    a.total_tiles = L.total_tiles;
     a.n_wg = L.n_wg;
     a.slot_stride = (int32_t)vp.slot_stride;
     a.rpad = vp.rpad;
@@ -434,21 +465,18 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.tile_keys = tile_keys(P.format, P.head_dim);
     bool any_split = false;
     for (int i = 0; i < L.count; ++i) {
-      const int sid = seq_ids[L.first + i];
+      const int ci = vp.order[L.first + i];
+      const int sid = seq_ids[ci];
       int32_t len;
       c->core.seq_len(sid, &len);
       a.seq[i] = sid;
       a.len[i] = len;
-      a.qrow0[i] = (int32_t)qrow;
-      a.nrows[i] = n_rows[L.first + i];
-      qrow += n_rows[L.first + i];
-      const int nt = (L.tile_base[i + 1] - L.tile_base[i]) / P.num_kv_heads;
-      for (int h = 0; h < P.num_kv_heads; ++h) {
-        const int first = L.tile_base[i] + h * nt;
-        if (first / L.tiles_per_wg != (first + nt - 1) / L.tiles_per_wg) any_split = true;
-      }
+      a.qrow0[i] = vp.qrow0[ci];
+      a.nrows[i] = n_rows[ci];
+      a.ksplit[i] = L.ksplit[i];
+      if (L.ksplit[i] > 1) any_split = true;
     }
-    for (int i = 0; i <= L.count; ++i) a.tile_base[i] = L.tile_base[i];
+    for (int i = 0; i <= L.count; ++i) a.wg_base[i] = L.wg_base[i];
     split[li] = any_split ? 1 : 0;
   }
   hipError_t e = hipSuccess;
