@@ -177,3 +177,67 @@ def record_bytes(d, is_key):
     if is_key:
         return (4 * d) // 8 + 2 + 2
     return (3 * d) // 8 + 2
+
+
+# --- the same steps over many vectors at once --------------------------------------
+#
+# encode_batch / decode_batch apply exactly the per-vector steps above to the
+# rows of a matrix (each row independent; the matrix products are the
+# per-vector products stacked).  tests/test_oracle_tq3.py pins them to the
+# per-vector functions.
+
+
+def fp16_sat_array(x):
+    with np.errstate(over="ignore"):
+        h = np.asarray(x, dtype=np.float64).astype(np.float16)
+    h = np.where(np.isinf(h), np.float16(FP16_MAX), h)
+    return h.astype(np.float64)
+
+
+def encode_batch(xs, is_key, pi, s_mat, c16, t, chunk=65536):
+    """Encode the rows of xs [N, d]: dict of arrays code [N, d] uint8, n16 [N],
+    z [N, d], and for keys bits [N, d] uint8, g16 [N], proj [N, d]."""
+    xs = np.asarray(xs, dtype=np.float64)
+    N, d = xs.shape
+    out = {"code": np.empty((N, d), np.uint8), "n16": np.empty(N), "z": np.empty((N, d)), "n": np.empty(N)}
+    if is_key:
+        out.update(bits=np.empty((N, d), np.uint8), g16=np.empty(N), proj=np.empty((N, d)), rho=np.empty(N))
+    s64 = s_mat.astype(np.float64)
+    for a in range(0, N, chunk):
+        x = xs[a: a + chunk]
+        n = np.sqrt(np.sum(x * x, axis=1))
+        safe = np.where(n == 0.0, 1.0, n)
+        y = (x / safe[:, None]) @ pi.T
+        y[n == 0.0] = 0.0
+        z = math.sqrt(d) * y
+        code = np.zeros(z.shape, dtype=np.uint8)
+        for tj in t:
+            code += (tj <= z).astype(np.uint8)
+        n16 = fp16_sat_array(n)
+        out["code"][a: a + chunk] = code
+        out["n16"][a: a + chunk] = n16
+        out["z"][a: a + chunk] = z
+        out["n"][a: a + chunk] = n
+        if is_key:
+            r = x @ pi.T - n16[:, None] * c16[code] / math.sqrt(d)
+            rho = np.sqrt(np.sum(r * r, axis=1))
+            proj = r @ s64.T
+            out["bits"][a: a + chunk] = (proj >= 0.0).astype(np.uint8)
+            out["g16"][a: a + chunk] = fp16_sat_array(rho)
+            out["proj"][a: a + chunk] = proj
+            out["rho"][a: a + chunk] = rho
+    return out
+
+
+def decode_values(code, n16, pi, c16):
+    """Rows of decoded values: Pi^T (n16 c16[code] / sqrt(d))."""
+    d = code.shape[1]
+    return (n16[:, None] * c16[code] / math.sqrt(d)) @ pi
+
+
+def decode_keys(code, bits, n16, g16, pi, s_mat, c16):
+    """Rows of decoded keys: Pi^T (n16 c16[code]/sqrt(d) + g16 sqrt(pi/2)/d S^T b)."""
+    d = code.shape[1]
+    b = np.where(bits != 0, 1.0, -1.0)
+    rot = n16[:, None] * c16[code] / math.sqrt(d) + g16[:, None] * math.sqrt(math.pi / 2.0) / d * (b @ s_mat.astype(np.float64))
+    return rot @ pi

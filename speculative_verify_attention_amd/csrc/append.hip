@@ -25,12 +25,7 @@ PoolLayout make_layout(int fmt, int hkv, int d) {
   L.hkv = hkv;
   L.d = d;
   if (fmt == 2) {
-    L.kc_off = 0;
-    L.kn_off = L.kc_off + (int64_t)hkv * 256 * (d / 2);
-    L.kg_off = L.kn_off + (int64_t)hkv * 256 * 2;
-    L.vc_off = L.kg_off + (int64_t)hkv * 256 * 2;
-    L.vn_off = L.vc_off + (int64_t)hkv * 4 * d * 24;
-    L.block_bytes = L.vn_off + (int64_t)hkv * 256 * 2;
+    L.block_bytes = (int64_t)hkv * 8 * tq3_sub_bytes(d);
   } else {
     int64_t e = fmt == 0 ? 4 : 2;
     L.k_off = 0;
@@ -250,15 +245,17 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
 
 // ---- quantize-on-append ----------------------------------------------------------
 
-// One workgroup (4 waves) per (segment, 64-token group, kv head).  Each wave
-// encodes whole tokens; value codes of the group are staged in LDS and then
-// packed per dimension, merging with the codes of tokens the append does not
-// touch (one writer per 24-byte row, so no two workgroups race on it).
+// One workgroup (4 waves) per (segment, 32-token sub-tile, kv head).  Each
+// wave encodes whole tokens; key codes and scales go straight to their
+// bytes (a byte never holds two tokens).  Value codes share 48-bit fields
+// across 16 tokens, so they are staged in LDS and then merged into their
+// fields by one thread each (one writer per field: no two workgroups race).
 template <int D>
 __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   constexpr int E = D / 64;
+  constexpr int SB = tq3_sub_bytes(D);
   __shared__ double rbuf[4][D];
-  __shared__ uint8_t vcode[64][D];
+  __shared__ uint8_t vcode[32][D];
   __shared__ uint32_t sat_any;
   const int unit = blockIdx.x;
   const int h = blockIdx.y;
@@ -267,53 +264,67 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   if (threadIdx.x == 0) sat_any = 0;
   const int seg = find_seg(a.unit0, a.n_segs, unit);
   const int pos0 = a.pos0[seg];
-  const int grp = (pos0 >> 6) + (unit - a.unit0[seg]);
-  const int t0 = max(pos0, grp * 64);
-  const int t1 = min(pos0 + a.n[seg], grp * 64 + 64);
-  const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 2)];
-  uint8_t* base = a.pool + (int64_t)block * a.lay.block_bytes;
+  const int grp = (pos0 >> 5) + (unit - a.unit0[seg]);  // 32-token sub-tile of the sequence
+  const int t0 = max(pos0, grp * 32);
+  const int t1 = min(pos0 + a.n[seg], grp * 32 + 32);
+  const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
+  uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
   uint32_t sat = 0;
   __syncthreads();
   for (int t = t0 + wave; t < t1; t += 4) {
-    const int slot = t & 255;
+    const int m = t & 31;
     const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
     const float* kx = reinterpret_cast<const float*>(a.k) + (src_row * a.lay.hkv + h) * D;
     const float* vx = reinterpret_cast<const float*>(a.v) + (src_row * a.lay.hkv + h) * D;
     EncOut<D> ko, vo;
     encode_vector<D>(kx, true, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
-    store_key_nibbles<D>(base + a.lay.kc_off + ((int64_t)h * 256 + slot) * (D / 2), ko);
-    if (lane == 0) {
-      store_half(base + a.lay.kn_off + ((int64_t)h * 256 + slot) * 2, ko.n16);
-      store_half(base + a.lay.kg_off + ((int64_t)h * 256 + slot) * 2, ko.g16);
+    // key nibbles: dims 2b, 2b+1 share a byte
+    if constexpr (E == 1) {
+      const uint32_t nib = (uint32_t)(ko.code[0] | (ko.bit[0] << 3));
+      const uint32_t hi = __shfl_down(nib, 1);
+      if ((lane & 1) == 0) {
+        int nb;
+        sub[tq3_k_byte(D, m, lane, &nb)] = (uint8_t)(nib | (hi << 4));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        const uint32_t lo = ko.code[e] | (ko.bit[e] << 3);
+        const uint32_t hi = ko.code[e + 1] | (ko.bit[e + 1] << 3);
+        int nb;
+        sub[tq3_k_byte(D, m, lane * E + e, &nb)] = (uint8_t)(lo | (hi << 4));
+      }
     }
     encode_vector<D>(vx, false, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
 #pragma unroll
-    for (int e = 0; e < E; ++e) vcode[t & 63][lane * E + e] = vo.code[e];
-    if (lane == 0) store_half(base + a.lay.vn_off + ((int64_t)h * 256 + slot) * 2, vo.n16);
+    for (int e = 0; e < E; ++e) vcode[m][lane * E + e] = vo.code[e];
+    if (lane == 0) {
+      store_half(sub + tq3_scale_byte(D, m, 0), ko.n16);
+      store_half(sub + tq3_scale_byte(D, m, 1), ko.g16);
+      store_half(sub + tq3_scale_byte(D, m, 2), vo.n16);
+    }
   }
   if (sat) atomicOr(&sat_any, 1u);
   __syncthreads();
-  // Pack value codes: row (h, group-in-block, dim) is 24 bytes = 6 words;
-  // token u of the group at bits 3u..3u+2.
-  const int q = grp & 3;
-  const int u0 = t0 & 63, u1 = u0 + (t1 - t0);
-  for (int dim = threadIdx.x; dim < D; dim += 256) {
-    uint32_t* row = reinterpret_cast<uint32_t*>(base + a.lay.vc_off + (((int64_t)h * 4 + q) * D + dim) * 24);
-    uint32_t w[6];
+  // Merge the staged value codes into their 48-bit fields: one thread per
+  // (dimension, half): the field of dimension i for tokens with bit 2 = h.
+  const int m0 = t0 & 31, m1 = m0 + (t1 - t0);
+  for (int f = threadIdx.x; f < 2 * D; f += 256) {
+    const int i = f >> 1, hsel = f & 1;
+    int bit0;
+    const int off = tq3_v_field(D, 4 * hsel, i, &bit0);  // any token of this half names the field
+    uint8_t* p = sub + off;
+    uint64_t field = 0;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) w[i] = row[i];
-    for (int u = u0; u < u1; ++u) {
-      const uint32_t c = vcode[u][dim];
-      const int bit = 3 * u;
-      const int wi = bit >> 5, sh = bit & 31;
-      w[wi] = (w[wi] & ~(7u << sh)) | (c << sh);
-      if (sh > 29) {  // the code straddles two words
-        const int rem = 32 - sh;
-        w[wi + 1] = (w[wi + 1] & ~(7u >> rem)) | (c >> rem);
-      }
+    for (int b = 0; b < 6; ++b) field |= (uint64_t)p[b] << (8 * b);
+    for (int m = m0; m < m1; ++m) {
+      if (((m >> 2) & 1) != hsel) continue;
+      int bit;
+      tq3_v_field(D, m, i, &bit);
+      field = (field & ~((uint64_t)7 << bit)) | ((uint64_t)vcode[m][i] << bit);
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) row[i] = w[i];
+    for (int b = 0; b < 6; ++b) p[b] = (uint8_t)(field >> (8 * b));
   }
   if (threadIdx.x == 0 && sat_any) atomicOr(a.status, 1u);
 }

@@ -31,47 +31,10 @@
 //    exchange per tile; the row sum stays per lane until the end.
 #include <hip/hip_runtime.h>
 
+#include "attn_common.h"
 #include "kernels.h"
 
 namespace svattn {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-#define NEG_INF (-__builtin_inff())
-
-// Depth of the register ring of 16 KiB tiles (tiles in flight + 1), and the
-// waves per SIMD the bf16 kernels at d <= 128 are compiled for.
-#ifndef SVATTN_NBUF
-#define SVATTN_NBUF 2
-#endif
-#ifndef SVATTN_BF16_WAVES
-#define SVATTN_BF16_WAVES 1
-#endif
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// tanh without branches, for the soft cap: an odd Taylor polynomial below
-// |x| = 0.55 (truncation below 2e-7 relative there) and 1 - 2 / (e^{2|x|} + 1)
-// above, where the subtraction loses no more than a few ulp.
-__device__ __forceinline__ float tanh_nb(float x) {
-  const float ax = fabsf(x);
-  const float x2 = x * x;
-  float p = 929569.0f / 638512875.0f;
-  p = fmaf(p, x2, -21844.0f / 6081075.0f);
-  p = fmaf(p, x2, 1382.0f / 155925.0f);
-  p = fmaf(p, x2, -62.0f / 2835.0f);
-  p = fmaf(p, x2, 17.0f / 315.0f);
-  p = fmaf(p, x2, -2.0f / 15.0f);
-  p = fmaf(p, x2, 1.0f / 3.0f);
-  const float small = fmaf(-x * x2, p, x);
-  const float e = fast_exp2(ax * 2.8853900817779268f);  // e^{2|x|}
-  const float big = copysignf(1.0f - 2.0f / (e + 1.0f), x);
-  return ax < 0.55f ? small : big;
-}
 
 // ---- per-format traits ---------------------------------------------------------------
 //
@@ -263,27 +226,6 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const TileRegs<
 
 // ---- the partial kernel ----------------------------------------------------------
 
-__device__ __forceinline__ int find_seq(const int32_t* base, int n, int f) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (base[mid] <= f)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
-// Online-softmax state of one lane: column c's running reference max m (log2
-// units, equal in both half-waves), this lane's partial sum l, and its part
-// of the column's O^T accumulator.
-template <int D>
-struct ColState {
-  float m, l;
-  f32x16_t acc[D / 32];
-};
-
 template <int FMT, int D, bool CAP>
 __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& b, const QOperand<FMT, D>& q,
                                              const AttnArgs& a, int key0, int L, int n, int ppos, int lane) {
@@ -315,60 +257,8 @@ __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& 
         p[st][r] = vis ? p[st][r] : NEG_INF;
       }
   }
-  float mt = NEG_INF;
-#pragma unroll
-  for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  // move the reference only when the tile max exceeds it by more than 2^8,
-  // so probabilities stay below 256 and rescales are rare
-  const bool up = mt > cs.m + 8.0f;
-  if (__builtin_amdgcn_ballot_w64(up)) {
-    // lanes that move: alpha = 2^(m_old - m_new), 0 when nothing was seen yet;
-    // lanes that stay keep alpha = 1 (their m may still be -inf)
-    const float alpha = up ? fast_exp2(cs.m - mt) : 1.0f;
-    cs.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) cs.acc[dt] *= alpha;
-    cs.m = up ? mt : cs.m;
-  }
-  const float m_use = cs.m == NEG_INF ? 0.0f : cs.m;
-  float lsum = 0.0f;
-#pragma unroll
-  for (int st = 0; st < NSUB; ++st)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(p[st][r] - m_use);
-      p[st][r] = e;
-      lsum += e;
-    }
-  cs.l += lsum;
+  softmax_update<D, NSUB>(cs, p);
   pv_tile<D>(cs.acc, b, p);
-}
-
-// Chunk of workgroup w: sequence index s, kv head h, tiles [t_begin, t_end)
-// of the pair, out of nt, split into k chunks.
-struct Chunk {
-  int s, h, k, nt, tlo, t_begin, t_end;
-};
-
-__device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
-  Chunk c;
-  c.s = find_seq(a.wg_base, a.n_seqs, w);
-  c.k = a.ksplit[c.s];
-  const int local = w - a.wg_base[c.s];
-  c.h = local / c.k;
-  const int part = local - c.h * c.k;
-  const int L = a.len[c.s], n = a.nrows[c.s];
-  const int tk = a.tile_keys;
-  const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
-  c.tlo = klo / tk;
-  c.nt = (L + tk - 1) / tk - c.tlo;
-  const int cs = (c.nt + c.k - 1) / c.k;
-  c.t_begin = part * cs;
-  c.t_end = min(c.nt, c.t_begin + cs);
-  return c;
 }
 
 template <int FMT, int D, int NCT, bool CAP>
@@ -380,11 +270,13 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   // registers per tile buffer decide how many tiles are kept in flight
   constexpr int TILE_REGS = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4;
   constexpr int NBUF = TILE_REGS <= 64 ? SVATTN_NBUF : 1;
-  constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
-  __shared__ float cbuf[NCT * (TL / 2) * CSTRIDE];
+  __shared__ float cbuf[CombineBuf<D, NCT>::FLOATS];
   __shared__ u32x4_t qlds[FMT == 1 ? NCT * (D / 16) * 64 : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform by construction; readfirstlane makes the compiler see it, so
+  // tile indices and block-table reads stay scalar (no wait on vector loads)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ct = wave % NCT, tl = wave / NCT;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
@@ -457,66 +349,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
     }
   }
 
-  // ---- combine the token lanes of each column group through LDS ----
-  cs.l += __shfl_xor(cs.l, 32);
-#pragma unroll
-  for (int half = TL / 2; half >= 1; half >>= 1) {
-    if (tl >= half && tl < 2 * half) {
-      float* slot = cbuf + (ct * (TL / 2) + (tl - half)) * CSTRIDE;
-      if (hh == 0) {
-        slot[col] = cs.m;
-        slot[32 + col] = cs.l;
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
-    }
-    __syncthreads();
-    if (tl < half) {
-      const float* slot = cbuf + (ct * (TL / 2) + tl) * CSTRIDE;
-      const float mp = slot[col], lp = slot[32 + col];
-      const float mm = fmaxf(cs.m, mp);
-      const float mu = mm == NEG_INF ? 0.0f : mm;
-      const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
-      cs.l = cs.l * fs + lp * fp;
-      cs.m = mm;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
-    }
-    if (half > 1) __syncthreads();
-  }
-
-  if (tl == 0 && col_ok) {
-    if (ch.k == 1 && !a.force_partial) {
-      const float inv = 1.0f / cs.l;
-      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4_t v = {cs.acc[dt][4 * j] * inv, cs.acc[dt][4 * j + 1] * inv, cs.acc[dt][4 * j + 2] * inv,
-                       cs.acc[dt][4 * j + 3] * inv};
-          *reinterpret_cast<f32x4_t*>(o + 32 * dt + 8 * j + 4 * hh) = v;
-        }
-    } else {
-      float* slot = a.part + (int64_t)w * a.slot_stride;
-      if (hh == 0) {
-        slot[c] = cs.m;
-        slot[a.rpad + c] = cs.l;
-      }
-      float* acc = slot + 2 * a.rpad + (int64_t)c * D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4_t v = {cs.acc[dt][4 * j], cs.acc[dt][4 * j + 1], cs.acc[dt][4 * j + 2], cs.acc[dt][4 * j + 3]};
-          *reinterpret_cast<f32x4_t*>(acc + 32 * dt + 8 * j + 4 * hh) = v;
-        }
-    }
-  }
+  combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
 
 // ---- merge of split partials -------------------------------------------------------
@@ -525,7 +358,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
 // workgroup covered whole were finished by the partial kernel and are
 // skipped.  The partials' maxima and sums are reduced across the wave; each
 // lane then accumulates D/64 output dimensions over the partials.
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   constexpr int EL = D / 64;
   const int hkv = a.lay.hkv;
@@ -562,10 +395,36 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
     for (int e = 0; e < EL; ++e) acc[e] += src[e] * f;
   }
   const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] *= inv;
+  if constexpr (ROT) {
+    // o = Pi^T o' = D H o' / sqrt(d): Walsh-Hadamard butterflies over the
+    // wave (lane owns dims lane*EL ..), then the signs and the scale
+#pragma unroll
+    for (int hs = 1; hs < EL; hs <<= 1)
+#pragma unroll
+      for (int e = 0; e < EL; ++e)
+        if (!(e & hs)) {
+          const float x = acc[e], y = acc[e + hs];
+          acc[e] = x + y;
+          acc[e + hs] = x - y;
+        }
+#pragma unroll
+    for (int hl = 1; hl < 64; hl <<= 1) {
+      const bool upper = (lane & hl) != 0;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const float pv = __shfl_xor(acc[e], hl);
+        acc[e] = upper ? (pv - acc[e]) : (acc[e] + pv);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] *= (a.signs[lane * EL + e] < 0 ? -a.inv_sqrt_d : a.inv_sqrt_d);
+  }
   const int row_i = c / a.g, head_j = c - row_i * a.g;
   float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;
 #pragma unroll
-  for (int e = 0; e < EL; ++e) o[e] = acc[e] * inv;
+  for (int e = 0; e < EL; ++e) o[e] = acc[e];
 }
 
 // ---- launchers ----------------------------------------------------------------------
@@ -605,21 +464,22 @@ hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s) {
   const int blocks = a.n_seqs * a.lay.hkv * a.rpad;
   if (blocks <= 0) return hipSuccess;
   const int d = a.lay.d;
-  if (d == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(64), 0, s, a);
+  const bool rot = a.lay.fmt == 2;
+  dim3 grid(blocks), block(64);
+  if (d == 64 && rot)
+    hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, s, a);
+  else if (d == 64)
+    hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, s, a);
+  else if (d == 128 && rot)
+    hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, s, a);
   else if (d == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(64), 0, s, a);
-  else if (d == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, dim3(blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, s, a);
+  else if (d == 256 && !rot)
+    hipLaunchKernelGGL((merge_kernel<256, false>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
-  (void)a;
-  (void)s;
-  return hipErrorNotSupported;
-}
 
 }  // namespace svattn

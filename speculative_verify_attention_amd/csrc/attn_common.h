@@ -1,0 +1,213 @@
+// attn_common.h - device helpers shared by the verify-attention kernels:
+// vector types, exp2, the branch-free tanh of the soft cap, work lookup
+// (which chunk of which (sequence, kv head) pair a workgroup owns), the
+// online-softmax state and update, and the combine/store epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace svattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define NEG_INF (-__builtin_inff())
+
+// Depth of the register ring of 16 KiB tiles (tiles in flight + 1), and the
+// waves per SIMD the bf16 kernels at d <= 128 are compiled for.
+#ifndef SVATTN_NBUF
+#define SVATTN_NBUF 2
+#endif
+#ifndef SVATTN_BF16_WAVES
+#define SVATTN_BF16_WAVES 1
+#endif
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh without branches, for the soft cap: an odd Taylor polynomial below
+// |x| = 0.55 (truncation below 2e-7 relative there) and 1 - 2 / (e^{2|x|} + 1)
+// above, where the subtraction loses no more than a few ulp.
+__device__ __forceinline__ float tanh_nb(float x) {
+  const float ax = fabsf(x);
+  const float x2 = x * x;
+  float p = 929569.0f / 638512875.0f;
+  p = fmaf(p, x2, -21844.0f / 6081075.0f);
+  p = fmaf(p, x2, 1382.0f / 155925.0f);
+  p = fmaf(p, x2, -62.0f / 2835.0f);
+  p = fmaf(p, x2, 17.0f / 315.0f);
+  p = fmaf(p, x2, -2.0f / 15.0f);
+  p = fmaf(p, x2, 1.0f / 3.0f);
+  const float small = fmaf(-x * x2, p, x);
+  const float e = fast_exp2(ax * 2.8853900817779268f);  // e^{2|x|}
+  const float big = copysignf(1.0f - 2.0f / (e + 1.0f), x);
+  return ax < 0.55f ? small : big;
+}
+
+__device__ __forceinline__ int find_seq(const int32_t* base, int n, int f) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= f)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Online-softmax state of one lane: column c's running reference max m (log2
+// units, equal in both half-waves), this lane's partial sum l, and its part
+// of the column's O^T accumulator.
+template <int D>
+struct ColState {
+  float m, l;
+  f32x16_t acc[D / 32];
+};
+
+// Online-softmax update of one tile's scores p (log2 units, -inf = masked):
+// row maxima over the two half-waves, lazy move of the reference max (only
+// when the tile max exceeds it by more than 2^8, so probabilities stay below
+// 256 and rescales are rare), then p <- 2^(p - m) and the running sum.
+template <int D, int NSUB>
+__device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB][16]) {
+  float mt = NEG_INF;
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // move the reference only when the tile max exceeds it by more than 2^8,
+  // so probabilities stay below 256 and rescales are rare
+  const bool up = mt > cs.m + 8.0f;
+  if (__builtin_amdgcn_ballot_w64(up)) {
+    // lanes that move: alpha = 2^(m_old - m_new), 0 when nothing was seen yet;
+    // lanes that stay keep alpha = 1 (their m may still be -inf)
+    const float alpha = up ? fast_exp2(cs.m - mt) : 1.0f;
+    cs.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) cs.acc[dt] *= alpha;
+    cs.m = up ? mt : cs.m;
+  }
+  const float m_use = cs.m == NEG_INF ? 0.0f : cs.m;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int st = 0; st < NSUB; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(p[st][r] - m_use);
+      p[st][r] = e;
+      lsum += e;
+    }
+  cs.l += lsum;
+}
+
+// Chunk of workgroup w: sequence index s, kv head h, tiles [t_begin, t_end)
+// of the pair, out of nt, split into k chunks.
+struct Chunk {
+  int s, h, k, nt, tlo, t_begin, t_end;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
+  Chunk c;
+  c.s = find_seq(a.wg_base, a.n_seqs, w);
+  c.k = a.ksplit[c.s];
+  const int local = w - a.wg_base[c.s];
+  c.h = local / c.k;
+  const int part = local - c.h * c.k;
+  const int L = a.len[c.s], n = a.nrows[c.s];
+  const int tk = a.tile_keys;
+  const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
+  c.tlo = klo / tk;
+  c.nt = (L + tk - 1) / tk - c.tlo;
+  const int cs = (c.nt + c.k - 1) / c.k;
+  c.t_begin = part * cs;
+  c.t_end = min(c.nt, c.t_begin + cs);
+  return c;
+}
+
+// Combine the token lanes of each column group through LDS, then either
+// write the normalized output (the pair was one chunk) or the chunk's
+// partial (m, l, acc) into its slot for the merge.
+template <int D, int NCT>
+struct CombineBuf {
+  static constexpr int TL = 4 / NCT;
+  static constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
+  static constexpr int FLOATS = NCT * (TL / 2) * CSTRIDE;
+};
+
+template <int D, int NCT>
+__device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, const AttnArgs& a, int w, int k,
+                                                  int s, int h, int row_i, int head_j, bool col_ok, int lane,
+                                                  int ct, int tl) {
+  constexpr int TL = 4 / NCT;
+  constexpr int NDT = D / 32;
+  constexpr int CSTRIDE = CombineBuf<D, NCT>::CSTRIDE;
+  const int col = lane & 31, hh = lane >> 5;
+  const int c = ct * 32 + col;
+  cs.l += __shfl_xor(cs.l, 32);
+#pragma unroll
+  for (int half = TL / 2; half >= 1; half >>= 1) {
+    if (tl >= half && tl < 2 * half) {
+      float* slot = cbuf + (ct * (TL / 2) + (tl - half)) * CSTRIDE;
+      if (hh == 0) {
+        slot[col] = cs.m;
+        slot[32 + col] = cs.l;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
+    }
+    __syncthreads();
+    if (tl < half) {
+      const float* slot = cbuf + (ct * (TL / 2) + tl) * CSTRIDE;
+      const float mp = slot[col], lp = slot[32 + col];
+      const float mm = fmaxf(cs.m, mp);
+      const float mu = mm == NEG_INF ? 0.0f : mm;
+      const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
+      cs.l = cs.l * fs + lp * fp;
+      cs.m = mm;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
+    }
+    if (half > 1) __syncthreads();
+  }
+
+  if (tl == 0 && col_ok) {
+    if (k == 1 && !a.force_partial) {
+      const float inv = 1.0f / cs.l;
+      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t v = {cs.acc[dt][4 * j] * inv, cs.acc[dt][4 * j + 1] * inv, cs.acc[dt][4 * j + 2] * inv,
+                       cs.acc[dt][4 * j + 3] * inv};
+          *reinterpret_cast<f32x4_t*>(o + 32 * dt + 8 * j + 4 * hh) = v;
+        }
+    } else {
+      float* slot = a.part + (int64_t)w * a.slot_stride;
+      if (hh == 0) {
+        slot[c] = cs.m;
+        slot[a.rpad + c] = cs.l;
+      }
+      float* acc = slot + 2 * a.rpad + (int64_t)c * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t v = {cs.acc[dt][4 * j], cs.acc[dt][4 * j + 1], cs.acc[dt][4 * j + 2], cs.acc[dt][4 * j + 3]};
+          *reinterpret_cast<f32x4_t*>(acc + 32 * dt + 8 * j + 4 * hh) = v;
+        }
+    }
+  }
+}
+
+}  // namespace svattn

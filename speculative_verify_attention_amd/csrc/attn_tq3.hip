@@ -1,0 +1,363 @@
+// attn_tq3.hip - verify attention over the compressed (TQ3) cache on gfx950:
+// the query rotation and the dequantize-inside-attention partial kernel.
+//
+// SwiftLM page, TurboQuant KV-cache compression passage: keys are 3-bit
+// Lloyd-Max codes plus a 1-bit QJL residual, values 3-bit codes; the codes
+// are dequantized inside the attention kernel.  The scores use the factored
+// form of the decoded key,
+//   <q, k> = n16/sqrt(d) <q', c16[code]> + g16 sqrt(pi/2)/d <q'', b>,
+// with q' = Pi q and q'' = S q' computed once per query (the rotation is
+// applied to the few queries, not to the many keys); values are accumulated
+// in the rotated frame with their norm folded into the probability, and the
+// merge rotates the result back (o = Pi^T o').
+//
+// Layout and work split follow the plain kernel: one chunk of 32-key
+// sub-tiles of one (sequence, kv head) per workgroup, 4 token-lane waves,
+// keys as the MFMA M dimension.  Every wave-wide load reads contiguous
+// memory: 1 KiB per 4 key k-steps, 768 B per two value d-tiles, and the
+// 192-byte scales.  Codes become fp16 operands through two small LDS tables:
+// one byte of key nibbles -> (2 levels, 2 signs), 6 bits of value codes ->
+// 2 levels.  Products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation;
+// in precise mode q', q'' and the probabilities are each split into two fp16
+// parts (hi + lo, ~2^-22 relative) while the code levels and signs are exact
+// in fp16.
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+#include "kernels.h"
+
+namespace svattn {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---- query rotation --------------------------------------------------------------
+
+// One wave per query vector: q' = H (D q) / sqrt(d) with an in-register
+// Walsh-Hadamard transform, then q'' = S q' (S read transposed, coalesced).
+template <int D>
+__global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
+  constexpr int E = D / 64;
+  __shared__ float buf[4][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t vec = (int64_t)blockIdx.x * 4 + wave;
+  if (vec >= a.n_vec) return;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane * E + e;
+    const float x = a.q[vec * D + i];
+    v[e] = a.signs[i] < 0 ? -x : x;
+  }
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!(e & h)) {
+        const float x = v[e], y = v[e + h];
+        v[e] = x + y;
+        v[e + h] = x - y;
+      }
+#pragma unroll
+  for (int hl = 1; hl < 64; hl <<= 1) {
+    const bool upper = (lane & hl) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float p = __shfl_xor(v[e], hl);
+      v[e] = upper ? (p - v[e]) : (v[e] + p);
+    }
+  }
+  const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] *= inv;
+    a.q1[vec * D + lane * E + e] = v[e];
+    buf[wave][lane * E + e] = v[e];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int j = 0; j < D; ++j) {
+    const float qj = buf[wave][j];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(a.s_t[j * D + lane * E + e], qj, acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) a.q2[vec * D + lane * E + e] = acc[e];
+}
+
+hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
+  if (a.n_vec <= 0) return hipSuccess;
+  dim3 grid((a.n_vec + 3) / 4);
+  if (a.d == 64)
+    hipLaunchKernelGGL(qprep_kernel<64>, grid, dim3(256), 0, s, a);
+  else if (a.d == 128)
+    hipLaunchKernelGGL(qprep_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---- the partial kernel ----------------------------------------------------------
+
+// Raw bytes of one 32-key sub-tile for this lane.
+template <int D>
+struct TQ3Regs {
+  u32x4_t kc[D / 64];     // key nibbles, 4 k-steps per plane
+  uint32_t vc[D / 64][3]; // value codes, 2 d-tiles per plane
+  uint32_t sc;            // scales dword `lane` (lanes 0..47)
+};
+
+template <int D>
+__device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restrict__ sub, int lane) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    t.kc[j] = *reinterpret_cast<const u32x4_t*>(sub + j * 1024 + lane * 16);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(sub + 16 * D + j * 768 + lane * 12);
+    t.vc[j][0] = vp[0];
+    t.vc[j][1] = vp[1];
+    t.vc[j][2] = vp[2];
+  }
+  t.sc = lane < 48 ? *reinterpret_cast<const uint32_t*>(sub + 28 * D + lane * 4) : 0u;
+}
+
+// fp16 fragments of one query vector part (k-step kk holds dims 16kk + 8hh .. +8).
+template <int D, int P2>
+struct TQ3Query {
+  f16x8_t hi[D / 16];
+  f16x8_t lo[P2 == 2 ? D / 16 : 1];
+  __device__ __forceinline__ void load(const float* q, bool ok, int hh) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      f16x8_t h{}, l{};
+      if (ok) {
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? x0[e] : x1[e - 4];
+          const _Float16 hx = (_Float16)x;
+          h[e] = hx;
+          l[e] = (_Float16)(x - (float)hx);
+        }
+      }
+      hi[kk] = h;
+      if constexpr (P2 == 2) lo[kk] = l;
+    }
+  }
+};
+
+template <int D, int P2, bool CAP>
+__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const TQ3Query<D, P2>& q1,
+                                            const TQ3Query<D, P2>& q2, const u32x2_t* __restrict__ klut,
+                                            const uint32_t* __restrict__ vlut, uint32_t* scl, const AttnArgs& a,
+                                            int key0, int L, int n, int ppos, int lane) {
+  const int hh = lane >> 5;
+  // scales of this half: K norm, K residual norm, V norm for score registers r
+  if (lane < 48) scl[lane] = t.sc;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  _Float16 sh[3][16];
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    const u32x4_t x0 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2];
+    const u32x4_t x1 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2 + 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sh[f][2 * j] = __builtin_bit_cast(_Float16, (uint16_t)(x0[j] & 0xFFFF));
+      sh[f][2 * j + 1] = __builtin_bit_cast(_Float16, (uint16_t)(x0[j] >> 16));
+      sh[f][8 + 2 * j] = __builtin_bit_cast(_Float16, (uint16_t)(x1[j] & 0xFFFF));
+      sh[f][8 + 2 * j + 1] = __builtin_bit_cast(_Float16, (uint16_t)(x1[j] >> 16));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // S1 = <q', c16[code]>, S2 = <q'', b> for the 32 keys of the sub-tile
+  f32x16_t s1 = {}, s2 = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint32_t w = t.kc[kk >> 2][kk & 3];
+    u32x4_t mse, qjl;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const u32x2_t e = klut[(w >> (8 * b)) & 0xFF];
+      mse[b] = e[0];
+      qjl[b] = e[1];
+    }
+    const f16x8_t km = __builtin_bit_cast(f16x8_t, mse), kq = __builtin_bit_cast(f16x8_t, qjl);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, q1.hi[kk], s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, q2.hi[kk], s2, 0, 0, 0);
+    if constexpr (P2 == 2) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, q1.lo[kk], s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, q2.lo[kk], s2, 0, 0, 0);
+    }
+  }
+  float p[1][16];
+  float nv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = s1[r] * ((float)sh[0][r] * a.scale * a.inv_sqrt_d) + s2[r] * ((float)sh[1][r] * a.scale * a.qjl_coef);
+    if constexpr (CAP) x = a.softcap * tanh_nb(x * a.inv_softcap);
+    p[0][r] = x * 1.4426950408889634f;
+    nv[r] = (float)sh[2][r] * a.inv_sqrt_d;
+  }
+  const bool full = key0 + 32 <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
+  if (!full) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kp = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool vis = kp <= ppos && (a.window == 0 || ppos - kp < a.window);
+      p[0][r] = vis ? p[0][r] : NEG_INF;
+      nv[r] = kp < L ? nv[r] : 0.0f;  // slots past the end may hold any bits
+    }
+  }
+  softmax_update<D, 1>(cs, p);
+  // O'^T += C16[vcode]^T (P * n16v / sqrt(d))^T
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    f16x8_t phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = p[0][8 * v + e] * nv[8 * v + e];
+      const _Float16 hx = (_Float16)x;
+      phi[e] = hx;
+      plo[e] = (_Float16)(x - (float)hx);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const uint32_t* w3 = t.vc[dt >> 1];
+      // the 48-bit field of this d-tile; codes 8v .. 8v+7 start at bit 24v
+      const uint64_t field = (dt & 1) ? ((uint64_t)(w3[1] >> 16) | ((uint64_t)w3[2] << 16))
+                                      : ((uint64_t)w3[0] | ((uint64_t)(w3[1] & 0xFFFF) << 32));
+      const uint32_t bits = (uint32_t)(field >> (24 * v));
+      u32x4_t vv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vv[q] = vlut[(bits >> (6 * q)) & 63];
+      const f16x8_t vop = __builtin_bit_cast(f16x8_t, vv);
+      cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, phi, cs.acc[dt], 0, 0, 0);
+      if constexpr (P2 == 2) cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int NCT, int P2, bool CAP>
+__global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
+  constexpr int TL = 4 / NCT;
+  constexpr int NDT = D / 32;
+  constexpr int SB = tq3_sub_bytes(D);
+  constexpr int NBUF = 4;
+  __shared__ float cbuf[CombineBuf<D, NCT>::FLOATS];
+  __shared__ u32x2_t klut[256];
+  __shared__ uint32_t vlut[64];
+  __shared__ __align__(16) uint32_t scl[4][48];
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform by construction; readfirstlane makes the compiler see it, so
+  // tile indices and block-table reads stay scalar (no wait on vector loads)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ct = wave % NCT, tl = wave / NCT;
+  const int col = lane & 31, hh = lane >> 5;
+  const int c = ct * 32 + col;
+  const int w = blockIdx.x;
+  const Chunk ch = chunk_of(a, w);
+  const int s = ch.s, h = ch.h, tlo = ch.tlo;
+  const int L = a.len[s], n = a.nrows[s];
+  const int R = n * a.g;
+  const bool col_ok = c < R;
+  const int row_i = col_ok ? c / a.g : 0;
+  const int head_j = col_ok ? c - row_i * a.g : 0;
+  const int ppos = L - n + row_i;
+
+  const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
+  auto sub_of = [&](int t) {
+    const int key0 = (tlo + t) * 32;
+    return a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + ((int64_t)h * 8 + ((key0 & 255) >> 5)) * SB;
+  };
+  const int t_first = ch.t_begin + tl;
+  const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
+  TQ3Regs<D> buf[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < cnt) load_tq3<D>(buf[j], sub_of(t_first + j * TL), lane);
+
+  // decode tables: key byte (two nibbles code | sign << 3) -> (levels, signs);
+  // 6 bits of value codes -> 2 levels
+  {
+    // the 8 levels through constant indices (scalar reads of the arguments),
+    // then picked per thread
+    uint32_t lv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lv[j] = a.lev16_bits[j];
+    auto level = [&](uint32_t code) {
+      uint32_t r = lv[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) r = code == (uint32_t)j ? lv[j] : r;
+      return r;
+    };
+    const int i = threadIdx.x;
+    const uint32_t lo = i & 15, hi = i >> 4;
+    const uint32_t lev = level(lo & 7) | (level(hi & 7) << 16);
+    const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
+    klut[i] = u32x2_t{lev, sg};
+    if (i < 64) vlut[i] = level(i & 7) | (level(i >> 3) << 16);
+  }
+  const float* qoff = a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+  const float* q2off = a.q2 + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+  TQ3Query<D, P2> q1, q2;
+  q1.load(qoff, col_ok, hh);
+  q2.load(q2off, col_ok, hh);
+  __syncthreads();
+
+  ColState<D> cs;
+  cs.m = NEG_INF;
+  cs.l = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
+
+  for (int i = 0; i < cnt; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int k = i + u;
+      if (k < cnt) {
+        if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
+        process_tq3<D, P2, CAP>(cs, buf[u], q1, q2, klut, vlut, scl[wave], a, (tlo + t_first + k * TL) * 32, L, n,
+                                ppos, lane);
+      }
+    }
+  }
+  combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
+}
+
+template <int D, int NCT>
+static hipError_t launch_tq3_dn(const AttnArgs& a, bool precise, hipStream_t s) {
+  const bool cap = a.softcap > 0.0f;
+  dim3 grid(a.n_wg), block(256);
+  if (precise) {
+    if (cap)
+      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, false>), grid, block, 0, s, a);
+  } else {
+    if (cap)
+      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 1, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 1, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_tq3(const AttnArgs& a, int nct, bool precise, hipStream_t s) {
+  if (a.n_wg <= 0) return hipSuccess;
+  const int d = a.lay.d;
+  if (d == 64) return nct == 1 ? launch_tq3_dn<64, 1>(a, precise, s) : launch_tq3_dn<64, 2>(a, precise, s);
+  if (d == 128) return nct == 1 ? launch_tq3_dn<128, 1>(a, precise, s) : launch_tq3_dn<128, 2>(a, precise, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace svattn

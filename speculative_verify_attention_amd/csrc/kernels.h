@@ -22,18 +22,19 @@ namespace svattn {
 //                   (v, dt, h, r, e) = V[16v + 8(e>>2) + 4h + (e&3)][32dt + r]
 //  FP32 K sub-tile: [d/8][2][32][4]: (kq, h, m, e) = K[m][(d/2)h + 4kq + e]
 //  FP32 V sub-tile: [4][d/32][2][32][4]: (uq, dt, h, r, e) = V[8uq + 4h + e][32dt + r]
-//  TQ3:
-//    K codes  [hkv][256][d/2]  (nibble = code | sign << 3, dim i in nibble i)
-//    K n16    [hkv][256]  fp16
-//    K g16    [hkv][256]  fp16
-//    V codes  [hkv][4][d][24 bytes]  (64 tokens x 3 bits, token t at bits 3t)
-//    V n16    [hkv][256]  fp16
+//  TQ3: per head, 8 sub-tiles of 32 tokens, each of 28 d + 192 bytes:
+//    K codes [d/64][64 lanes][16 B]: lane 32h + m, its 16 bytes = 4 k-steps
+//      kk = 4j..4j+3, 4 bytes each = nibbles of dims 16kk + 8h + e
+//      (e = 0..7, nibble e at bits 4e), nibble = code | sign << 3;
+//    V codes [d/64][64 lanes][12 B]: lane 32h + r, bytes 0-5 for d-tile 2j,
+//      6-11 for 2j+1; in each 48-bit field 16 codes at bits 3q, q = 0..15,
+//      q <-> token 16(q>>3) + 8((q&7)>>2) + 4h + (q&3), dimension 32dt + r;
+//    scales [2 halves][3 fields][16] fp16: fields K norm, K residual norm,
+//      V norm; half h, index i <-> token 8(i>>2) + 4h + (i&3).
 struct PoolLayout {
   int32_t fmt, hkv, d;
   int64_t block_bytes;
-  int64_t k_off, v_off;            // FP32/BF16
-  int64_t kc_off, kn_off, kg_off;  // TQ3
-  int64_t vc_off, vn_off;          // TQ3
+  int64_t k_off, v_off;  // FP32/BF16 regions (TQ3: one region of 8 sub-tiles per head)
 };
 
 // Element offset of (token slot j in 0..255, dimension d) inside one head's
@@ -57,7 +58,29 @@ __host__ __device__ inline int64_t plain_v_index(int fmt, int D, int j, int d) {
 
 // Keys per attention tile (one wavefront iteration): 16 KiB of bf16 K and V
 // at d <= 128, one 32-key sub-tile otherwise.
-constexpr int tile_keys(int fmt, int d) { return fmt == 1 ? 32 * (128 / d > 1 ? 128 / d : 1) : fmt == 0 ? 32 : 64; }
+constexpr int tile_keys(int fmt, int d) { return fmt == 1 ? 32 * (128 / d > 1 ? 128 / d : 1) : 32; }
+
+// Bytes of one 32-token TQ3 sub-tile of one head.
+__host__ __device__ constexpr int tq3_sub_bytes(int d) { return 28 * d + 192; }
+// Byte (and nibble) of key dimension i of sub-tile token m.
+__host__ __device__ inline int tq3_k_byte(int d, int m, int i, int* nibble) {
+  const int kk = i >> 4, h = (i >> 3) & 1, e = i & 7;
+  *nibble = e & 1;
+  return (kk >> 2) * 1024 + (32 * h + m) * 16 + (kk & 3) * 4 + (e >> 1);
+}
+// Byte offset of the 48-bit V field holding dimension i of token t (0..31),
+// and the code's bit position inside that field.
+__host__ __device__ inline int tq3_v_field(int d, int t, int i, int* bit) {
+  const int v = t >> 4, h = (t >> 2) & 1, q = 8 * v + 4 * ((t >> 3) & 1) + (t & 3);
+  const int dt = i >> 5, r = i & 31;
+  *bit = 3 * q;
+  return 16 * d + (dt >> 1) * 768 + (32 * h + r) * 12 + (dt & 1) * 6;
+}
+// Byte offset of scale field f (0 K norm, 1 K residual norm, 2 V norm) of token t.
+__host__ __device__ inline int tq3_scale_byte(int d, int t, int f) {
+  const int h = (t >> 2) & 1, i = 4 * (t >> 3) + (t & 3);
+  return 28 * d + (h * 3 + f) * 32 + i * 2;
+}
 
 PoolLayout make_layout(int fmt, int hkv, int d);
 
@@ -121,6 +144,7 @@ constexpr int kMaxAttnSeqs = 128;
 struct AttnArgs {
   const uint8_t* pool;
   const int32_t* table;
+  const int8_t* signs;  // TQ3: rotation signs D (merge applies Pi^T)
   const float* q;    // [rows][hq][d] (TQ3: q' = Pi q)
   const float* q2;   // TQ3: q'' = S Pi q
   float* out;        // [rows][hq][d]
@@ -162,6 +186,9 @@ static_assert(sizeof(TableUpdateArgs) <= 4096, "kernel arguments must fit the 4 
 
 hipError_t launch_attn(const AttnArgs& a, int nct, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s);
+// TQ3: the query rotation, and the partial kernel with two-part (hi + lo)
+// fp16 operands when precise, one fp16 part otherwise.
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
+hipError_t launch_attn_tq3(const AttnArgs& a, int nct, bool precise, hipStream_t s);
 
 }  // namespace svattn

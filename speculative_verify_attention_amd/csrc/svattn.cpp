@@ -45,6 +45,11 @@ constexpr size_t kAlign = 256;
 #ifndef SVATTN_WG_PER_CALL_D256
 #define SVATTN_WG_PER_CALL_D256 256
 #endif
+// TQ3 calls whose every row sees at least this many keys use one-part fp16
+// operands (two-part below it).
+#ifndef SVATTN_TQ3_FAST_KEYS
+#define SVATTN_TQ3_FAST_KEYS 65536
+#endif
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MetaLayout {
@@ -318,7 +323,7 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
     int64_t units = 0;
     while (i < segs.size() && a.n_segs < kMaxAppendSegs) {
       const AppendSeg& g = *segs[i];
-      const int64_t u = tq3 ? (int64_t)((g.pos0 + g.n - 1) / 64 - g.pos0 / 64 + 1) : g.n;
+      const int64_t u = tq3 ? (int64_t)((g.pos0 + g.n - 1) / 32 - g.pos0 / 32 + 1) : g.n;
       if (units + u > (int64_t)INT32_MAX / 2 && a.n_segs > 0) break;
       a.unit0[a.n_segs] = (int32_t)units;
       a.seq[a.n_segs] = g.seq;
@@ -435,8 +440,37 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   if (vp.total > 0 && (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return set_err(c, KV_EINVAL, "workspace must be non-null and 256-byte aligned");
   const CoreParams& P = c->core.params();
-  if (P.format == KV_TQ3) return set_err(c, KV_EINVAL, "KV_TQ3 attention not available in this build");
+  const bool tq3 = P.format == KV_TQ3;
+  if (tq3 && P.head_dim > 128) return set_err(c, KV_EINVAL, "KV_TQ3 attention supports head_dim 64 and 128");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // TQ3: the rotated queries q' = Pi q and q'' = S q' live after the partials
+  float* q1 = nullptr;
+  float* q2 = nullptr;
+  bool precise = true;
+  if (tq3) {
+    q1 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes);
+    q2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes + vp.q_bytes);
+    // two-part fp16 operands unless every row sees many keys (errors of the
+    // one-part products average out over the keys)
+    int min_keys = INT32_MAX;
+    for (int i = 0; i < n_seqs; ++i) {
+      int32_t len;
+      c->core.seq_len(seq_ids[i], &len);
+      const int lo = window > 0 ? std::max(0, len - n_rows[i] - window + 1) : 0;
+      min_keys = std::min(min_keys, len - n_rows[i] + 1 - lo);
+    }
+    precise = min_keys < SVATTN_TQ3_FAST_KEYS;
+    QPrepArgs qa;
+    qa.q = q;
+    qa.q1 = q1;
+    qa.q2 = q2;
+    qa.signs = c->dsigns;
+    qa.s_t = c->ds_t;
+    qa.n_vec = (int32_t)(vp.rows * num_q_heads);
+    qa.d = P.head_dim;
+    hipError_t e = launch_qprep(qa, s);
+    if (e != hipSuccess) return hip_fail(c, e, "query rotation launch");
+  }
   const int g = num_q_heads / P.num_kv_heads;
   std::vector<AttnArgs> args(vp.launches.size());
   std::vector<char> split(vp.launches.size(), 0);
@@ -446,7 +480,12 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     std::memset(&a, 0, sizeof(a));
     a.pool = c->pool;
     a.table = c->dtable;
-    a.q = q;
+    a.signs = c->dsigns;
+    a.q = tq3 ? q1 : q;
+    a.q2 = q2;
+    a.inv_sqrt_d = 1.0f / std::sqrt((float)P.head_dim);
+    a.qjl_coef = (float)(std::sqrt(M_PI / 2.0) / P.head_dim);
+    for (int j = 0; j < 8; ++j) a.lev16_bits[j] = tq3 ? c->core.codec().levels16_bits[j] : 0;
     a.out = out;
     a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace)) + L.slot0 * vp.slot_stride;
     a.lay = c->lay;
@@ -461,9 +500,9 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.n_wg = L.n_wg;
     a.slot_stride = (int32_t)vp.slot_stride;
     a.rpad = vp.rpad;
-    a.force_partial = 0;
+    a.force_partial = tq3 ? 1 : 0;  // the merge rotates TQ3 outputs back
     a.tile_keys = tile_keys(P.format, P.head_dim);
-    bool any_split = false;
+    bool any_split = tq3;
     for (int i = 0; i < L.count; ++i) {
       const int ci = vp.order[L.first + i];
       const int sid = seq_ids[ci];
@@ -481,7 +520,8 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   }
   hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, s);
-  for (size_t li = 0; li < args.size() && e == hipSuccess; ++li) e = launch_attn(args[li], vp.nct, s);
+  for (size_t li = 0; li < args.size() && e == hipSuccess; ++li)
+    e = tq3 ? launch_attn_tq3(args[li], vp.nct, precise, s) : launch_attn(args[li], vp.nct, s);
   if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, s);
   if (e != hipSuccess) return hip_fail(c, e, "attention launch");
   for (size_t li = 0; li < args.size(); ++li) {

@@ -217,3 +217,26 @@ def test_codec_draw_statistics():
     assert abs(flat.var() - 1.0) <= 5 * math.sqrt(2.0 / n)
     # Gaussian fourth moment 3
     assert abs(np.mean(flat ** 4) - 3.0) <= 5 * math.sqrt(96.0 / n)
+
+
+def test_batch_encode_decode_match_per_vector(codec128):
+    _, s, pi, _, c16, t = codec128
+    rng = np.random.default_rng(9)
+    xs = rng.standard_normal((64, 128)) * rng.uniform(0.2, 5, size=(64, 1))
+    xs[3] = 0.0
+    for is_key in (True, False):
+        batch = tq3.encode_batch(xs, is_key, pi, s, c16, t, chunk=17)
+        for i, x in enumerate(xs):
+            one = tq3.encode(x, is_key, pi, s, c16, t)
+            assert np.array_equal(batch["code"][i], one["code"])
+            assert batch["n16"][i] == one["n16"]
+            if is_key:
+                assert np.array_equal(batch["bits"][i], one["bits"])
+                assert batch["g16"][i] == one["g16"]
+                kb = tq3.decode_keys(batch["code"][i:i + 1], batch["bits"][i:i + 1], batch["n16"][i:i + 1],
+                                     batch["g16"][i:i + 1], pi, s, c16)[0]
+                ko = tq3.decode_key(one["code"], one["bits"], one["n16"], one["g16"], pi, s, c16)
+                assert np.allclose(kb, ko, rtol=0, atol=1e-12)
+            else:
+                vb = tq3.decode_values(batch["code"][i:i + 1], batch["n16"][i:i + 1], pi, c16)[0]
+                assert np.allclose(vb, tq3.decode_value(one["code"], one["n16"], pi, c16), rtol=0, atol=1e-12)
