@@ -280,17 +280,83 @@ def run(args, name):
 
 
 def copy_probe(nbytes=1 << 30):
-    """A plain device-to-device copy of known size (for scaling the HBM
-    byte counters)."""
+    """A plain elementwise copy of known size (reads nbytes, writes nbytes),
+    run before the timed steps so that a counter run can scale the attention
+    kernel's HBM byte counters by what they read for a known stream."""
     import torch
 
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
-    a.fill_(1)
     torch.cuda.synchronize()
-    b.copy_(a)
+    torch.mul(a, 1, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_trace(directory, workload, cmd, out_path=None):
+    """profiles/attn_kernel_<workload>_trace.txt from a rocprofv3 --kernel-trace
+    --stats run: the library's kernels with calls and durations."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    out = [f"# rocprofv3 --kernel-trace --stats summary, workload {workload}",
+           f"# command: {cmd}", "# name | calls | average_us | min_us | max_us | percent_of_gpu_time"]
+    for r in rows:
+        name = r["Name"]
+        if "svattn::" not in name:
+            continue
+        out.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}")
+    path = out_path or os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_trace.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_bytes, out_path=None):
+    """profiles/attn_kernel_<workload>_pmc.txt from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the 1 GiB copy probe."""
+    def per_kernel(directory, counter):
+        acc = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            k = r["Kernel_Name"]
+            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        return acc
+
+    kib = (1 << 30) / 1024.0
+    res = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc = per_kernel(directory, counter)
+        attn = [v for k, vs in acc.items() if "attn_kernel" in k or "attn_tq3_kernel" in k for v in vs]
+        copy = [v for k, vs in acc.items() if "MulFunctor" in k or "mul" in k.lower() and "elementwise" in k
+                for v in vs if v > kib / 4]
+        res[counter] = (sum(attn) / max(1, len(attn)), max(copy) if copy else float("nan"), len(attn))
+    f_attn, f_copy, n_f = res["FETCH_SIZE"]
+    w_attn, w_copy, n_w = res["WRITE_SIZE"]
+    f_scale, w_scale = kib / f_copy, kib / w_copy
+    traffic = (f_attn * f_scale + w_attn * w_scale) * 1024.0
+    out = [f"# rocprofv3 --pmc summary for the attention kernel, workload {workload}",
+           f"# fetch command: {cmd_fetch}", f"# write command: {cmd_write}",
+           "# counters are KiB per dispatch; each is scaled by its reading for a plain copy of 1 GiB",
+           f"kernel_sources_sha256_16: {source_hash()}",
+           f"attn_dispatches_fetch: {n_f}", f"attn_dispatches_write: {n_w}",
+           f"attn_fetch_kib_avg: {f_attn:.1f}", f"copy_fetch_kib: {f_copy:.1f}", f"fetch_scale: {f_scale:.4f}",
+           f"attn_write_kib_avg: {w_attn:.1f}", f"copy_write_kib: {w_copy:.1f}", f"write_scale: {w_scale:.4f}",
+           f"alg_bytes_per_launch: {alg_bytes}", f"hbm_bytes_per_launch: {traffic:.0f}",
+           f"traffic_over_alg: {traffic / alg_bytes:.4f}"]
+    path = out_path or os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_pmc.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
 
 
 def main():
@@ -301,7 +367,21 @@ def main():
     ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB plain copy first (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write the profiles/ summary of a kernel-trace run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summary of two --pmc runs")
+    ap.add_argument("--cmd", nargs="*", default=[], help="the profiled command(s), recorded in the summary")
+    ap.add_argument("--alg-bytes", type=float, default=0.0)
+    ap.add_argument("--out", help="summary path (default: profiles/attn_kernel_<workload>_*.txt)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.workload, " ".join(args.cmd), args.out))
+        return
+    if args.summarize_pmc:
+        cmds = args.cmd + ["", ""]
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, cmds[0], cmds[1],
+                            args.alg_bytes, args.out))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
