@@ -98,12 +98,19 @@ typedef struct {
  *    V as [4][d/32][2][32][4]:    element (uq, dt, h, r, e) = V[8uq + 4h + e][32dt + r]
  *  (this order makes every wavefront-wide load of the attention kernel read
  *  1 KiB of contiguous memory straight into its matrix-core operands).
- *  KV_TQ3 (per kv head, heads one after another inside each field): K codes
- *    as [256][d/2] bytes, dimension i in nibble i (low nibble first) holding
- *    code | sign_bit << 3; K norms n16 as [256] fp16; K residual norms g16 as
- *    [256] fp16; V codes as [4][d][24 bytes], the 24 bytes holding 64 tokens'
- *    3-bit codes, token t at bits 3t..3t+2 (little-endian bit order); V norms
- *    as [256] fp16.
+ *  KV_TQ3: one region per kv head, in head order, of 8 sub-tiles of 32
+ *  tokens, each sub-tile 28 d + 192 bytes (3776 B at d=128, i.e. 118 B per
+ *  token: 68 B of key record and 50 B of value record):
+ *    K codes as [d/64][64 lanes][16 B]: lane 32h + m holds, for k-steps
+ *      kk = 4j .. 4j+3 (4 bytes each), the nibbles of dimensions
+ *      16kk + 8h + e (e = 0..7, nibble e at bits 4e) of token m; a nibble is
+ *      code | sign_bit << 3.
+ *    V codes as [d/64][64 lanes][12 B]: lane 32h + r, bytes 0-5 for d-tile
+ *      2j and 6-11 for d-tile 2j+1; each 48-bit little-endian field holds 16
+ *      3-bit codes at bits 3q (q = 0..15) of dimension 32 dt + r of tokens
+ *      16(q>>3) + 8((q&7)>>2) + 4h + (q&3).
+ *    Scales as [2 halves][3 fields][16] fp16, fields K norm n16, K residual
+ *      norm g16, V norm n16; half h, index i <-> token 8(i>>2) + 4h + (i&3).
  */
 int kv_pool_bytes(const kv_params* p, size_t* out);
 
