@@ -418,8 +418,11 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
         acc[e] = upper ? (pv - acc[e]) : (acc[e] + pv);
       }
     }
+    // 1/sqrt(d) of the rotation and 1/sqrt(d) of the value reconstruction
+    // (the partial kernel accumulates n16 * c16[code] without it)
+    constexpr float inv_d = 1.0f / D;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] *= (a.signs[lane * EL + e] < 0 ? -a.inv_sqrt_d : a.inv_sqrt_d);
+    for (int e = 0; e < EL; ++e) acc[e] *= (a.signs[lane * EL + e] < 0 ? -inv_d : inv_d);
   }
   const int row_i = c / a.g, head_j = c - row_i * a.g;
   float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;

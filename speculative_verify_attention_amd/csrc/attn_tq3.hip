@@ -124,12 +124,13 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
   t.sc = lane < 48 ? *reinterpret_cast<const uint32_t*>(sub + 28 * D + lane * 4) : 0u;
 }
 
-// fp16 fragments of one query vector part (k-step kk holds dims 16kk + 8hh .. +8).
+// fp16 fragments of one query vector part (k-step kk holds dims 16kk + 8hh .. +8),
+// multiplied by `mul` in fp32 before rounding.
 template <int D, int P2>
 struct TQ3Query {
   f16x8_t hi[D / 16];
   f16x8_t lo[P2 == 2 ? D / 16 : 1];
-  __device__ __forceinline__ void load(const float* q, bool ok, int hh) {
+  __device__ __forceinline__ void load(const float* q, float mul, bool ok, int hh) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       f16x8_t h{}, l{};
@@ -138,7 +139,7 @@ struct TQ3Query {
         const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = e < 4 ? x0[e] : x1[e - 4];
+          const float x = (e < 4 ? x0[e] : x1[e - 4]) * mul;
           const _Float16 hx = (_Float16)x;
           h[e] = hx;
           l[e] = (_Float16)(x - (float)hx);
@@ -150,33 +151,47 @@ struct TQ3Query {
   }
 };
 
+// Shared memory of the partial kernel.  The key table is indexed by (byte
+// of two key nibbles, lane slot): every lane of a 32-lane group reads its own
+// 8-byte column, so table reads never conflict on LDS banks whatever the
+// codes are.  The combine buffer reuses the table's space after the loop.
+template <int D, int NCT>
+struct TQ3Smem {
+  static constexpr int KLUT_BYTES = 256 * 32 * 8;
+  static constexpr int CBUF_BYTES = CombineBuf<D, NCT>::FLOATS * 4;
+  static constexpr int MAIN_BYTES = KLUT_BYTES > CBUF_BYTES ? KLUT_BYTES : CBUF_BYTES;
+  static constexpr int VLUT_OFF = MAIN_BYTES;
+  static constexpr int SCL_OFF = VLUT_OFF + 64 * 4;
+  static constexpr int BYTES = SCL_OFF + 4 * 48 * 4;
+};
+
 template <int D, int P2, bool CAP>
 __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const TQ3Query<D, P2>& q1,
-                                            const TQ3Query<D, P2>& q2, const u32x2_t* __restrict__ klut,
+                                            const TQ3Query<D, P2>& q2, const uint8_t* __restrict__ klut,
                                             const uint32_t* __restrict__ vlut, uint32_t* scl, const AttnArgs& a,
-                                            int key0, int L, int n, int ppos, int lane) {
+                                            int key0, int L, int n, int ppos, int lane, uint32_t slot8) {
   const int hh = lane >> 5;
-  // scales of this half: K norm, K residual norm, V norm for score registers r
+  // scales of this half (K norm, K residual norm, V norm of the keys of the
+  // lane's score registers) through the wave's LDS slice; a wave's LDS
+  // accesses execute in order, so the write is visible to the reads after it
   if (lane < 48) scl[lane] = t.sc;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  _Float16 sh[3][16];
+  uint32_t shw[3][8];
 #pragma unroll
   for (int f = 0; f < 3; ++f) {
     const u32x4_t x0 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2];
     const u32x4_t x1 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2 + 1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sh[f][2 * j] = __builtin_bit_cast(_Float16, (uint16_t)(x0[j] & 0xFFFF));
-      sh[f][2 * j + 1] = __builtin_bit_cast(_Float16, (uint16_t)(x0[j] >> 16));
-      sh[f][8 + 2 * j] = __builtin_bit_cast(_Float16, (uint16_t)(x1[j] & 0xFFFF));
-      sh[f][8 + 2 * j + 1] = __builtin_bit_cast(_Float16, (uint16_t)(x1[j] >> 16));
+      shw[f][j] = x0[j];
+      shw[f][4 + j] = x1[j];
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  auto half_of = [&](int f, int r) -> float {
+    const uint32_t w = shw[f][r >> 1];
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xFFFF)));
+  };
 
   // S1 = <q', c16[code]>, S2 = <q'', b> for the 32 keys of the sub-tile
   f32x16_t s1 = {}, s2 = {};
@@ -186,7 +201,10 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     u32x4_t mse, qjl;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const u32x2_t e = klut[(w >> (8 * b)) & 0xFF];
+      // byte b of the nibble word selects the table row; the lane's slot
+      // selects the column: address = byte * 256 + slot * 8
+      const uint32_t addr = __builtin_amdgcn_perm(w, slot8, 0x0C0C0000u | ((4u + b) << 8));
+      const u32x2_t e = *reinterpret_cast<const u32x2_t*>(klut + addr);
       mse[b] = e[0];
       qjl[b] = e[1];
     }
@@ -198,36 +216,39 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
       s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, q2.lo[kk], s2, 0, 0, 0);
     }
   }
+  // scores in log2 units (q'' already carries the QJL coefficient relative
+  // to the first term)
   float p[1][16];
-  float nv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float x = s1[r] * ((float)sh[0][r] * a.scale * a.inv_sqrt_d) + s2[r] * ((float)sh[1][r] * a.scale * a.qjl_coef);
-    if constexpr (CAP) x = a.softcap * tanh_nb(x * a.inv_softcap);
-    p[0][r] = x * 1.4426950408889634f;
-    nv[r] = (float)sh[2][r] * a.inv_sqrt_d;
+    float x = fmaf(s2[r], half_of(1, r), s1[r] * half_of(0, r)) * a.q1_mul;
+    if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
+    p[0][r] = x;
   }
   const bool full = key0 + 32 <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
+  uint32_t vmask = 0xFFFFu;  // score registers whose key lies inside the sequence
   if (!full) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kp = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       const bool vis = kp <= ppos && (a.window == 0 || ppos - kp < a.window);
       p[0][r] = vis ? p[0][r] : NEG_INF;
-      nv[r] = kp < L ? nv[r] : 0.0f;  // slots past the end may hold any bits
+      vmask &= kp < L ? 0xFFFFu : ~(1u << r);  // slots past the end may hold any bits
     }
   }
   softmax_update<D, 1>(cs, p);
-  // O'^T += C16[vcode]^T (P * n16v / sqrt(d))^T
+  // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     f16x8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = p[0][8 * v + e] * nv[8 * v + e];
+      const int r = 8 * v + e;
+      const float nvr = (vmask >> r) & 1 ? half_of(2, r) : 0.0f;
+      const float x = p[0][r] * nvr;
       const _Float16 hx = (_Float16)x;
       phi[e] = hx;
-      plo[e] = (_Float16)(x - (float)hx);
+      if constexpr (P2 == 2) plo[e] = (_Float16)(x - (float)hx);
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -252,15 +273,17 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
   constexpr int NDT = D / 32;
   constexpr int SB = tq3_sub_bytes(D);
   constexpr int NBUF = 4;
-  __shared__ float cbuf[CombineBuf<D, NCT>::FLOATS];
-  __shared__ u32x2_t klut[256];
-  __shared__ uint32_t vlut[64];
-  __shared__ __align__(16) uint32_t scl[4][48];
+  using SM = TQ3Smem<D, NCT>;
+  __shared__ __align__(16) uint8_t smem[SM::BYTES];
+  uint8_t* klut = smem;
+  float* cbuf = reinterpret_cast<float*>(smem);
+  uint32_t* vlut = reinterpret_cast<uint32_t*>(smem + SM::VLUT_OFF);
 
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane makes the compiler see it, so
   // tile indices and block-table reads stay scalar (no wait on vector loads)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 48;
   const int ct = wave % NCT, tl = wave / NCT;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
@@ -286,32 +309,31 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
   for (int j = 0; j < NBUF - 1; ++j)
     if (j < cnt) load_tq3<D>(buf[j], sub_of(t_first + j * TL), lane);
 
-  // decode tables: key byte (two nibbles code | sign << 3) -> (levels, signs);
-  // 6 bits of value codes -> 2 levels
+  // decode tables: key byte (two nibbles code | sign << 3) -> (levels, signs),
+  // one copy per lane slot; 6 bits of value codes -> 2 levels.  The 8 levels
+  // pass through LDS (the wave's scale slice, unused until the loop).
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) scl[j] = a.lev16_bits[j];  // constant indices: scalar argument reads
+  }
+  __syncthreads();
   {
-    // the 8 levels through constant indices (scalar reads of the arguments),
-    // then picked per thread
-    uint32_t lv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lv[j] = a.lev16_bits[j];
-    auto level = [&](uint32_t code) {
-      uint32_t r = lv[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) r = code == (uint32_t)j ? lv[j] : r;
-      return r;
-    };
+    const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
     const int i = threadIdx.x;
     const uint32_t lo = i & 15, hi = i >> 4;
-    const uint32_t lev = level(lo & 7) | (level(hi & 7) << 16);
+    const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
     const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-    klut[i] = u32x2_t{lev, sg};
-    if (i < 64) vlut[i] = level(i & 7) | (level(i >> 3) << 16);
+    u32x2_t* row = reinterpret_cast<u32x2_t*>(klut + i * 256);
+#pragma unroll
+    for (int sl = 0; sl < 32; ++sl) row[sl] = u32x2_t{lev, sg};
+    if (i < 64) vlut[i] = lv[i & 7] | (lv[i >> 3] << 16);
   }
   const float* qoff = a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
   const float* q2off = a.q2 + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
   TQ3Query<D, P2> q1, q2;
-  q1.load(qoff, col_ok, hh);
-  q2.load(q2off, col_ok, hh);
+  q1.load(qoff, 1.0f, col_ok, hh);
+  q2.load(q2off, a.q2_mul, col_ok, hh);
+  const uint32_t slot8 = (uint32_t)(lane & 31) * 8;
   __syncthreads();
 
   ColState<D> cs;
@@ -326,11 +348,12 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
       const int k = i + u;
       if (k < cnt) {
         if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
-        process_tq3<D, P2, CAP>(cs, buf[u], q1, q2, klut, vlut, scl[wave], a, (tlo + t_first + k * TL) * 32, L, n,
-                                ppos, lane);
+        process_tq3<D, P2, CAP>(cs, buf[u], q1, q2, klut, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos,
+                                lane, slot8);
       }
     }
   }
+  __syncthreads();  // the combine buffer overlays the key table
   combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
 

@@ -156,6 +156,13 @@ struct AttnArgs {
   float inv_softcap;
   float qjl_coef;    // TQ3: sqrt(pi/2) / d
   float inv_sqrt_d;  // TQ3
+  // TQ3 scores in log2 units: score = q1_mul (n16 <q', c16> + g16 <q2_mul q'', b>),
+  // q2_mul applied before q'' is rounded to fp16 (it keeps q'' and its
+  // low-order part within the normal fp16 range)
+  float q1_mul;      // scale * log2(e) / sqrt(d)
+  float q2_mul;      // sqrt(pi/2) / sqrt(d)
+  float cap_l2;      // softcap * log2(e) (TQ3 scores are in log2 units)
+  float inv_cap_l2;  // 1 / cap_l2
   int32_t n_seqs;
   int32_t n_wg;
   int32_t slot_stride;    // floats per partial slot

@@ -485,6 +485,10 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.q2 = q2;
     a.inv_sqrt_d = 1.0f / std::sqrt((float)P.head_dim);
     a.qjl_coef = (float)(std::sqrt(M_PI / 2.0) / P.head_dim);
+    a.q1_mul = (float)((double)scale * M_LOG2E / std::sqrt((double)P.head_dim));
+    a.q2_mul = (float)(std::sqrt(M_PI / 2.0) / std::sqrt((double)P.head_dim));
+    a.cap_l2 = (float)((double)softcap * M_LOG2E);
+    a.inv_cap_l2 = softcap > 0.0f ? (float)(1.0 / ((double)softcap * M_LOG2E)) : 0.0f;
     for (int j = 0; j < 8; ++j) a.lev16_bits[j] = tq3 ? c->core.codec().levels16_bits[j] : 0;
     a.out = out;
     a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace)) + L.slot0 * vp.slot_stride;
