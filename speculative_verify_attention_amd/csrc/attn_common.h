@@ -133,20 +133,21 @@ __device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
 // Combine the token lanes of each column group through LDS, then either
 // write the normalized output (the pair was one chunk) or the chunk's
 // partial (m, l, acc) into its slot for the merge.
-template <int D, int NCT>
+// NW waves per workgroup: NCT column groups of NW / NCT token-lane waves.
+template <int D, int NCT, int NW = 4>
 struct CombineBuf {
-  static constexpr int TL = 4 / NCT;
+  static constexpr int TL = NW / NCT;
   static constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
   static constexpr int FLOATS = NCT * (TL / 2) * CSTRIDE;
 };
 
-template <int D, int NCT>
+template <int D, int NCT, int NW = 4>
 __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, const AttnArgs& a, int w, int k,
                                                   int s, int h, int row_i, int head_j, bool col_ok, int lane,
                                                   int ct, int tl) {
-  constexpr int TL = 4 / NCT;
+  constexpr int TL = NW / NCT;
   constexpr int NDT = D / 32;
-  constexpr int CSTRIDE = CombineBuf<D, NCT>::CSTRIDE;
+  constexpr int CSTRIDE = CombineBuf<D, NCT, NW>::CSTRIDE;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
   cs.l += __shfl_xor(cs.l, 32);

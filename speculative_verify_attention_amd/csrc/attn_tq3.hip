@@ -124,72 +124,56 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
   t.sc = lane < 48 ? *reinterpret_cast<const uint32_t*>(sub + 28 * D + lane * 4) : 0u;
 }
 
-// fp16 fragments of one query vector part (k-step kk holds dims 16kk + 8hh .. +8),
-// multiplied by `mul` in fp32 before rounding.
-template <int D, int P2>
-struct TQ3Query {
-  f16x8_t hi[D / 16];
-  f16x8_t lo[P2 == 2 ? D / 16 : 1];
-  __device__ __forceinline__ void load(const float* q, float mul, bool ok, int hh) {
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      f16x8_t h{}, l{};
-      if (ok) {
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (e < 4 ? x0[e] : x1[e - 4]) * mul;
-          const _Float16 hx = (_Float16)x;
-          h[e] = hx;
-          l[e] = (_Float16)(x - (float)hx);
-        }
-      }
-      hi[kk] = h;
-      if constexpr (P2 == 2) lo[kk] = l;
-    }
-  }
+// Shared memory of the partial kernel (NW = 8 waves, two per SIMD).
+//  * key table, indexed by (byte of two key nibbles, lane slot): every lane of
+//    a 32-lane group reads its own 8-byte column, so table reads never
+//    conflict on LDS banks whatever the codes are;
+//  * query fragments: per column group, the fp16 parts of q' and q'' in the
+//    matrix-core operand order, [part][k-step][lane] x 16 bytes, shared by
+//    the column group's waves;
+//  * value table (6 bits of codes -> 2 levels), per-wave scale slices.
+// The combine buffer reuses the key table and fragments after the loop.
+template <int D, int NCT, int P2>
+struct TQ3Smem {
+  static constexpr int NW = 8;
+  static constexpr int TL = NW / NCT;
+  static constexpr int NPART = 2 * P2;  // q' hi, q'' hi (, q' lo, q'' lo)
+  static constexpr int KLUT_BYTES = 256 * 32 * 8;
+  static constexpr int QF_OFF = KLUT_BYTES;
+  static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
+  static constexpr int VLUT_OFF = QF_OFF + NCT * QF_CT_BYTES;
+  static constexpr int SCL_OFF = VLUT_OFF + 64 * 4;
+  static constexpr int BYTES = SCL_OFF + NW * 48 * 4;
+  static_assert(CombineBuf<D, NCT, NW>::FLOATS * 4 <= VLUT_OFF, "the combine buffer overlays table and fragments");
 };
 
-// Shared memory of the partial kernel.  The key table is indexed by (byte
-// of two key nibbles, lane slot): every lane of a 32-lane group reads its own
-// 8-byte column, so table reads never conflict on LDS banks whatever the
-// codes are.  The combine buffer reuses the table's space after the loop.
-template <int D, int NCT>
-struct TQ3Smem {
-  static constexpr int KLUT_BYTES = 256 * 32 * 8;
-  static constexpr int CBUF_BYTES = CombineBuf<D, NCT>::FLOATS * 4;
-  static constexpr int MAIN_BYTES = KLUT_BYTES > CBUF_BYTES ? KLUT_BYTES : CBUF_BYTES;
-  static constexpr int VLUT_OFF = MAIN_BYTES;
-  static constexpr int SCL_OFF = VLUT_OFF + 64 * 4;
-  static constexpr int BYTES = SCL_OFF + 4 * 48 * 4;
-};
+template <int D>
+__device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, int lane) {
+  return *reinterpret_cast<const f16x8_t*>(qf + (part * (D / 16) + kk) * 1024 + lane * 16);
+}
 
 template <int D, int P2, bool CAP>
-__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const TQ3Query<D, P2>& q1,
-                                            const TQ3Query<D, P2>& q2, const uint8_t* __restrict__ klut,
-                                            const uint32_t* __restrict__ vlut, uint32_t* scl, const AttnArgs& a,
-                                            int key0, int L, int n, int ppos, int lane, uint32_t slot8) {
+__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const uint8_t* __restrict__ qf,
+                                            const uint8_t* __restrict__ klut, const uint32_t* __restrict__ vlut,
+                                            uint32_t* scl, const AttnArgs& a, int key0, int L, int n, int ppos,
+                                            int lane, uint32_t slot8) {
   const int hh = lane >> 5;
   // scales of this half (K norm, K residual norm, V norm of the keys of the
   // lane's score registers) through the wave's LDS slice; a wave's LDS
   // accesses execute in order, so the write is visible to the reads after it
   if (lane < 48) scl[lane] = t.sc;
   __builtin_amdgcn_wave_barrier();
-  uint32_t shw[3][8];
-#pragma unroll
-  for (int f = 0; f < 3; ++f) {
+  auto scale_words = [&](int f, uint32_t(&wd)[8]) {
     const u32x4_t x0 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2];
     const u32x4_t x1 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2 + 1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      shw[f][j] = x0[j];
-      shw[f][4 + j] = x1[j];
+      wd[j] = x0[j];
+      wd[4 + j] = x1[j];
     }
-  }
-  __builtin_amdgcn_wave_barrier();
-  auto half_of = [&](int f, int r) -> float {
-    const uint32_t w = shw[f][r >> 1];
+  };
+  auto half_at = [](const uint32_t(&wd)[8], int r) -> float {
+    const uint32_t w = wd[r >> 1];
     return (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xFFFF)));
   };
 
@@ -201,29 +185,34 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     u32x4_t mse, qjl;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      // byte b of the nibble word selects the table row; the lane's slot
-      // selects the column: address = byte * 256 + slot * 8
+      // byte b of the nibble word selects the table row, the lane's slot the
+      // column: address = byte * 256 + slot * 8
       const uint32_t addr = __builtin_amdgcn_perm(w, slot8, 0x0C0C0000u | ((4u + b) << 8));
       const u32x2_t e = *reinterpret_cast<const u32x2_t*>(klut + addr);
       mse[b] = e[0];
       qjl[b] = e[1];
     }
     const f16x8_t km = __builtin_bit_cast(f16x8_t, mse), kq = __builtin_bit_cast(f16x8_t, qjl);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, q1.hi[kk], s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, q2.hi[kk], s2, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qfrag<D>(qf, 0, kk, lane), s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qfrag<D>(qf, 1, kk, lane), s2, 0, 0, 0);
     if constexpr (P2 == 2) {
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, q1.lo[kk], s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, q2.lo[kk], s2, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qfrag<D>(qf, 2, kk, lane), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qfrag<D>(qf, 3, kk, lane), s2, 0, 0, 0);
     }
   }
   // scores in log2 units (q'' already carries the QJL coefficient relative
   // to the first term)
   float p[1][16];
+  {
+    uint32_t nw[8], gw[8];
+    scale_words(0, nw);
+    scale_words(1, gw);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float x = fmaf(s2[r], half_of(1, r), s1[r] * half_of(0, r)) * a.q1_mul;
-    if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
-    p[0][r] = x;
+    for (int r = 0; r < 16; ++r) {
+      float x = fmaf(s2[r], half_at(gw, r), s1[r] * half_at(nw, r)) * a.q1_mul;
+      if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
+      p[0][r] = x;
+    }
   }
   const bool full = key0 + 32 <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
   uint32_t vmask = 0xFFFFu;  // score registers whose key lies inside the sequence
@@ -237,6 +226,9 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     }
   }
   softmax_update<D, 1>(cs, p);
+  uint32_t vw[8];
+  scale_words(2, vw);
+  __builtin_amdgcn_wave_barrier();
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -244,7 +236,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 8 * v + e;
-      const float nvr = (vmask >> r) & 1 ? half_of(2, r) : 0.0f;
+      const float nvr = (vmask >> r) & 1 ? half_at(vw, r) : 0.0f;
       const float x = p[0][r] * nvr;
       const _Float16 hx = (_Float16)x;
       phi[e] = hx;
@@ -253,13 +245,15 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const uint32_t* w3 = t.vc[dt >> 1];
-      // the 48-bit field of this d-tile; codes 8v .. 8v+7 start at bit 24v
-      const uint64_t field = (dt & 1) ? ((uint64_t)(w3[1] >> 16) | ((uint64_t)w3[2] << 16))
-                                      : ((uint64_t)w3[0] | ((uint64_t)(w3[1] & 0xFFFF) << 32));
-      const uint32_t bits = (uint32_t)(field >> (24 * v));
+      // 24 bits of codes: d-tile dt, keys of k-step v
+      uint32_t g;
+      if ((dt & 1) == 0)
+        g = v == 0 ? w3[0] : __builtin_amdgcn_alignbit(w3[1], w3[0], 24);
+      else
+        g = v == 0 ? __builtin_amdgcn_alignbit(w3[2], w3[1], 16) : (w3[2] >> 8);
       u32x4_t vv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vv[q] = vlut[(bits >> (6 * q)) & 63];
+      for (int q = 0; q < 4; ++q) vv[q] = vlut[(g >> (6 * q)) & 63];
       const f16x8_t vop = __builtin_bit_cast(f16x8_t, vv);
       cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, phi, cs.acc[dt], 0, 0, 0);
       if constexpr (P2 == 2) cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
@@ -268,12 +262,13 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 }
 
 template <int D, int NCT, int P2, bool CAP>
-__global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
-  constexpr int TL = 4 / NCT;
+__global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
+  using SM = TQ3Smem<D, NCT, P2>;
+  constexpr int NW = SM::NW;
+  constexpr int TL = SM::TL;
   constexpr int NDT = D / 32;
   constexpr int SB = tq3_sub_bytes(D);
-  constexpr int NBUF = 4;
-  using SM = TQ3Smem<D, NCT>;
+  constexpr int NBUF = 3;
   __shared__ __align__(16) uint8_t smem[SM::BYTES];
   uint8_t* klut = smem;
   float* cbuf = reinterpret_cast<float*>(smem);
@@ -285,6 +280,7 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 48;
   const int ct = wave % NCT, tl = wave / NCT;
+  uint8_t* qf = smem + SM::QF_OFF + ct * SM::QF_CT_BYTES;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
   const int w = blockIdx.x;
@@ -309,30 +305,53 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
   for (int j = 0; j < NBUF - 1; ++j)
     if (j < cnt) load_tq3<D>(buf[j], sub_of(t_first + j * TL), lane);
 
-  // decode tables: key byte (two nibbles code | sign << 3) -> (levels, signs),
-  // one copy per lane slot; 6 bits of value codes -> 2 levels.  The 8 levels
-  // pass through LDS (the wave's scale slice, unused until the loop).
+  // the 8 levels pass through LDS (wave 0's scale slice, unused until the loop)
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) scl[j] = a.lev16_bits[j];  // constant indices: scalar argument reads
   }
   __syncthreads();
   {
+    // key table: byte (two nibbles code | sign << 3) -> (levels, signs), one
+    // copy per lane slot; value table: 6 bits of codes -> 2 levels
     const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
-    const int i = threadIdx.x;
+    const int i = threadIdx.x & 255, half = threadIdx.x >> 8;
     const uint32_t lo = i & 15, hi = i >> 4;
     const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
     const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-    u32x2_t* row = reinterpret_cast<u32x2_t*>(klut + i * 256);
+    u32x2_t* row = reinterpret_cast<u32x2_t*>(klut + i * 256) + half * 16;
 #pragma unroll
-    for (int sl = 0; sl < 32; ++sl) row[sl] = u32x2_t{lev, sg};
-    if (i < 64) vlut[i] = lv[i & 7] | (lv[i >> 3] << 16);
+    for (int sl = 0; sl < 16; ++sl) row[sl] = u32x2_t{lev, sg};
+    if (threadIdx.x < 64) vlut[threadIdx.x] = lv[threadIdx.x & 7] | (lv[threadIdx.x >> 3] << 16);
+    // query fragments of this wave's column group: k-steps tl, tl + TL, ...
+    const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+    for (int kk = tl; kk < D / 16; kk += TL) {
+      f16x8_t h1{}, l1{}, h2{}, l2{};
+      if (col_ok) {
+        const float* q1p = a.q + qrow + 16 * kk + 8 * hh;
+        const float* q2p = a.q2 + qrow + 16 * kk + 8 * hh;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q1p);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
+        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
+        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? x0[e] : x1[e - 4];
+          const float y = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
+          h1[e] = (_Float16)x;
+          l1[e] = (_Float16)(x - (float)h1[e]);
+          h2[e] = (_Float16)y;
+          l2[e] = (_Float16)(y - (float)h2[e]);
+        }
+      }
+      *reinterpret_cast<f16x8_t*>(qf + (0 * (D / 16) + kk) * 1024 + lane * 16) = h1;
+      *reinterpret_cast<f16x8_t*>(qf + (1 * (D / 16) + kk) * 1024 + lane * 16) = h2;
+      if constexpr (P2 == 2) {
+        *reinterpret_cast<f16x8_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
+        *reinterpret_cast<f16x8_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
+      }
+    }
   }
-  const float* qoff = a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
-  const float* q2off = a.q2 + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
-  TQ3Query<D, P2> q1, q2;
-  q1.load(qoff, 1.0f, col_ok, hh);
-  q2.load(q2off, a.q2_mul, col_ok, hh);
   const uint32_t slot8 = (uint32_t)(lane & 31) * 8;
   __syncthreads();
 
@@ -348,19 +367,19 @@ __global__ __launch_bounds__(256) void attn_tq3_kernel(AttnArgs a) {
       const int k = i + u;
       if (k < cnt) {
         if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
-        process_tq3<D, P2, CAP>(cs, buf[u], q1, q2, klut, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos,
-                                lane, slot8);
+        process_tq3<D, P2, CAP>(cs, buf[u], qf, klut, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos, lane,
+                                slot8);
       }
     }
   }
-  __syncthreads();  // the combine buffer overlays the key table
-  combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
+  __syncthreads();  // the combine buffer overlays the tables
+  combine_and_store<D, NCT, NW>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
 
 template <int D, int NCT>
 static hipError_t launch_tq3_dn(const AttnArgs& a, bool precise, hipStream_t s) {
   const bool cap = a.softcap > 0.0f;
-  dim3 grid(a.n_wg), block(256);
+  dim3 grid(a.n_wg), block(512);
   if (precise) {
     if (cap)
       hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, true>), grid, block, 0, s, a);
