@@ -138,13 +138,25 @@ struct TQ3Smem {
   static constexpr int NW = 8;
   static constexpr int TL = NW / NCT;
   static constexpr int NPART = 2 * P2;  // q' hi, q'' hi (, q' lo, q'' lo)
-  static constexpr int KLUT_BYTES = 256 * 32 * 8;
-  static constexpr int QF_OFF = KLUT_BYTES;
+  // below 64 KiB: value table, scale slices, query fragments; the key table
+  // fills the next 64 KiB, so that a key-table address is one byte permute
+  // of (slot, code byte, 1) and every other address fits an instruction's
+  // 16-bit offset field
+  static constexpr int VLUT_OFF = 0;
+  static constexpr int SCL_OFF = 256;
+  static constexpr int QF_OFF = 2048;
   static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
-  static constexpr int VLUT_OFF = QF_OFF + NCT * QF_CT_BYTES;
-  static constexpr int SCL_OFF = VLUT_OFF + 64 * 4;
-  static constexpr int BYTES = SCL_OFF + NW * 48 * 4;
-  static_assert(CombineBuf<D, NCT, NW>::FLOATS * 4 <= VLUT_OFF, "the combine buffer overlays table and fragments");
+  static constexpr int KLUT_OFF = 65536;  // row = code byte: [levels x 32 slots][signs x 32 slots]
+  // a second column group's fragments go above the key table when both do
+  // not fit below it (two-part fragments of 64 KiB for d = 128)
+  static constexpr bool LOW2 = QF_OFF + NCT * QF_CT_BYTES <= KLUT_OFF;
+  static constexpr int qf_off(int ct) { return (LOW2 || ct == 0) ? QF_OFF + ct * QF_CT_BYTES : KLUT_OFF + 65536; }
+  static constexpr int BYTES = (LOW2 || NCT == 1) ? KLUT_OFF + 65536 : KLUT_OFF + 65536 + QF_CT_BYTES;
+  static_assert(SCL_OFF + NW * 48 * 4 <= QF_OFF, "scale slices");
+  static_assert(QF_OFF + QF_CT_BYTES <= KLUT_OFF, "query fragments");
+  static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
+  static constexpr int CBUF_OFF = QF_OFF;  // the combine buffer reuses fragments and key table
+  static_assert(CBUF_OFF + CombineBuf<D, NCT, NW>::FLOATS * 4 <= BYTES, "combine buffer");
 };
 
 template <int D>
@@ -152,11 +164,37 @@ __device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, in
   return *reinterpret_cast<const f16x8_t*>(qf + (part * (D / 16) + kk) * 1024 + lane * 16);
 }
 
+// Query fragments of one lane: held in registers when they fit (one fp16
+// part each), else read from LDS at every use.
+template <int D, int P2>
+struct QFrags {
+  static constexpr bool IN_REGS = P2 == 1;
+  f16x8_t f[IN_REGS ? 2 * P2 : 1][IN_REGS ? D / 16 : 1];
+  const uint8_t* qf;
+  int lane;
+  __device__ __forceinline__ void init(const uint8_t* q, int l) {
+    qf = q;
+    lane = l;
+    if constexpr (IN_REGS) {
+#pragma unroll
+      for (int pt = 0; pt < 2 * P2; ++pt)
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
+    }
+  }
+  __device__ __forceinline__ f16x8_t get(int pt, int kk) const {
+    if constexpr (IN_REGS)
+      return f[pt][kk];
+    else
+      return qfrag<D>(qf, pt, kk, lane);
+  }
+};
+
 template <int D, int P2, bool CAP>
-__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const uint8_t* __restrict__ qf,
-                                            const uint8_t* __restrict__ klut, const uint32_t* __restrict__ vlut,
+__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const QFrags<D, P2>& qr,
+                                            const uint8_t* __restrict__ lds, const uint32_t* __restrict__ vlut,
                                             uint32_t* scl, const AttnArgs& a, int key0, int L, int n, int ppos,
-                                            int lane, uint32_t slot8) {
+                                            int lane, uint32_t kslot) {
   const int hh = lane >> 5;
   // scales of this half (K norm, K residual norm, V norm of the keys of the
   // lane's score registers) through the wave's LDS slice; a wave's LDS
@@ -186,18 +224,18 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       // byte b of the nibble word selects the table row, the lane's slot the
-      // column: address = byte * 256 + slot * 8
-      const uint32_t addr = __builtin_amdgcn_perm(w, slot8, 0x0C0C0000u | ((4u + b) << 8));
-      const u32x2_t e = *reinterpret_cast<const u32x2_t*>(klut + addr);
-      mse[b] = e[0];
-      qjl[b] = e[1];
+      // column: address = 65536 + byte * 256 + slot * 4 (+ 128 for the signs),
+      // assembled from the bytes of (kslot, w) by one permute each
+      const uint32_t sel = 0x0C020000u | ((4u + b) << 8);
+      mse[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot, sel));
+      qjl[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot + 128, sel));
     }
     const f16x8_t km = __builtin_bit_cast(f16x8_t, mse), kq = __builtin_bit_cast(f16x8_t, qjl);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qfrag<D>(qf, 0, kk, lane), s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qfrag<D>(qf, 1, kk, lane), s2, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(0, kk), s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(1, kk), s2, 0, 0, 0);
     if constexpr (P2 == 2) {
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qfrag<D>(qf, 2, kk, lane), s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qfrag<D>(qf, 3, kk, lane), s2, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(2, kk), s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(3, kk), s2, 0, 0, 0);
     }
   }
   // scores in log2 units (q'' already carries the QJL coefficient relative
@@ -209,26 +247,26 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     scale_words(1, gw);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = fmaf(s2[r], half_at(gw, r), s1[r] * half_at(nw, r)) * a.q1_mul;
+      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f)) * a.q1_mul;
       if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
       p[0][r] = x;
     }
   }
+  uint32_t vw[8];
+  scale_words(2, vw);
+  __builtin_amdgcn_wave_barrier();
   const bool full = key0 + 32 <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
-  uint32_t vmask = 0xFFFFu;  // score registers whose key lies inside the sequence
   if (!full) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kp = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       const bool vis = kp <= ppos && (a.window == 0 || ppos - kp < a.window);
       p[0][r] = vis ? p[0][r] : NEG_INF;
-      vmask &= kp < L ? 0xFFFFu : ~(1u << r);  // slots past the end may hold any bits
+      // slots past the end of the sequence may hold any bits: zero their norm
+      if (kp >= L) vw[r >> 1] &= (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
     }
   }
   softmax_update<D, 1>(cs, p);
-  uint32_t vw[8];
-  scale_words(2, vw);
-  __builtin_amdgcn_wave_barrier();
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -236,11 +274,10 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int r = 8 * v + e;
-      const float nvr = (vmask >> r) & 1 ? half_at(vw, r) : 0.0f;
-      const float x = p[0][r] * nvr;
-      const _Float16 hx = (_Float16)x;
+      const float nvr = half_at(vw, r);
+      const _Float16 hx = (_Float16)fmaf(p[0][r], nvr, 0.0f);
       phi[e] = hx;
-      if constexpr (P2 == 2) plo[e] = (_Float16)(x - (float)hx);
+      if constexpr (P2 == 2) plo[e] = (_Float16)fmaf(p[0][r], nvr, -(float)hx);
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -268,10 +305,10 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
   constexpr int TL = SM::TL;
   constexpr int NDT = D / 32;
   constexpr int SB = tq3_sub_bytes(D);
-  constexpr int NBUF = 3;
+  constexpr int NBUF = P2 == 1 ? 2 : 3;  // register budget of two waves per SIMD
   __shared__ __align__(16) uint8_t smem[SM::BYTES];
-  uint8_t* klut = smem;
-  float* cbuf = reinterpret_cast<float*>(smem);
+  uint8_t* klut = smem + SM::KLUT_OFF;
+  float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF);
   uint32_t* vlut = reinterpret_cast<uint32_t*>(smem + SM::VLUT_OFF);
 
   const int lane = threadIdx.x & 63;
@@ -280,7 +317,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 48;
   const int ct = wave % NCT, tl = wave / NCT;
-  uint8_t* qf = smem + SM::QF_OFF + ct * SM::QF_CT_BYTES;
+  uint8_t* qf = smem + SM::qf_off(ct);
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
   const int w = blockIdx.x;
@@ -319,9 +356,9 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
     const uint32_t lo = i & 15, hi = i >> 4;
     const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
     const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-    u32x2_t* row = reinterpret_cast<u32x2_t*>(klut + i * 256) + half * 16;
+    uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half * 32;
 #pragma unroll
-    for (int sl = 0; sl < 16; ++sl) row[sl] = u32x2_t{lev, sg};
+    for (int sl = 0; sl < 32; ++sl) row[sl] = half ? sg : lev;
     if (threadIdx.x < 64) vlut[threadIdx.x] = lv[threadIdx.x & 7] | (lv[threadIdx.x >> 3] << 16);
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
@@ -352,9 +389,11 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
       }
     }
   }
-  const uint32_t slot8 = (uint32_t)(lane & 31) * 8;
+  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
   __syncthreads();
 
+  QFrags<D, P2> qr;
+  qr.init(qf, lane);
   ColState<D> cs;
   cs.m = NEG_INF;
   cs.l = 0.0f;
@@ -367,8 +406,8 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
       const int k = i + u;
       if (k < cnt) {
         if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
-        process_tq3<D, P2, CAP>(cs, buf[u], qf, klut, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos, lane,
-                                slot8);
+        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos, lane,
+                                kslot);
       }
     }
   }
