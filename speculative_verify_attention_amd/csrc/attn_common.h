@@ -48,6 +48,14 @@ __device__ __forceinline__ float tanh_nb(float x) {
   return ax < 0.55f ? small : big;
 }
 
+// Value of lane l ^ 32: one lane-swap between the wave's halves (no LDS
+// round trip).
+__device__ __forceinline__ float xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ int find_seq(const int32_t* base, int n, int f) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
@@ -80,7 +88,7 @@ __device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB]
   for (int st = 0; st < NSUB; ++st)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  mt = fmaxf(mt, xor32(mt));
   // move the reference only when the tile max exceeds it by more than 2^8,
   // so probabilities stay below 256 and rescales are rare
   const bool up = mt > cs.m + 8.0f;
@@ -150,7 +158,7 @@ __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, 
   constexpr int CSTRIDE = CombineBuf<D, NCT, NW>::CSTRIDE;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
-  cs.l += __shfl_xor(cs.l, 32);
+  cs.l += xor32(cs.l);
 #pragma unroll
   for (int half = TL / 2; half >= 1; half >>= 1) {
     if (tl >= half && tl < 2 * half) {

@@ -26,6 +26,22 @@
 #include "attn_common.h"
 #include "kernels.h"
 
+// Query-fragment parts held in registers and depth of the sub-tile ring,
+// for one-part (fast) and two-part (precise) products; the rest of the
+// fragments are read from LDS (register budget of two waves per SIMD).
+#ifndef SVATTN_TQ3_QREGS_FAST
+#define SVATTN_TQ3_QREGS_FAST 2
+#endif
+#ifndef SVATTN_TQ3_NBUF_FAST
+#define SVATTN_TQ3_NBUF_FAST 2
+#endif
+#ifndef SVATTN_TQ3_QREGS_PRECISE
+#define SVATTN_TQ3_QREGS_PRECISE 1
+#endif
+#ifndef SVATTN_TQ3_NBUF_PRECISE
+#define SVATTN_TQ3_NBUF_PRECISE 3
+#endif
+
 namespace svattn {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -121,7 +137,8 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
     t.vc[j][1] = vp[1];
     t.vc[j][2] = vp[2];
   }
-  t.sc = lane < 48 ? *reinterpret_cast<const uint32_t*>(sub + 28 * D + lane * 4) : 0u;
+  // lanes 48..63 repeat lanes 32..47 (no branch around the load)
+  t.sc = *reinterpret_cast<const uint32_t*>(sub + 28 * D + (lane < 48 ? lane : lane - 16) * 4);
 }
 
 // Shared memory of the partial kernel (NW = 8 waves, two per SIMD).
@@ -143,8 +160,8 @@ struct TQ3Smem {
   // of (slot, code byte, 1) and every other address fits an instruction's
   // 16-bit offset field
   static constexpr int VLUT_OFF = 0;
-  static constexpr int SCL_OFF = 256;
-  static constexpr int QF_OFF = 2048;
+  static constexpr int SCL_OFF = 256;  // per wave: two slots of 48 dwords, alternating between sub-tiles
+  static constexpr int QF_OFF = 4096;
   static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
   static constexpr int KLUT_OFF = 65536;  // row = code byte: [levels x 32 slots][signs x 32 slots]
   // a second column group's fragments go above the key table when both do
@@ -152,7 +169,7 @@ struct TQ3Smem {
   static constexpr bool LOW2 = QF_OFF + NCT * QF_CT_BYTES <= KLUT_OFF;
   static constexpr int qf_off(int ct) { return (LOW2 || ct == 0) ? QF_OFF + ct * QF_CT_BYTES : KLUT_OFF + 65536; }
   static constexpr int BYTES = (LOW2 || NCT == 1) ? KLUT_OFF + 65536 : KLUT_OFF + 65536 + QF_CT_BYTES;
-  static_assert(SCL_OFF + NW * 48 * 4 <= QF_OFF, "scale slices");
+  static_assert(SCL_OFF + NW * 2 * 48 * 4 <= QF_OFF, "scale slices");
   static_assert(QF_OFF + QF_CT_BYTES <= KLUT_OFF, "query fragments");
   static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
   static constexpr int CBUF_OFF = QF_OFF;  // the combine buffer reuses fragments and key table
@@ -164,27 +181,26 @@ __device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, in
   return *reinterpret_cast<const f16x8_t*>(qf + (part * (D / 16) + kk) * 1024 + lane * 16);
 }
 
-// Query fragments of one lane: held in registers when they fit (one fp16
-// part each), else read from LDS at every use.
+// Query fragments of one lane: the leading NREG parts in registers, the
+// others read from LDS at every use.
 template <int D, int P2>
 struct QFrags {
-  static constexpr bool IN_REGS = P2 == 1;
-  f16x8_t f[IN_REGS ? 2 * P2 : 1][IN_REGS ? D / 16 : 1];
+  static constexpr int NREG = P2 == 1 ? SVATTN_TQ3_QREGS_FAST : SVATTN_TQ3_QREGS_PRECISE;
+  static constexpr int NR = NREG > 0 ? NREG : 1;
+  f16x8_t f[NR][D / 16];
   const uint8_t* qf;
   int lane;
   __device__ __forceinline__ void init(const uint8_t* q, int l) {
     qf = q;
     lane = l;
-    if constexpr (IN_REGS) {
 #pragma unroll
-      for (int pt = 0; pt < 2 * P2; ++pt)
+    for (int pt = 0; pt < NREG; ++pt)
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
-    }
+      for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
   }
   __device__ __forceinline__ f16x8_t get(int pt, int kk) const {
-    if constexpr (IN_REGS)
-      return f[pt][kk];
+    if (pt < NREG)
+      return f[pt < NR ? pt : 0][kk];
     else
       return qfrag<D>(qf, pt, kk, lane);
   }
@@ -196,11 +212,8 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
                                             uint32_t* scl, const AttnArgs& a, int key0, int L, int n, int ppos,
                                             int lane, uint32_t kslot) {
   const int hh = lane >> 5;
-  // scales of this half (K norm, K residual norm, V norm of the keys of the
-  // lane's score registers) through the wave's LDS slice; a wave's LDS
-  // accesses execute in order, so the write is visible to the reads after it
-  if (lane < 48) scl[lane] = t.sc;
-  __builtin_amdgcn_wave_barrier();
+  // scl: this sub-tile's scales (K norm, K residual norm, V norm), written
+  // to the wave's LDS slot during the previous sub-tile
   auto scale_words = [&](int f, uint32_t(&wd)[8]) {
     const u32x4_t x0 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2];
     const u32x4_t x1 = reinterpret_cast<const u32x4_t*>(scl)[(hh * 3 + f) * 2 + 1];
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
   constexpr int TL = SM::TL;
   constexpr int NDT = D / 32;
   constexpr int SB = tq3_sub_bytes(D);
-  constexpr int NBUF = P2 == 1 ? 2 : 3;  // register budget of two waves per SIMD
+  constexpr int NBUF = P2 == 1 ? SVATTN_TQ3_NBUF_FAST : SVATTN_TQ3_NBUF_PRECISE;
   __shared__ __align__(16) uint8_t smem[SM::BYTES];
   uint8_t* klut = smem + SM::KLUT_OFF;
   float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF);
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
   // wave-uniform by construction; readfirstlane makes the compiler see it, so
   // tile indices and block-table reads stay scalar (no wait on vector loads)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 48;
+  uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 96;
   const int ct = wave % NCT, tl = wave / NCT;
   uint8_t* qf = smem + SM::qf_off(ct);
   const int col = lane & 31, hh = lane >> 5;
@@ -400,14 +413,20 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
 
+  // a wave's LDS accesses execute in order: the scales of sub-tile k+1 go to
+  // the other slot while sub-tile k's are read from this one
+  if (cnt > 0 && lane < 48) scl[lane] = buf[0].sc;
   for (int i = 0; i < cnt; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int k = i + u;
       if (k < cnt) {
         if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
-        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut, scl, a, (tlo + t_first + k * TL) * 32, L, n, ppos, lane,
-                                kslot);
+        if (k + 1 < cnt && lane < 48) scl[((k + 1) & 1) * 48 + lane] = buf[(u + 1) % NBUF].sc;
+        __builtin_amdgcn_wave_barrier();
+        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut, scl + (k & 1) * 48, a, (tlo + t_first + k * TL) * 32, L,
+                                n, ppos, lane, kslot);
+        __builtin_amdgcn_wave_barrier();
       }
     }
   }
