@@ -19,6 +19,9 @@ Modules
                  1+k verify rows of one sequence, written as its definition.
 ``tq3``          the compressed-cache codec: Lloyd-Max codebook solver,
                  Sylvester-Hadamard rotation, encode and decode.
+``accept``       acceptance of the drafts after the verify forward: greedy
+                 argmax and rejection sampling against the draft
+                 distribution, with the caller's uniforms.
 
 Every function cites the passage of the pages it follows; where the pages are
 silent the plainest reading is taken and named in the docstring.
@@ -27,4 +30,4 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, library routines or published tables.
 """
 
-from . import splitmix, bookkeeping, attention, tq3  # noqa: F401
+from . import splitmix, bookkeeping, attention, tq3, accept  # noqa: F401
