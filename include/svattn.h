@@ -219,6 +219,53 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
                      int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Acceptance of the drafts after the verify forward (SwiftLM page,
+ * speculative-decoding passage: rejection sampling per Leviathan et al., the
+ * ratio P_target / P_draft deciding each draft and a rejected position
+ * re-sampled from the corrected distribution; greedy argmax when the
+ * temperature is 0).  Stateless: no handle.
+ *  n_seqs, n_draft: host; n_draft[i] in [0, KV_MAX_ROWS - 1].
+ *  vocab: logits per row, >= 1.
+ *  target_logits: device float32 [sum(n_draft + 1)][vocab], sequences in
+ *    order; row j of sequence i is the target's distribution of the j-th
+ *    token after the sequence's last accepted token: rows j < n_draft[i]
+ *    check draft j, row n_draft[i] gives the bonus token.
+ *  draft_logits: device float32 [sum(n_draft)][vocab], or NULL when the
+ *    drafts are point masses (n-gram drafts, AX Engine page, "Core Technical
+ *    Architecture & Methods").  Unused when temperature is 0.
+ *  draft_tokens: device int32 [sum(n_draft)]; a token outside [0, vocab) is
+ *    never accepted.
+ *  uniforms: device float32 [sum(n_draft + 1)] in [0, 1): entry j < n decides
+ *    draft j, entry n draws the final token.  Unused when temperature is 0.
+ *  temperature: 0 = greedy (accept while a draft equals the first argmax of
+ *    its row); > 0: p = softmax(target / T), q = softmax(draft / T), draft j
+ *    accepted iff u_j * q_j(d_j) < p_j(d_j); the first rejection draws from
+ *    max(0, p_j - q_j) (a point-mass draft: p_j without its token), else the
+ *    bonus is drawn from p_n; a draw returns the smallest token whose
+ *    cumulative weight (tokens in index order) exceeds u_n times the total.
+ *  out_accepted: device int32 [n_seqs]: accepted drafts (0 .. n_draft[i]).
+ *  out_token: device int32 [n_seqs]: the token that follows them.
+ *  workspace: device, >= spec_accept_workspace_bytes(...), 256-byte aligned.
+ * Arithmetic is fp32; decisions within about 1e-6 relative of a threshold may
+ * differ from an exact evaluation.  The caller rolls the cache back by
+ * n_draft[i] - out_accepted[i] (kv_rollback_batch, after copying the counts
+ * to the host).  Errors: KV_EINVAL, KV_ENOMEM (workspace), KV_EDEVICE;
+ * spec_accept_last_error() gives the message of the calling thread's last
+ * failure.
+ */
+int spec_accept(int32_t n_seqs, const int32_t* n_draft, int32_t vocab, const float* target_logits,
+                const float* draft_logits, const int32_t* draft_tokens, const float* uniforms,
+                float temperature, int32_t* out_accepted, int32_t* out_token, void* workspace,
+                size_t ws_bytes, void* stream);
+
+/* Workspace bytes of spec_accept for this shape (with_draft: draft_logits
+ * will be non-NULL).  Errors as spec_accept's validation. */
+int spec_accept_workspace_bytes(int32_t n_seqs, const int32_t* n_draft, int32_t vocab, int32_t with_draft,
+                                float temperature, size_t* out);
+
+const char* spec_accept_last_error(void);
+
+/*
  * Tracing: while set, every spec_verify_attn call records event `before` on
  * its stream just before its first attention-partial kernel and `after` just
  * after its last one (hipEvent_t handles passed as void*, owned by the

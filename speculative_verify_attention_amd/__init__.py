@@ -4,7 +4,8 @@ MI355X (gfx950).
 The work runs in ``libsvattn.so`` (C ABI in ``include/svattn.h``): a
 deterministic host block manager with 256-token blocks and O(1) rollback,
 slice-update and quantize-on-append kernels, and a split-context MFMA
-attention kernel with its log-sum-exp merge.  This package is the Python
+attention kernel with its log-sum-exp merge, and the acceptance step that
+follows it (greedy or rejection sampling).  This package is the Python
 binding (argument marshalling only) plus the seeded synthetic-input
 generators in ``synth``.
 """
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     KV_TQ3,
     KVCache,
     SvattnError,
+    accept,
     core_lib,
     kv_append,
     kv_block_table,
@@ -42,6 +44,8 @@ from ._binding import (  # noqa: F401
     kv_seq_len,
     kv_workspace_bytes,
     lib,
+    spec_accept,
+    spec_accept_workspace_bytes,
     spec_verify_attn,
     svcore_params,
 )

@@ -88,6 +88,9 @@ _SIGS = {
     "kv_free_blocks": [_p, _i32p],
     "kv_codec": [_p, _p, _p, _p, _p, _p],
     "kv_last_error": [_p],
+    "spec_accept": [_i32, _i32p, _i32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_size_t, _p],
+    "spec_accept_workspace_bytes": [_i32, _i32p, _i32, _i32, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)],
+    "spec_accept_last_error": [],
 }
 
 _CORE_SIGS = {
@@ -256,6 +259,61 @@ def kv_codec(h, head_dim):
 
 def kv_last_error(h):
     return lib().kv_last_error(h).decode()
+
+
+def _check_accept(rc):
+    if rc != KV_OK:
+        raise SvattnError(rc, lib().spec_accept_last_error().decode())
+    return rc
+
+
+def spec_accept_workspace_bytes(n_draft, vocab, with_draft, temperature):
+    out = ctypes.c_size_t()
+    _check_accept(lib().spec_accept_workspace_bytes(len(n_draft), _arr(n_draft), vocab, int(bool(with_draft)),
+                                                    float(temperature), ctypes.byref(out)))
+    return out.value
+
+
+def spec_accept(n_draft, target_logits, draft_logits, draft_tokens, uniforms, temperature, out_accepted,
+                out_token, workspace, stream=None):
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return lib().spec_accept(len(n_draft), _arr(n_draft), target_logits.shape[-1], ptr(target_logits),
+                             ptr(draft_logits), ptr(draft_tokens), ptr(uniforms), float(temperature),
+                             ptr(out_accepted), ptr(out_token), ptr(workspace), ws_bytes, _stream_ptr(stream))
+
+
+def accept(n_draft, target_logits, draft_tokens, uniforms, temperature, draft_logits=None, workspace=None,
+           stream=None):
+    """Acceptance of drafts (argument marshalling for spec_accept).  Returns
+    (accepted, token) as device int32 tensors of len(n_draft)."""
+    import torch
+
+    n_draft = [int(x) for x in n_draft]
+    rows_t, rows_d = sum(n_draft) + len(n_draft), sum(n_draft)
+    dev = target_logits.device
+    if target_logits.dtype != torch.float32 or target_logits.dim() != 2 or target_logits.shape[0] != rows_t:
+        raise ValueError(f"target_logits must be float32 [{rows_t}, vocab]")
+    if not target_logits.is_contiguous():
+        raise ValueError("target_logits must be contiguous")
+    vocab = target_logits.shape[1]
+    if draft_logits is not None and (draft_logits.dtype != torch.float32 or tuple(draft_logits.shape) != (rows_d, vocab)
+                                     or not draft_logits.is_contiguous()):
+        raise ValueError(f"draft_logits must be contiguous float32 [{rows_d}, {vocab}]")
+    if draft_tokens.dtype != torch.int32 or draft_tokens.numel() != rows_d:
+        raise ValueError(f"draft_tokens must be int32 [{rows_d}]")
+    if uniforms.dtype != torch.float32 or uniforms.numel() != rows_t:
+        raise ValueError(f"uniforms must be float32 [{rows_t}]")
+    need = spec_accept_workspace_bytes(n_draft, vocab, draft_logits is not None, temperature)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    acc = torch.empty(len(n_draft), dtype=torch.int32, device=dev)
+    tok = torch.empty(len(n_draft), dtype=torch.int32, device=dev)
+    _check_accept(spec_accept(n_draft, target_logits, draft_logits, draft_tokens.contiguous(), uniforms.contiguous(),
+                              temperature, acc, tok, workspace, stream))
+    return acc, tok
 
 
 # ---- convenience wrapper ---------------------------------------------------------------

@@ -39,7 +39,7 @@ HIP_FLAGS = [
     "-I", CSRC,
 ]
 
-HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "svattn.cpp", "kvcore.cpp"]
+HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "accept.hip", "svattn.cpp", "kvcore.cpp"]
 CORE_SOURCES = ["kvcore.cpp", "svcore_capi.cpp"]
 
 

@@ -187,7 +187,47 @@ struct QPrepArgs {
   int32_t n_vec, d;
 };
 
+// ---- acceptance of drafts ------------------------------------------------------
+//
+// Rows: the target rows of all sequences (sum of n+1), then the draft rows
+// (sum of n).  A row is cut into chunks of kAcceptChunk logits; the first
+// kernel reduces every (row, chunk), the second decides each sequence, the
+// last two draw the final token of sampled sequences from their weights.
+constexpr int kMaxAcceptSeqs = 128;
+constexpr int kAcceptChunk = 4096;
+
+// Per-sequence decision handed from the decide kernel to the draw kernels.
+struct AcceptPlan {
+  int32_t mode;   // 0 token already written (greedy), 1 draw from the weights
+  int32_t row_t;  // target row of the weights
+  int32_t row_q;  // draft row (-1: none)
+  int32_t tok_q;  // point-mass draft token whose mass is removed (-1: none)
+  float m_t, s_t; // target row max and sum of exp((l - max) / T)
+  float m_q, s_q; // draft row, likewise
+  float u;        // uniform of the draw
+  int32_t pad[3];
+};
+
+struct AcceptArgs {
+  const float* target;      // [rows_t][vocab]
+  const float* draft;       // [rows_d][vocab] or null (point-mass drafts)
+  const int32_t* drafts;    // [rows_d]
+  const float* u;           // [rows_t]
+  int32_t* out_acc;         // [n_seqs] (this group's first sequence at index seq0)
+  int32_t* out_tok;
+  float4* stats;            // [rows_t + rows_d][nch]: max, sum, argmax bits, -
+  AcceptPlan* plan;         // [n_seqs]
+  float* fsum;              // [n_seqs][nch]
+  float inv_t;              // 1 / temperature, 0 = greedy
+  int32_t vocab, nch, rows_t, rows_d;
+  int32_t seq0, count;      // this launch group's sequences
+  int32_t n[kMaxAcceptSeqs];   // drafts of each sequence
+  int32_t t0[kMaxAcceptSeqs];  // first target row
+  int32_t d0[kMaxAcceptSeqs];  // first draft row (relative to rows_t)
+};
+
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
+static_assert(sizeof(AcceptArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
 static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
 static_assert(sizeof(TableUpdateArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
 
@@ -197,5 +237,9 @@ hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s);
 // fp16 operands when precise, one fp16 part otherwise.
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
 hipError_t launch_attn_tq3(const AttnArgs& a, int nct, bool precise, hipStream_t s);
+// Acceptance: row statistics over every row (once per call), then decide and
+// draw for one group of up to kMaxAcceptSeqs sequences.
+hipError_t launch_accept_stats(const AcceptArgs& a, hipStream_t s);
+hipError_t launch_accept_group(const AcceptArgs& a, hipStream_t s);
 
 }  // namespace svattn

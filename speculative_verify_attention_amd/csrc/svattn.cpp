@@ -575,3 +575,111 @@ int kv_codec(const kv_cache* c, int8_t* signs, float* s_matrix, double* levels, 
 const char* kv_last_error(const kv_cache* c) { return c ? c->err.c_str() : "null handle"; }
 
 }  // extern "C"
+
+// ---- acceptance of drafts ---------------------------------------------------------
+
+namespace {
+
+thread_local std::string g_accept_err;
+
+int accept_fail(int code, const char* msg) {
+  g_accept_err = msg;
+  return code;
+}
+
+struct AcceptLayout {
+  int64_t rows_t = 0, rows_d = 0, nch = 0;
+  size_t stats_off = 0, plan_off = 0, fsum_off = 0, total = 0;
+};
+
+int accept_layout(int32_t n_seqs, const int32_t* n_draft, int32_t vocab, bool with_draft, float temperature,
+                  AcceptLayout* L) {
+  if (n_seqs < 0) return accept_fail(KV_EINVAL, "n_seqs must be >= 0");
+  if (n_seqs > 0 && !n_draft) return accept_fail(KV_EINVAL, "null n_draft");
+  if (vocab < 1) return accept_fail(KV_EINVAL, "vocab must be >= 1");
+  if (!std::isfinite(temperature) || temperature < 0.0f)
+    return accept_fail(KV_EINVAL, "temperature must be finite and >= 0");
+  int64_t nd = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_draft[i] < 0 || n_draft[i] > KV_MAX_ROWS - 1) return accept_fail(KV_EINVAL, "n_draft must be in [0, 7]");
+    nd += n_draft[i];
+  }
+  L->rows_t = nd + n_seqs;
+  L->rows_d = (with_draft && temperature > 0.0f) ? nd : 0;
+  L->nch = (vocab + kAcceptChunk - 1) / kAcceptChunk;
+  L->stats_off = 0;
+  L->plan_off = align_up((size_t)(L->rows_t + L->rows_d) * L->nch * 16);
+  L->fsum_off = L->plan_off + align_up((size_t)n_seqs * sizeof(AcceptPlan));
+  L->total = L->fsum_off + align_up((size_t)n_seqs * L->nch * 4);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_accept_workspace_bytes(int32_t n_seqs, const int32_t* n_draft, int32_t vocab, int32_t with_draft,
+                                float temperature, size_t* out) {
+  if (!out) return accept_fail(KV_EINVAL, "null out");
+  AcceptLayout L;
+  const int rc = accept_layout(n_seqs, n_draft, vocab, with_draft != 0, temperature, &L);
+  if (rc != KV_OK) return rc;
+  *out = L.total;
+  return KV_OK;
+}
+
+int spec_accept(int32_t n_seqs, const int32_t* n_draft, int32_t vocab, const float* target_logits,
+                const float* draft_logits, const int32_t* draft_tokens, const float* uniforms, float temperature,
+                int32_t* out_accepted, int32_t* out_token, void* workspace, size_t ws_bytes, void* stream) {
+  AcceptLayout L;
+  int rc = accept_layout(n_seqs, n_draft, vocab, draft_logits != nullptr, temperature, &L);
+  if (rc != KV_OK) return rc;
+  if (n_seqs == 0) return KV_OK;
+  if (!target_logits || !uniforms || !out_accepted || !out_token)
+    return accept_fail(KV_EINVAL, "null target_logits / uniforms / outputs");
+  if (L.rows_t > n_seqs && !draft_tokens) return accept_fail(KV_EINVAL, "null draft_tokens");
+  if (ws_bytes < L.total) return accept_fail(KV_ENOMEM, "workspace too small");
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return accept_fail(KV_EINVAL, "workspace must be non-null and 256-byte aligned");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return accept_fail(KV_EDEVICE, hipGetErrorString(e));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  AcceptArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.target = target_logits;
+  a.draft = L.rows_d > 0 ? draft_logits : nullptr;
+  a.drafts = draft_tokens;
+  a.u = uniforms;
+  a.out_acc = out_accepted;
+  a.out_tok = out_token;
+  a.stats = reinterpret_cast<float4*>(ws + L.stats_off);
+  a.plan = reinterpret_cast<AcceptPlan*>(ws + L.plan_off);
+  a.fsum = reinterpret_cast<float*>(ws + L.fsum_off);
+  a.inv_t = temperature > 0.0f ? 1.0f / temperature : 0.0f;
+  a.vocab = vocab;
+  a.nch = (int32_t)L.nch;
+  a.rows_t = (int32_t)L.rows_t;
+  a.rows_d = (int32_t)L.rows_d;
+  e = launch_accept_stats(a, s);
+  if (e != hipSuccess) return accept_fail(KV_EDEVICE, hipGetErrorString(e));
+  int32_t t0 = 0, d0 = 0;
+  for (int first = 0; first < n_seqs; first += kMaxAcceptSeqs) {
+    a.seq0 = first;
+    a.count = std::min(kMaxAcceptSeqs, n_seqs - first);
+    for (int i = 0; i < a.count; ++i) {
+      a.n[i] = n_draft[first + i];
+      a.t0[i] = t0;
+      a.d0[i] = d0;
+      t0 += n_draft[first + i] + 1;
+      d0 += n_draft[first + i];
+    }
+    e = launch_accept_group(a, s);
+    if (e != hipSuccess) return accept_fail(KV_EDEVICE, hipGetErrorString(e));
+  }
+  return KV_OK;
+}
+
+const char* spec_accept_last_error(void) { return g_accept_err.c_str(); }
+
+}  // extern "C"

@@ -29,7 +29,7 @@ import numpy as np
 KV_FP32, KV_BF16, KV_TQ3 = 0, 1, 2
 BLOCK = 256
 
-_TAG = {"prefill": 1, "step": 2, "query": 3, "scale": 4, "plan": 5}
+_TAG = {"prefill": 1, "step": 2, "query": 3, "scale": 4, "plan": 5, "accept": 6}
 
 
 def _mix(*parts):
@@ -211,3 +211,40 @@ def queries(wl, step, n_total, device, scale=1.0):
     if wl.fmt == KV_BF16:
         q = q.to(torch.bfloat16).to(torch.float32)
     return q
+
+
+# ---- inputs of the acceptance step -------------------------------------------------------
+
+
+def accept_inputs(n_draft, vocab, seed, device, with_draft=True, spread=3.0, noise=0.5, hit=0.7, boost=0.0):
+    """Seeded inputs of spec_accept: target logits N(0, spread^2) per row,
+    draft logits = the matching target row + N(0, noise^2) (a draft model
+    close to the target) with `boost` added at the drafted token (a draft
+    model surer of its token than the target), draft tokens = the target
+    row's largest logit with probability `hit`, else a uniform token, and
+    uniforms in [0, 1).
+    Returns (target [sum(n+1), vocab], draft [sum(n), vocab] or None,
+    tokens int32 [sum(n)], uniforms [sum(n+1)])."""
+    import torch
+
+    rows_t, rows_d = sum(n_draft) + len(n_draft), sum(n_draft)
+    g = _gen(device, seed, _TAG["accept"])
+    target = torch.randn((rows_t, vocab), generator=g, device=device, dtype=torch.float32) * spread
+    # the target row that checks each draft
+    check = []
+    t0 = 0
+    for n in n_draft:
+        check.extend(range(t0, t0 + n))
+        t0 += n + 1
+    check = torch.tensor(check, dtype=torch.int64, device=device)
+    draft = None
+    if with_draft:
+        draft = target[check] + torch.randn((rows_d, vocab), generator=g, device=device, dtype=torch.float32) * noise
+    top = target[check].argmax(dim=1).to(torch.int32) if rows_d else torch.zeros(0, dtype=torch.int32, device=device)
+    rnd = torch.randint(0, vocab, (rows_d,), generator=g, device=device, dtype=torch.int32)
+    keep = torch.rand((rows_d,), generator=g, device=device) < hit
+    tokens = torch.where(keep, top, rnd).contiguous()
+    if draft is not None and boost and rows_d:
+        draft[torch.arange(rows_d, device=device), tokens.long()] += boost
+    uniforms = torch.rand((rows_t,), generator=g, device=device, dtype=torch.float32)
+    return target.contiguous(), draft, tokens, uniforms

@@ -1,0 +1,132 @@
+"""GPU parity of the acceptance step (spec_accept) against the fp64 oracle.
+
+* greedy (temperature 0): accepted counts and tokens bit-exact (argmax of the
+  same fp32 logits, ties to the lowest index);
+* sampling: the kernel works in fp32, the oracle in fp64, so a decision may
+  differ only where the oracle's margin is inside a narrow band: an accept /
+  reject decision within 1e-5 relative of u * q(d) = p(d), a drawn token
+  whose cumulative-weight boundary is within 1e-5 of u * total.  Such cases
+  are counted and must stay rare; every other result is exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import accept as A
+from parity import require_gpu
+from speculative_verify_attention_amd import accept, synth
+
+pytestmark = pytest.mark.gpu
+
+BAND = 1e-5
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(n_draft, vocab, temperature, with_draft, seed, boost=4.0):
+    target, draft, tokens, u = synth.accept_inputs(n_draft, vocab, seed, "cuda", with_draft=with_draft, boost=boost)
+    acc, tok = accept(n_draft, target, tokens, u, temperature, draft_logits=draft)
+    torch.cuda.synchronize()
+    ora = A.accept_batch(target.double().cpu().numpy(), None if draft is None else draft.double().cpu().numpy(),
+                         tokens.cpu().numpy(), u.double().cpu().numpy(), n_draft, temperature)
+    return acc.cpu().numpy(), tok.cpu().numpy(), ora
+
+
+def in_band_draw(info, token):
+    """The GPU's token is a valid draw of the oracle's weights up to BAND."""
+    w, u = info["draw"]
+    c = np.cumsum(w)
+    target = u * c[-1]
+    lo = c[token - 1] if token > 0 else 0.0
+    return w[token] > 0 and lo <= target + BAND * c[-1] and c[token] > target - BAND * c[-1]
+
+
+def compare(acc, tok, ora, sampled):
+    oa, ot, infos = ora
+    excluded = 0
+    for s in range(len(acc)):
+        if acc[s] == oa[s] and tok[s] == ot[s]:
+            continue
+        assert sampled, (s, acc[s], oa[s], tok[s], ot[s])
+        if acc[s] != oa[s]:
+            j = min(acc[s], oa[s])
+            assert abs(infos[s]["ratio_margin"][j]) < BAND, (s, infos[s]["ratio_margin"][j])
+        else:
+            assert in_band_draw(infos[s], tok[s]), (s, tok[s], ot[s])
+        excluded += 1
+    return excluded
+
+
+@pytest.mark.parametrize("vocab", [1000, 5003, 151936])
+def test_greedy_exact(vocab):
+    banner(f"accept greedy vocab={vocab}")
+    n_draft = [4, 0, 3, 4, 1, 2, 4, 4]
+    acc, tok, ora = run(n_draft, vocab, 0.0, True, 100 + vocab)
+    compare(acc, tok, ora, sampled=False)
+    assert acc.max() > 0  # some drafts (the planted argmax hits) are accepted
+
+
+@pytest.mark.parametrize("vocab,temperature,with_draft", [(1000, 1.0, True), (5003, 0.7, True), (151936, 0.8, True),
+                                                          (151936, 1.0, False), (4097, 2.0, False)])
+def test_sampling_parity(vocab, temperature, with_draft):
+    banner(f"accept sampling vocab={vocab} T={temperature} draft={with_draft}")
+    rng = np.random.default_rng(vocab)
+    n_draft = rng.integers(0, 5, size=24).tolist()
+    acc, tok, ora = run(n_draft, vocab, temperature, with_draft, 7 + vocab)
+    excluded = compare(acc, tok, ora, sampled=True)
+    print(f"boundary-band cases: {excluded} of {len(n_draft)}", flush=True)
+    assert excluded <= 1
+    assert sum(acc) < sum(n_draft)  # rejections (and their corrected draws) occur
+    if with_draft:
+        assert sum(acc) > 0  # and acceptances
+
+
+def test_many_sequences_two_groups():
+    banner("accept 200 sequences (two launch groups)")
+    rng = np.random.default_rng(200)
+    n_draft = rng.integers(0, 5, size=200).tolist()
+    acc, tok, ora = run(n_draft, 3000, 0.9, True, 200)
+    assert compare(acc, tok, ora, sampled=True) <= 2
+    acc0, tok0, ora0 = run(n_draft, 3000, 0.0, True, 201)
+    compare(acc0, tok0, ora0, sampled=False)
+
+
+def test_repeatable():
+    banner("accept repeatable")
+    n_draft = [4, 4, 2]
+    target, draft, tokens, u = synth.accept_inputs(n_draft, 151936, 3, "cuda")
+    a1, t1 = accept(n_draft, target, tokens, u, 0.8, draft_logits=draft)
+    a2, t2 = accept(n_draft, target, tokens, u, 0.8, draft_logits=draft)
+    assert torch.equal(a1, a2) and torch.equal(t1, t2)
+
+
+def test_draft_equal_to_target_accepts_everything():
+    banner("accept q == p")
+    n_draft = [4, 3, 4, 1]
+    target, _, tokens, u = synth.accept_inputs(n_draft, 2048, 9, "cuda", with_draft=False)
+    check = torch.tensor([0, 1, 2, 3, 5, 6, 7, 9, 10, 11, 12, 14], device="cuda")
+    draft = target[check].contiguous()
+    acc, _ = accept(n_draft, target, tokens, u, 1.0, draft_logits=draft)
+    assert acc.cpu().tolist() == n_draft
+
+
+def test_invalid_arguments():
+    from speculative_verify_attention_amd import SvattnError
+
+    banner("accept argument errors")
+    target, draft, tokens, u = synth.accept_inputs([2], 100, 1, "cuda")
+    with pytest.raises(SvattnError):
+        accept([8], torch.zeros((9, 100), device="cuda"), torch.zeros(8, dtype=torch.int32, device="cuda"),
+               torch.zeros(9, device="cuda"), 1.0)
+    with pytest.raises(SvattnError):
+        accept([2], target, tokens, u, -1.0, draft_logits=draft)
