@@ -48,6 +48,103 @@ def workloads():
     }
 
 
+# The acceptance step after the verify forward (not part of the default run):
+# 16 sequences with 4 drafts each, a Qwen3-sized vocabulary, draft-model
+# logits, temperature 0.8.
+ACCEPT_WORKLOADS = {
+    "accept_qwen3_sampled": dict(n_draft=[4] * 16, vocab=151936, temperature=0.8, with_draft=True),
+    "accept_qwen3_greedy": dict(n_draft=[4] * 16, vocab=151936, temperature=0.0, with_draft=True),
+}
+
+
+def run_accept(args, name):
+    """Times spec_accept on seeded logits resident in HBM (replicated past
+    1 GiB so that every call reads HBM, not the MALL)."""
+    import time
+
+    import torch
+
+    from speculative_verify_attention_amd import spec_accept, spec_accept_workspace_bytes, synth
+    from speculative_verify_attention_amd._binding import _check_accept
+
+    cfg = ACCEPT_WORKLOADS[name]
+    n_draft, vocab, temp, with_draft = cfg["n_draft"], cfg["vocab"], cfg["temperature"], cfg["with_draft"]
+    torch.cuda.set_device(0)
+    rows_t, rows_d = sum(n_draft) + len(n_draft), sum(n_draft)
+    # algorithmic bytes: the logits the step must read once (greedy reads
+    # only the target rows)
+    alg = (rows_t + (rows_d if temp > 0 and with_draft else 0)) * vocab * 4
+    reps = max(1, math.ceil((1 << 30) / ((rows_t + rows_d) * vocab * 4)))
+    sets = [synth.accept_inputs(n_draft, vocab, 50 + r, "cuda", with_draft=with_draft, boost=4.0) for r in range(reps)]
+    need = spec_accept_workspace_bytes(n_draft, vocab, with_draft, temp)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    acc = torch.empty(len(n_draft), dtype=torch.int32, device="cuda")
+    tok = torch.empty_like(acc)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        target, draft, tokens, u = sets[i % reps]
+        _check_accept(spec_accept(n_draft, target, draft, tokens, u, temp, acc, tok, ws, stream))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        ev[j][0].record(stream)
+        step(args.warmup + j)
+        ev[j][1].record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    value = rows_d * args.steps / el
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    res = {
+        "metric": "drafts decided/s + logits GB/s (% HBM peak), acceptance step",
+        "value": round(value, 2),
+        "unit": "drafts decided/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(el * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: {len(n_draft)} seqs x {n_draft[0]} drafts, vocab {vocab}, "
+                               f"temperature {temp}, {'draft-model logits' if with_draft else 'point-mass drafts'}",
+                   "input_sets": reps, "step": "spec_accept (row statistics, decisions, final draws)"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "spec_accept (all four kernels)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": alg,
+            "avg_launch_ms": round(call_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        from oracle import accept as A
+
+        target, draft, tokens, u = [None if x is None else x.cpu() for x in sets[0]]
+        tn, dn = target.double().numpy(), None if draft is None else draft.double().numpy()
+        kn, un = tokens.numpy(), u.double().numpy()
+        calls, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < 10.0:
+            A.accept_batch(tn, dn, kn, un, n_draft, temp)
+            calls += 1
+        cel = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": round(rows_d * calls / cel, 3), "unit": "drafts decided/s",
+                               "cores": 1,  # the oracle's per-row softmax and draw are single-threaded numpy
+                               "kind": "oracle", "sample": f"the whole call on input set 0, {calls} times in {cel:.1f} s"}
+    return res
+
+
 def describe(name, wl, layers):
     kv = {0: "fp32", 1: "bf16", 2: "tq3 (3-bit Lloyd-Max + QJL keys, 3-bit values)"}[wl.fmt]
     lens = sorted(set(wl.prefill))
@@ -364,7 +461,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()))
+    ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()) + sorted(ACCEPT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB plain copy first (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the profiles/ summary of a kernel-trace run")
@@ -388,7 +485,7 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
-    res = run(args, args.workload)
+    res = run_accept(args, args.workload) if args.workload in ACCEPT_WORKLOADS else run(args, args.workload)
     print(json.dumps(res), flush=True)
 
 
