@@ -245,7 +245,9 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
  *    cumulative weight (tokens in index order) exceeds u_n times the total.
  *  out_accepted: device int32 [n_seqs]: accepted drafts (0 .. n_draft[i]).
  *  out_token: device int32 [n_seqs]: the token that follows them.
- *  workspace: device, >= spec_accept_workspace_bytes(...), 256-byte aligned.
+ *  workspace: device, >= spec_accept_workspace_bytes(...), 256-byte aligned;
+ *    it holds row statistics, chunk sums and draw plans, so calls
+ *    that share a workspace must not overlap (order them on one stream).
  * Arithmetic is fp32; decisions within about 1e-6 relative of a threshold may
  * differ from an exact evaluation.  The caller rolls the cache back by
  * n_draft[i] - out_accepted[i] (kv_rollback_batch, after copying the counts

@@ -9,18 +9,25 @@
 // (n-gram drafts, AX Engine page, "Core Technical Architecture & Methods")
 // are point masses.
 //
-// Four launches, all reading logits straight from HBM with coalesced loads:
+// Three launches, all reading logits straight from HBM:
 //  1. stats:  one workgroup per (row, 4096-logit chunk): chunk max, first
-//             argmax and sum of exp((l - max) / T);
-//  2. decide: one wave per sequence: combine the chunk statistics of the
-//             rows it needs, walk the drafts, write the accepted count (and
-//             the token, for greedy) and the plan of the final draw;
-//  3. sums:   one workgroup per (sequence, chunk): chunk sums of the final
-//             draw's weights;
-//  4. pick:   one workgroup per sequence: the chunk where u * total falls,
-//             then the token inside it.
-// Every weight is computed by one function in kernels 3 and 4, so the draw
-// sees the same values in both.
+//             argmax and sum of exp((l - max) / T), coalesced 16-byte loads;
+//  2. decide: one workgroup per (sequence, chunk) when sampling (one per
+//             sequence when greedy).  Its waves combine the chunk statistics
+//             of the sequence's rows in parallel, every thread then walks the
+//             drafts from LDS and reaches the same decision; chunk 0 writes
+//             the accepted count (greedy: and the token) and the draw's plan;
+//             sampling: the workgroup sums the draw's weights over its chunk;
+//  3. pick:   one workgroup per sampled sequence: a wave scan over the chunk
+//             sums finds the chunk where u * total falls, a block scan over
+//             runs of 8 logits finds the token.
+// (Handing the draw to the last workgroup of step 2 instead of a third launch
+// needs device-scope release/acquire between workgroups, which on this chip
+// writes back and invalidates the L2 of every XCD; that costs more than a
+// launch.)  One function computes every weight, so the draw sees the same
+// values in the chunk sums and in the final scan.  Nothing is serial over the
+// vocabulary: the only dependent chains are the drafts (at most 7) and the
+// chunk count / 64.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -31,15 +38,21 @@ namespace svattn {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPer = kAcceptChunk / kThreads;  // logits per thread per chunk
+constexpr int kStatThreads = 256;  // stats: 16 logits per thread
+constexpr int kThreads = 512;      // decide and pick: 8 logits per thread
+constexpr int kWaves = kThreads / 64;
+constexpr int kStatPer = kAcceptChunk / kStatThreads;
+constexpr int kPer = kAcceptChunk / kThreads;
+constexpr int kMaxRows = 2 * 7 + 1;  // target + draft rows of one sequence
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// Block-wide max with first index, then (if wanted) sum; 256 threads.
-__device__ __forceinline__ void block_argmax(float& v, int& idx, float* sv, int* si) {
+__device__ __forceinline__ float expt(float l, float m, float inv_t) { return __expf((l - m) * inv_t); }
+
+// Wave-wide max with first index.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(v, o);
@@ -49,79 +62,130 @@ __device__ __forceinline__ void block_argmax(float& v, int& idx, float* sv, int*
       idx = oi;
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    sv[wave] = v;
-    si[wave] = idx;
-  }
-  __syncthreads();
-  v = sv[0];
-  idx = si[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w)
-    if (better(sv[w], si[w], v, idx)) {
-      v = sv[w];
-      idx = si[w];
-    }
-  __syncthreads();
 }
 
-__device__ __forceinline__ float block_sum(float x, float* sv) {
+__device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Block-wide sum in a fixed order (NT threads).
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* sv) {
+  x = wave_sum(x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) sv[wave] = x;
   __syncthreads();
   float t = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) t += sv[w];  // fixed order
+  for (int w = 0; w < NT / 64; ++w) t += sv[w];
   __syncthreads();
   return t;
 }
 
-__device__ __forceinline__ float expt(float l, float m, float inv_t) { return __expf((l - m) * inv_t); }
+// Logits of a chunk in the coalesced order: element e of thread t is token
+// c0 + 4 (e/4 * NT + t) + e%4 with 16-byte loads (VEC: vocab % 4 == 0 and
+// aligned rows), else c0 + e * NT + t.  Tokens past the vocabulary read -inf.
+template <bool VEC, int NT>
+__device__ __forceinline__ int chunk_token(int c0, int e) {
+  if constexpr (VEC) return c0 + 4 * ((e >> 2) * NT + (int)threadIdx.x) + (e & 3);
+  else return c0 + e * NT + (int)threadIdx.x;
+}
 
-// Weight of token x in the final draw of plan pl.
-__device__ __forceinline__ float draw_weight(const AcceptArgs& a, const AcceptPlan& pl, int x) {
-  const float p = expt(a.target[(int64_t)pl.row_t * a.vocab + x], pl.m_t, a.inv_t) / pl.s_t;
-  if (pl.row_q >= 0) {
-    const float q = expt(a.draft[(int64_t)pl.row_q * a.vocab + x], pl.m_q, a.inv_t) / pl.s_q;
-    return fmaxf(0.0f, p - q);
+__device__ __forceinline__ void put4(float* v, float4 f) {
+  v[0] = f.x;
+  v[1] = f.y;
+  v[2] = f.z;
+  v[3] = f.w;
+}
+
+template <bool VEC, int NT, int PER>
+__device__ __forceinline__ void load_chunk(const float* src, int c0, int vocab, float (&v)[PER]) {
+  if constexpr (VEC) {
+#pragma unroll
+    for (int g = 0; g < PER / 4; ++g) {
+      const int x = c0 + 4 * (g * NT + (int)threadIdx.x);
+      float4 f = float4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (x < vocab) f = *reinterpret_cast<const float4*>(src + x);  // vocab % 4 == 0: all four exist
+      put4(v + 4 * g, f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int x = c0 + e * NT + (int)threadIdx.x;
+      v[e] = x < vocab ? src[x] : -INFINITY;
+    }
   }
+}
+
+// The run of kPer consecutive tokens x0 .. x0 + kPer - 1 (x0 % kPer == 0).
+template <bool VEC>
+__device__ __forceinline__ void load_run(const float* src, int x0, int vocab, float (&v)[kPer]) {
+  if constexpr (VEC) {
+#pragma unroll
+    for (int g = 0; g < kPer / 4; ++g) {
+      const int x = x0 + 4 * g;
+      float4 f = float4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (x < vocab) f = *reinterpret_cast<const float4*>(src + x);
+      put4(v + 4 * g, f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) v[e] = x0 + e < vocab ? src[x0 + e] : -INFINITY;
+  }
+}
+
+// Weight of token x in the final draw (lt, lq: its target and draft logits).
+__device__ __forceinline__ float draw_weight(const AcceptPlan& pl, float inv_t, float lt, float lq, int x) {
+  const float p = expt(lt, pl.m_t, inv_t) * pl.is_t;
+  if (pl.row_q >= 0) return fmaxf(0.0f, p - expt(lq, pl.m_q, inv_t) * pl.is_q);
   return x == pl.tok_q ? 0.0f : p;
 }
 
 // 1. Per (row, chunk) statistics.
-__global__ __launch_bounds__(kThreads) void accept_stats_kernel(AcceptArgs a) {
-  __shared__ float sv[kThreads / 64];
-  __shared__ int si[kThreads / 64];
+template <bool VEC>
+__global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a) {
+  __shared__ float sv[kStatThreads / 64];
+  __shared__ int si[kStatThreads / 64];
   const int row = blockIdx.x / a.nch, chunk = blockIdx.x - row * a.nch;
   const float* src = row < a.rows_t ? a.target + (int64_t)row * a.vocab
                                     : a.draft + (int64_t)(row - a.rows_t) * a.vocab;
   const int c0 = chunk * kAcceptChunk;
-  float v[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int x = c0 + e * kThreads + threadIdx.x;  // each load: 256 consecutive logits
-    v[e] = x < a.vocab ? src[x] : -INFINITY;
-  }
+  float v[kStatPer];
+  load_chunk<VEC, kStatThreads, kStatPer>(src, c0, a.vocab, v);
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int x = c0 + e * kThreads + threadIdx.x;
+  for (int e = 0; e < kStatPer; ++e) {
+    const int x = chunk_token<VEC, kStatThreads>(c0, e);
     if (x < a.vocab && better(v[e], x, bv, bi)) {
       bv = v[e];
       bi = x;
     }
   }
-  block_argmax(bv, bi, sv, si);
+  wave_argmax(bv, bi);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  bv = sv[0];
+  bi = si[0];
+#pragma unroll
+  for (int w = 1; w < kStatThreads / 64; ++w)
+    if (better(sv[w], si[w], bv, bi)) {
+      bv = sv[w];
+      bi = si[w];
+    }
+  __syncthreads();
   float sum = 0.0f;
   if (a.inv_t > 0.0f) {
     float t = 0.0f;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) t += expt(v[e], bv, a.inv_t);  // -inf -> 0
-    sum = block_sum(t, sv);
+    for (int e = 0; e < kStatPer; ++e) t += expt(v[e], bv, a.inv_t);  // -inf -> 0
+    sum = block_sum<kStatThreads>(t, sv);
   }
   if (threadIdx.x == 0) a.stats[blockIdx.x] = float4{bv, sum, __int_as_float(bi), 0.0f};
 }
@@ -136,187 +200,129 @@ struct RowStats {
 __device__ __forceinline__ RowStats row_stats(const AcceptArgs& a, int row) {
   const int lane = threadIdx.x & 63;
   const float4* st = a.stats + (int64_t)row * a.nch;
-  float m = -INFINITY;
-  int arg = 0x7FFFFFFF;
-  for (int c = lane; c < a.nch; c += 64) {
+  const float4 none = float4{-INFINITY, 0.0f, __int_as_float(0x7FFFFFFF), 0.0f};
+  // chunks lane and lane + 64 stay in registers (one round trip up to 128 chunks)
+  const float4 x0 = lane < a.nch ? st[lane] : none;
+  const float4 x1 = lane + 64 < a.nch ? st[lane + 64] : none;
+  float m = x0.x;
+  int arg = __float_as_int(x0.z);
+  if (better(x1.x, __float_as_int(x1.z), m, arg)) {
+    m = x1.x;
+    arg = __float_as_int(x1.z);
+  }
+  for (int c = lane + 128; c < a.nch; c += 64) {
     const float4 x = st[c];
     if (better(x.x, __float_as_int(x.z), m, arg)) {
       m = x.x;
       arg = __float_as_int(x.z);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float om = __shfl_xor(m, o);
-    const int oa = __shfl_xor(arg, o);
-    if (better(om, oa, m, arg)) {
-      m = om;
-      arg = oa;
-    }
-  }
+  wave_argmax(m, arg);
   float s = 0.0f;
   if (a.inv_t > 0.0f) {
-    for (int c = lane; c < a.nch; c += 64) {
+    s = x0.y * expt(x0.x, m, a.inv_t) + x1.y * expt(x1.x, m, a.inv_t);  // -inf -> 0
+    for (int c = lane + 128; c < a.nch; c += 64) {
       const float4 x = st[c];
       s += x.y * expt(x.x, m, a.inv_t);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    s = wave_sum(s);
   }
   return RowStats{m, s, arg};
 }
 
-// 2. Decide each sequence of the group.
-__global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a) {
-  const int i = blockIdx.x;  // sequence within the group
-  const int n = a.n[i], t0 = a.t0[i], d0 = a.d0[i];
-  const int sidx = a.seq0 + i;
-  AcceptPlan pl{};
-  pl.mode = 0;
-  pl.row_q = -1;
-  pl.tok_q = -1;
-  int acc = n, tok = -1;
-  if (a.inv_t == 0.0f) {
-    for (int j = 0; j < n; ++j) {
-      const int am = row_stats(a, t0 + j).arg;
-      if (a.drafts[d0 + j] != am) {
-        acc = j;
-        tok = am;
-        break;
-      }
-    }
-    if (acc == n) tok = row_stats(a, t0 + n).arg;
-  } else {
-    pl.mode = 1;
-    pl.u = a.u[t0 + n];
-    bool rejected = false;
-    for (int j = 0; j < n && !rejected; ++j) {
-      const RowStats rt = row_stats(a, t0 + j);
-      const int d = a.drafts[d0 + j];
-      const bool valid = d >= 0 && d < a.vocab;
-      const float pd = valid ? expt(a.target[(int64_t)(t0 + j) * a.vocab + d], rt.m, a.inv_t) / rt.s : 0.0f;
-      float qd = 1.0f;
-      RowStats rq{0.0f, 1.0f, 0};
-      if (a.draft) {
-        rq = row_stats(a, a.rows_t + d0 + j);
-        if (valid) qd = expt(a.draft[(int64_t)(d0 + j) * a.vocab + d], rq.m, a.inv_t) / rq.s;
-      }
-      if (!(a.u[t0 + j] * qd < pd)) {
-        rejected = true;
-        acc = j;
-        pl.row_t = t0 + j;
-        pl.m_t = rt.m;
-        pl.s_t = rt.s;
-        if (a.draft) {
-          pl.row_q = d0 + j;
-          pl.m_q = rq.m;
-          pl.s_q = rq.s;
-        } else {
-          pl.tok_q = valid ? d : -1;
-        }
-      }
-    }
-    if (!rejected) {
-      const RowStats rt = row_stats(a, t0 + n);
-      pl.row_t = t0 + n;
-      pl.m_t = rt.m;
-      pl.s_t = rt.s;
-    }
-  }
-  if (threadIdx.x == 0) {
-    a.out_acc[sidx] = acc;
-    if (pl.mode == 0) a.out_tok[sidx] = tok;
-    a.plan[sidx] = pl;
-  }
-}
-
-// 3. Chunk sums of the final draw's weights.
-__global__ __launch_bounds__(kThreads) void accept_sums_kernel(AcceptArgs a) {
-  __shared__ float sv[kThreads / 64];
-  const int i = blockIdx.x / a.nch, chunk = blockIdx.x - i * a.nch;
-  const int sidx = a.seq0 + i;
-  const AcceptPlan pl = a.plan[sidx];
-  if (pl.mode == 0) return;
-  const int c0 = chunk * kAcceptChunk;
-  float t = 0.0f;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int x = c0 + e * kThreads + threadIdx.x;
-    if (x < a.vocab) t += draw_weight(a, pl, x);
-  }
-  const float s = block_sum(t, sv);
-  if (threadIdx.x == 0) a.fsum[(int64_t)sidx * a.nch + chunk] = s;
-}
-
-// 4. The token: smallest x with cumulative weight > u * total (tokens in
-// index order); chunk by chunk, then inside the chunk.
-__global__ __launch_bounds__(kThreads) void accept_pick_kernel(AcceptArgs a) {
-  __shared__ int s_chunk;
-  __shared__ float s_rem;
-  __shared__ float part[kThreads];
+// The final draw of one sequence from its chunk sums fs: the smallest token x
+// with cumulative weight > u * total (tokens in index order).  Every wave
+// finds the chunk the same way from the same values; then a block scan over
+// runs of kPer tokens.
+template <bool VEC>
+__device__ void draw_token(const AcceptArgs& a, const AcceptPlan& pl, int sidx, const float* fs) {
+  __shared__ float wsum[kWaves];
   __shared__ int s_tok, s_last;
-  const int i = blockIdx.x;
-  const int sidx = a.seq0 + i;
-  const AcceptPlan pl = a.plan[sidx];
-  if (pl.mode == 0) return;
-  const float* fs = a.fsum + (int64_t)sidx * a.nch;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) {
-    float total = 0.0f;
-    for (int c = 0; c < a.nch; ++c) total += fs[c];
-    const float target = pl.u * total;
-    float cum = 0.0f;
-    int pick = -1, lastpos = 0;
-    float rem = 0.0f;
-    for (int c = 0; c < a.nch; ++c) {
-      if (fs[c] > 0.0f) lastpos = c;
-      if (pick < 0 && cum + fs[c] > target) {
-        pick = c;
-        rem = target - cum;
-      }
-      cum += fs[c];
-    }
-    if (pick < 0) {  // rounding put u * total at or past the end
-      pick = lastpos;
-      rem = INFINITY;
-    }
-    s_chunk = pick;
-    s_rem = rem;
     s_tok = 0x7FFFFFFF;
     s_last = -1;
   }
-  __syncthreads();
-  const int c0 = s_chunk * kAcceptChunk;
-  const float rem = s_rem;
-  // thread t owns logits c0 + kPer t .. +kPer (contiguous: a sequential scan)
-  float w[kPer];
-  float t = 0.0f;
-  int lastpos = -1;
+  // inclusive scan of the chunk sums in chunk order, 64 at a time; total =
+  // the last value, so u < 1 always lands inside
+  auto scan64 = [&](float f) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int x = c0 + kPer * threadIdx.x + e;
-    w[e] = x < a.vocab ? draw_weight(a, pl, x) : 0.0f;
-    t += w[e];
-    if (w[e] > 0.0f) lastpos = x;
-  }
-  part[threadIdx.x] = t;
-  if (lastpos >= 0) atomicMax(&s_last, lastpos);
-  __syncthreads();
-  if (threadIdx.x == 0) {  // exclusive scan in thread order
-    float cum = 0.0f;
-    for (int k = 0; k < kThreads; ++k) {
-      const float x = part[k];
-      part[k] = cum;
-      cum += x;
+    for (int o = 1; o < 64; o <<= 1) {
+      const float up = __shfl_up(f, o);
+      if (lane >= o) f += up;
+    }
+    return f;
+  };
+  float rem = INFINITY;
+  int pick = -1, lastpos = -1;
+  if (a.nch <= 64) {  // one round trip
+    const float f = lane < a.nch ? fs[lane] : 0.0f;
+    const float inc = scan64(f);
+    const float target = pl.u * __shfl(inc, 63);
+    const uint64_t pos = __builtin_amdgcn_ballot_w64(f > 0.0f);
+    if (pos) lastpos = 63 - __builtin_clzll(pos);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.nch && inc > target);
+    if (hit) {
+      pick = __builtin_ctzll(hit);
+      rem = target - (__shfl(inc, pick) - __shfl(f, pick));
+    }
+  } else {
+    float total = 0.0f;
+    for (int base = 0; base < a.nch; base += 64)
+      total += __shfl(scan64(base + lane < a.nch ? fs[base + lane] : 0.0f), 63);
+    const float target = pl.u * total;
+    float carry = 0.0f;
+    for (int base = 0; base < a.nch; base += 64) {
+      const int c = base + lane;
+      const float f = c < a.nch ? fs[c] : 0.0f;
+      const float inc = scan64(f);
+      const uint64_t pos = __builtin_amdgcn_ballot_w64(f > 0.0f);
+      if (pos) lastpos = base + 63 - __builtin_clzll(pos);
+      if (pick < 0) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(c < a.nch && carry + inc > target);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          pick = base + l;
+          rem = target - (carry + __shfl(inc, l) - __shfl(f, l));
+        }
+      }
+      carry += __shfl(inc, 63);
     }
   }
-  __syncthreads();
-  float cum = part[threadIdx.x];
+  if (pick < 0) pick = lastpos >= 0 ? lastpos : 0;  // rounding put u * total at or past the end
+
+  // thread t owns tokens c0 + kPer t .. c0 + kPer t + kPer - 1
+  const int c0 = pick * kAcceptChunk;
+  const int x0 = c0 + kPer * (int)threadIdx.x;
+  float lt[kPer], lq[kPer], w[kPer];
+  load_run<VEC>(a.target + (int64_t)pl.row_t * a.vocab, x0, a.vocab, lt);
+  if (pl.row_q >= 0) load_run<VEC>(a.draft + (int64_t)pl.row_q * a.vocab, x0, a.vocab, lq);
+  float ts = 0.0f;
+  int mylast = -1;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    w[e] = x0 + e < a.vocab ? draw_weight(pl, a.inv_t, lt[e], pl.row_q >= 0 ? lq[e] : 0.0f, x0 + e) : 0.0f;
+    ts += w[e];
+    if (w[e] > 0.0f) mylast = x0 + e;
+  }
+  // exclusive block scan of the runs' sums in thread order
+  float inc = ts;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float up = __shfl_up(inc, o);
+    if (lane >= o) inc += up;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();  // also orders the s_tok / s_last initialisation before the atomics
+  float cum = inc - ts;
+  for (int w2 = 0; w2 < wave; ++w2) cum += wsum[w2];
+  if (mylast >= 0) atomicMax(&s_last, mylast);
   if (cum <= rem) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       cum += w[e];
       if (cum > rem) {
-        atomicMin(&s_tok, c0 + kPer * threadIdx.x + e);
+        atomicMin(&s_tok, x0 + e);
         break;
       }
     }
@@ -325,21 +331,134 @@ __global__ __launch_bounds__(kThreads) void accept_pick_kernel(AcceptArgs a) {
   if (threadIdx.x == 0) a.out_tok[sidx] = s_tok != 0x7FFFFFFF ? s_tok : (s_last >= 0 ? s_last : c0);
 }
 
+// 2. Decide each sequence of the group; sum the draw's weights over a chunk.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void accept_decide_kernel(AcceptArgs a) {
+  __shared__ float r_m[kMaxRows], r_is[kMaxRows], r_l[kMaxRows], r_u[kMaxRows];
+  __shared__ int r_arg[kMaxRows], r_tok[kMaxRows];
+  __shared__ float sv[kWaves];
+  const bool samp = a.inv_t > 0.0f;
+  const int per_seq = samp ? a.nch : 1;
+  const int i = blockIdx.x / per_seq, chunk = blockIdx.x - i * per_seq;
+  const int n = a.n[i], t0 = a.t0[i], d0 = a.d0[i];
+  const int sidx = a.seq0 + i;
+  const bool has_q = samp && a.draft != nullptr;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // rows 0..n: target rows j; rows n+1 .. 2n: draft rows j (sampling with a
+  // draft); one wave per row, all rows at once
+  const int R = n + 1 + (has_q ? n : 0);
+  for (int r = wave; r < R; r += kWaves) {
+    const bool tr = r <= n;
+    const int j = tr ? r : r - n - 1;
+    const int grow = tr ? t0 + j : a.rows_t + d0 + j;
+    const float* src = tr ? a.target + (int64_t)(t0 + j) * a.vocab : a.draft + (int64_t)(d0 + j) * a.vocab;
+    const int tok = j < n ? a.drafts[d0 + j] : -1;
+    const RowStats rs = row_stats(a, grow);
+    const float l = (samp && tok >= 0 && tok < a.vocab) ? src[tok] : -INFINITY;
+    if (lane == 0) {
+      r_m[r] = rs.m;
+      r_is[r] = samp ? 1.0f / rs.s : 0.0f;
+      r_arg[r] = rs.arg;
+      r_tok[r] = tok;
+      r_l[r] = l;
+      r_u[r] = (samp && tr) ? a.u[t0 + j] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  AcceptPlan pl{};
+  pl.row_q = -1;
+  pl.tok_q = -1;
+  int acc = n, tok = -1;
+  if (!samp) {
+    for (int j = 0; j < n; ++j)
+      if (r_tok[j] != r_arg[j]) {
+        acc = j;
+        tok = r_arg[j];
+        break;
+      }
+    if (acc == n) tok = r_arg[n];
+  } else {
+    pl.mode = 1;
+    pl.u = r_u[n];
+    int rt = n, rq = -1;
+    for (int j = 0; j < n; ++j) {
+      const int d = r_tok[j];
+      const bool valid = d >= 0 && d < a.vocab;
+      const float pd = valid ? expt(r_l[j], r_m[j], a.inv_t) * r_is[j] : 0.0f;
+      const float qd = (has_q && valid) ? expt(r_l[n + 1 + j], r_m[n + 1 + j], a.inv_t) * r_is[n + 1 + j] : 1.0f;
+      if (!(r_u[j] * qd < pd)) {
+        acc = j;
+        rt = j;
+        if (has_q) rq = n + 1 + j;
+        else pl.tok_q = valid ? d : -1;
+        break;
+      }
+    }
+    pl.row_t = t0 + rt;
+    pl.m_t = r_m[rt];
+    pl.is_t = r_is[rt];
+    if (rq >= 0) {
+      pl.row_q = d0 + (rq - n - 1);
+      pl.m_q = r_m[rq];
+      pl.is_q = r_is[rq];
+    }
+  }
+  if (chunk == 0 && threadIdx.x == 0) {
+    a.out_acc[sidx] = acc;
+    if (!samp) a.out_tok[sidx] = tok;
+    else a.plan[sidx] = pl;
+  }
+  if (!samp) return;
+
+  const int c0 = chunk * kAcceptChunk;
+  float lt[kPer], lq[kPer];
+  load_chunk<VEC, kThreads, kPer>(a.target + (int64_t)pl.row_t * a.vocab, c0, a.vocab, lt);
+  if (pl.row_q >= 0) load_chunk<VEC, kThreads, kPer>(a.draft + (int64_t)pl.row_q * a.vocab, c0, a.vocab, lq);
+  float t = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int x = chunk_token<VEC, kThreads>(c0, e);
+    if (x < a.vocab) t += draw_weight(pl, a.inv_t, lt[e], pl.row_q >= 0 ? lq[e] : 0.0f, x);
+  }
+  const float s = block_sum<kThreads>(t, sv);
+  if (threadIdx.x == 0) a.fsum[(int64_t)sidx * a.nch + chunk] = s;
+}
+
+// 3. The draw of each sampled sequence.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void accept_pick_kernel(AcceptArgs a) {
+  const int sidx = a.seq0 + (int)blockIdx.x;
+  draw_token<VEC>(a, a.plan[sidx], sidx, a.fsum + (int64_t)sidx * a.nch);
+}
+
+bool vec_ok(const AcceptArgs& a) {
+  return a.vocab % 4 == 0 && reinterpret_cast<uintptr_t>(a.target) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.draft) % 16 == 0;
+}
+
 }  // namespace
 
 hipError_t launch_accept_stats(const AcceptArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)(a.rows_t + a.rows_d) * a.nch;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(accept_stats_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  if (vec_ok(a))
+    hipLaunchKernelGGL(accept_stats_kernel<true>, dim3((unsigned)blocks), dim3(kStatThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(accept_stats_kernel<false>, dim3((unsigned)blocks), dim3(kStatThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_accept_group(const AcceptArgs& a, hipStream_t s) {
   if (a.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(accept_decide_kernel, dim3(a.count), dim3(64), 0, s, a);
-  if (a.inv_t > 0.0f) {
-    hipLaunchKernelGGL(accept_sums_kernel, dim3(a.count * a.nch), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(accept_pick_kernel, dim3(a.count), dim3(kThreads), 0, s, a);
+  const bool samp = a.inv_t > 0.0f, vec = vec_ok(a);
+  const dim3 grid(samp ? a.count * a.nch : a.count);
+  if (vec) hipLaunchKernelGGL(accept_decide_kernel<true>, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(accept_decide_kernel<false>, grid, dim3(kThreads), 0, s, a);
+  if (samp) {
+    if (vec) hipLaunchKernelGGL(accept_pick_kernel<true>, dim3(a.count), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(accept_pick_kernel<false>, dim3(a.count), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

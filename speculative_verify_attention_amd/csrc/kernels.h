@@ -191,20 +191,21 @@ struct QPrepArgs {
 //
 // Rows: the target rows of all sequences (sum of n+1), then the draft rows
 // (sum of n).  A row is cut into chunks of kAcceptChunk logits; the first
-// kernel reduces every (row, chunk), the second decides each sequence, the
-// last two draw the final token of sampled sequences from their weights.
+// kernel reduces every (row, chunk); the second decides each sequence (every
+// workgroup of a sequence takes the same decision from the row statistics)
+// and sums the final draw's weights over one chunk; the third draws the token.
 constexpr int kMaxAcceptSeqs = 128;
 constexpr int kAcceptChunk = 4096;
 
-// Per-sequence decision handed from the decide kernel to the draw kernels.
+// Per-sequence draw handed from the decide kernel to the pick kernel.
 struct AcceptPlan {
-  int32_t mode;   // 0 token already written (greedy), 1 draw from the weights
-  int32_t row_t;  // target row of the weights
-  int32_t row_q;  // draft row (-1: none)
-  int32_t tok_q;  // point-mass draft token whose mass is removed (-1: none)
-  float m_t, s_t; // target row max and sum of exp((l - max) / T)
-  float m_q, s_q; // draft row, likewise
-  float u;        // uniform of the draw
+  int32_t mode;    // 0 token already written (greedy), 1 draw from the weights
+  int32_t row_t;   // target row of the weights
+  int32_t row_q;   // draft row (-1: none)
+  int32_t tok_q;   // point-mass draft token whose mass is removed (-1: none)
+  float m_t, is_t; // target row max and 1 / sum of exp((l - max) / T)
+  float m_q, is_q; // draft row, likewise
+  float u;         // uniform of the draw
   int32_t pad[3];
 };
 
@@ -217,7 +218,7 @@ struct AcceptArgs {
   int32_t* out_tok;
   float4* stats;            // [rows_t + rows_d][nch]: max, sum, argmax bits, -
   AcceptPlan* plan;         // [n_seqs]
-  float* fsum;              // [n_seqs][nch]
+  float* fsum;              // [n_seqs][nch] chunk sums of each draw's weights
   float inv_t;              // 1 / temperature, 0 = greedy
   int32_t vocab, nch, rows_t, rows_d;
   int32_t seq0, count;      // this launch group's sequences

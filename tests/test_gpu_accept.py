@@ -67,7 +67,7 @@ def compare(acc, tok, ora, sampled):
     return excluded
 
 
-@pytest.mark.parametrize("vocab", [1000, 5003, 151936])
+@pytest.mark.parametrize("vocab", [1000, 5003, 151936, 300001])
 def test_greedy_exact(vocab):
     banner(f"accept greedy vocab={vocab}")
     n_draft = [4, 0, 3, 4, 1, 2, 4, 4]
@@ -77,7 +77,8 @@ def test_greedy_exact(vocab):
 
 
 @pytest.mark.parametrize("vocab,temperature,with_draft", [(1000, 1.0, True), (5003, 0.7, True), (151936, 0.8, True),
-                                                          (151936, 1.0, False), (4097, 2.0, False)])
+                                                          (151936, 1.0, False), (4097, 2.0, False),
+                                                          (300000, 0.9, True), (270339, 1.1, False)])
 def test_sampling_parity(vocab, temperature, with_draft):
     banner(f"accept sampling vocab={vocab} T={temperature} draft={with_draft}")
     rng = np.random.default_rng(vocab)
