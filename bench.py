@@ -3,8 +3,10 @@
 
 A step is one pass of the whole path over one batch: roll back the previous
 step's draft rows (host, O(1) per sequence), append the new rows into their
-blocks (quantize-on-append for compressed caches), and run the verify
-attention (partials + merge).  Steps rotate over enough independent layer
+blocks and run the verify attention over them (kv_append_verify: for the
+plain formats the attention kernel writes the rows itself; compressed caches
+quantize on append in a launch before it), partials + merge.  --separate
+times kv_append + spec_verify_attn instead.  Steps rotate over enough independent layer
 caches (>= 1 GiB in all) that the 256 MB Infinity Cache cannot hold the
 working set, as successive layers of a model would.
 
@@ -281,7 +283,9 @@ def run(args, name):
     seqs = list(range(wl.n_seqs))
     # one workspace per (replica, layer): the partial-slot count is bounded by
     # the workgroup target plus the (sequence, kv head) pairs, whatever the lengths
-    ws_need = max(runners[0].caches[li].workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq, layers[li][0])
+    ws_need = max(max(runners[0].caches[li].workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq, layers[li][0]),
+                      runners[0].caches[li].append_verify_workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq,
+                                                                          layers[li][0]))
                   for li in range(len(layers)))
     ws = [[torch.empty(2 * ws_need, dtype=torch.uint8, device=dev) for _ in layers] for _ in range(reps)]
     hip = Hip()
@@ -304,13 +308,18 @@ def run(args, name):
         if any(back):
             for c in r.caches:
                 c.rollback_batch(seqs, back)
-        for c in r.caches:
-            c.append(seqs, rows, k, v)
+        if args.separate:
+            for c in r.caches:
+                c.append(seqs, rows, k, v)
         lens[rep] = [L - b + n for L, b, n in zip(lens[rep], back, rows)]
         for li, c in enumerate(r.caches):
             if li == dom and timed_idx is not None:
                 c.trace_events(*ev[timed_idx])
-            c.verify(seqs, rows, q, wl.hq, wl.scale, layers[li][1], layers[li][0], out=out, workspace=ws[rep][li])
+            window, cap = layers[li][0], layers[li][1]
+            if args.separate:
+                c.verify(seqs, rows, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
+            else:
+                c.append_verify(seqs, rows, k, v, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
             if li == dom and timed_idx is not None:
                 c.trace_events(None, None)
         last_rows[rep] = rows
@@ -356,7 +365,9 @@ def run(args, name):
         "dtype": {0: "f32", 1: "bf16", 2: "f16"}[wl.fmt],
         "data": "synthetic",
         "config": {"workload": describe(name, wl, layers), "layer_replicas": reps,
-                   "step": "rollback previous drafts + append new rows + verify attention (partials + merge)"},
+                   "step": ("rollback previous drafts + append new rows + verify attention (partials + merge)"
+                            + (", append and verify as separate calls" if args.separate else
+                               ", append and verify in one call (kv_append_verify)"))},
         "effective_kv_gbs": round(kv_gbs, 2),
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -463,6 +474,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()) + sorted(ACCEPT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="append and verify as two calls (kv_append + spec_verify_attn) instead of kv_append_verify")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB plain copy first (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the profiles/ summary of a kernel-trace run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

@@ -31,9 +31,11 @@
  *    kv_last_error() gives a message for the last failure on a handle.
  *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).  All
  *    device work of a call is enqueued on it; no call waits for the device
- *    except kv_create (once, for its constant uploads) and kv_destroy.  A
- *    handle is not thread-safe; calls on one handle must be issued from one
- *    thread and, if they use different streams, ordered by the caller.
+ *    except kv_create (once, for its constant uploads), kv_sync, and the
+ *    host-side calls that first apply pending device rollbacks (see
+ *    kv_rollback_device).  A handle is not thread-safe; calls on one handle
+ *    must be issued from one thread and, if they use different streams,
+ *    ordered by the caller.
  *  - "host" pointer arguments are read during the call only.  "device"
  *    pointers must stay valid until the enqueued work has finished.
  *  - Device faults are not detected synchronously; a sticky HIP error seen at
@@ -83,8 +85,9 @@ typedef struct {
 
 /*
  * Bytes of device memory a pool for these parameters needs (blocks followed
- * by the library's metadata: the device block table and, for KV_TQ3, the
- * codec constants).  p->pool and p->pool_bytes are ignored.
+ * by the library's metadata: the device block table, a status word, the
+ * pending device-rollback counters and, for KV_TQ3, the codec constants).
+ * p->pool and p->pool_bytes are ignored.
  *
  * Block layout.  A block holds 256 token positions of every kv head: first
  * each head's K region in head order, then each head's V region.  d =
@@ -158,6 +161,36 @@ int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens);
  */
 int kv_rollback_batch(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens);
 
+/*
+ * Roll sequences back on the device, from acceptance counts the device
+ * produced (spec_accept's out_accepted), without a device-to-host copy: the
+ * rollback the AX Engine page describes ("Core Technical Architecture &
+ * Methods": O(1), the length pointer only) moved to the device so that a
+ * decode step (append, verify, accept, rollback) never waits for the host.
+ * Sequence seq_ids[i] loses n_draft[i] - accepted[i] positions (accepted[i]
+ * clamped to [0, n_draft[i]]).
+ *  seq_ids, n_draft: host arrays of n_seqs entries; ids distinct;
+ *    0 <= n_draft[i] <= the sequence's length.
+ *  accepted: device int32 [n_seqs].
+ * Until kv_sync, the host knows each length only up to the pending amount:
+ * kv_append and spec_verify_attn / kv_append_verify read the exact lengths
+ * on the device (reservations cover the upper bound; blocks stay owned
+ * anyway).  kv_rollback, kv_rollback_batch, kv_seq_free, kv_seq_len and
+ * kv_block_table first apply the pending rollbacks (kv_sync).  Every
+ * kv_rollback_device call between two syncs must use the same stream.
+ * Errors: KV_ENOSEQ, KV_EINVAL, KV_ERANGE, KV_EDEVICE.
+ */
+int kv_rollback_device(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_draft,
+                       const int32_t* accepted, void* stream);
+
+/*
+ * Apply pending device rollbacks to the host state: copies the counters from
+ * the device (waiting for the stream of the last kv_rollback_device call),
+ * moves the host lengths, clears the counters.  A no-op without pending
+ * rollbacks.  Errors: KV_EDEVICE.
+ */
+int kv_sync(kv_cache* c);
+
 /* Release every block of a sequence (pushed back onto the front of the free
  * list, first-owned block first) and reset its length to 0.  The caller must
  * not free a sequence that enqueued work still reads.  Errors: KV_ENOSEQ. */
@@ -219,6 +252,35 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
                      int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Append the verified rows' K/V and verify them, in one call: kv_append of
+ * n_rows[i] positions to each sequence followed by spec_verify_attn over
+ * those same positions (AX Engine page, "Core Technical Architecture &
+ * Methods": slice-update appends; SwiftLM page, speculative-decoding
+ * passage: the N+1 positions verified at once).  For KV_FP32 and KV_BF16
+ * the attention kernel itself writes the rows into their blocks before it
+ * reads them, so the append costs no launch of its own; KV_TQ3 encodes in a
+ * launch before the attention.
+ *  k, v: as kv_append's, [sum(n_rows)][num_kv_heads][head_dim], rows in the
+ *    order of q's rows.
+ *  Everything else as spec_verify_attn's; the row positions count the
+ *  appended rows (row r of sequence i sits at seq_len + r before the call).
+ *  workspace: ws_bytes >= kv_append_verify_workspace_bytes(...).
+ * The stored bytes and outputs equal those of kv_append followed by
+ * spec_verify_attn.  Errors: the union of both calls' errors; a failed call
+ * changes nothing.
+ */
+int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                     const void* k, const void* v, const float* q, int32_t num_q_heads, float scale,
+                     float softcap, int32_t window, float* out, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes of kv_append_verify for this call shape (planned with the
+ * lengths after the append).  Errors as kv_append_verify's validation. */
+int kv_append_verify_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids,
+                                     const int32_t* n_rows, int32_t num_q_heads, int32_t window,
+                                     size_t* out);
+
+/*
  * Acceptance of the drafts after the verify forward (SwiftLM page,
  * speculative-decoding passage: rejection sampling per Leviathan et al., the
  * ratio P_target / P_draft deciding each draft and a rejected position
@@ -268,7 +330,8 @@ int spec_accept_workspace_bytes(int32_t n_seqs, const int32_t* n_draft, int32_t 
 const char* spec_accept_last_error(void);
 
 /*
- * Tracing: while set, every spec_verify_attn call records event `before` on
+ * Tracing: while set, every spec_verify_attn and kv_append_verify call
+ * records event `before` on
  * its stream just before its first attention-partial kernel and `after` just
  * after its last one (hipEvent_t handles passed as void*, owned by the
  * caller), so that hipEventElapsedTime gives the partial kernels' time
@@ -276,7 +339,8 @@ const char* spec_accept_last_error(void);
  */
 int kv_trace_events(kv_cache* c, void* before, void* after);
 
-/* ---- introspection (host only; never touches the device) ---- */
+/* ---- introspection (host only; touches the device only to apply pending
+ * device rollbacks first) ---- */
 
 /* Current length of a sequence.  Errors: KV_ENOSEQ. */
 int kv_seq_len(const kv_cache* c, int32_t seq_id, int32_t* out);

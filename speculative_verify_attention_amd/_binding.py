@@ -83,6 +83,11 @@ _SIGS = {
     "kv_workspace_bytes": [_p, _i32, _i32p, _i32p, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)],
     "spec_verify_attn": [_p, _i32, _i32p, _i32p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p,
                          ctypes.c_size_t, _p],
+    "kv_append_verify": [_p, _i32, _i32p, _i32p, _p, _p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p,
+                         ctypes.c_size_t, _p],
+    "kv_append_verify_workspace_bytes": [_p, _i32, _i32p, _i32p, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)],
+    "kv_rollback_device": [_p, _i32, _i32p, _i32p, _p, _p],
+    "kv_sync": [_p],
     "kv_seq_len": [_p, _i32, _i32p],
     "kv_block_table": [_p, _i32, _i32p, _i32, _i32p],
     "kv_free_blocks": [_p, _i32p],
@@ -223,6 +228,32 @@ def spec_verify_attn(h, seq_ids, n_rows, q, num_q_heads, scale, softcap, window,
                                   num_q_heads, float(scale), float(softcap), window,
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws_ptr), ws_bytes,
                                   _stream_ptr(stream))
+
+
+def kv_append_verify_workspace_bytes(h, seq_ids, n_rows, num_q_heads, window):
+    out = ctypes.c_size_t()
+    rc = lib().kv_append_verify_workspace_bytes(h, len(seq_ids), _arr(seq_ids), _arr(n_rows), num_q_heads, window,
+                                                ctypes.byref(out))
+    _check(rc, h)
+    return out.value
+
+
+def kv_append_verify(h, seq_ids, n_rows, k, v, q, num_q_heads, scale, softcap, window, out, workspace, stream=None):
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return lib().kv_append_verify(h, len(seq_ids), _arr(seq_ids), _arr(n_rows), ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(q.data_ptr()), num_q_heads,
+                                  float(scale), float(softcap), window, ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(ws_ptr), ws_bytes, _stream_ptr(stream))
+
+
+def kv_rollback_device(h, seq_ids, n_draft, accepted, stream=None):
+    return lib().kv_rollback_device(h, len(seq_ids), _arr(seq_ids), _arr(n_draft),
+                                    ctypes.c_void_p(accepted.data_ptr()), _stream_ptr(stream))
+
+
+def kv_sync(h):
+    return lib().kv_sync(h)
 
 
 def kv_seq_len(h, seq_id):
@@ -412,6 +443,46 @@ class KVCache:
         _check(spec_verify_attn(self.handle, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out,
                                 workspace, stream), self.handle)
         return out
+
+    def append_verify(self, seq_ids, n_rows, k, v, q, num_q_heads, scale, softcap=0.0, window=0, out=None,
+                      workspace=None, stream=None):
+        """kv_append of the verified rows' K/V, then verify them: one call
+        (for the plain formats the attention kernel writes the rows itself)."""
+        import torch
+
+        rows = int(sum(n_rows))
+        dt = torch.bfloat16 if self.fmt == KV_BF16 else torch.float32
+        for name, t in (("k", k), ("v", v)):
+            self._check_rows(name, t, rows, self.num_kv_heads, dt)
+        self._check_rows("q", q, rows, num_q_heads, torch.float32)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_rows("out", out, rows, num_q_heads, torch.float32)
+        if workspace is None:
+            need = max(256, kv_append_verify_workspace_bytes(self.handle, seq_ids, n_rows, num_q_heads, window))
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+            workspace = self._ws
+        _check(kv_append_verify(self.handle, seq_ids, n_rows, k, v, q, num_q_heads, scale, softcap, window, out,
+                                workspace, stream), self.handle)
+        return out
+
+    def append_verify_workspace_bytes(self, seq_ids, n_rows, num_q_heads, window=0):
+        return kv_append_verify_workspace_bytes(self.handle, seq_ids, n_rows, num_q_heads, window)
+
+    def rollback_device(self, seq_ids, n_draft, accepted, stream=None):
+        """Roll back n_draft[i] - accepted[i] positions, accepted being a
+        device int32 tensor (spec_accept's output): no host round trip."""
+        import torch
+
+        if (not isinstance(accepted, torch.Tensor) or accepted.device.type != "cuda" or accepted.dtype != torch.int32
+                or not accepted.is_contiguous() or accepted.numel() < len(seq_ids)):
+            raise ValueError("accepted must be a contiguous CUDA int32 tensor with an entry per sequence")
+        return _check(kv_rollback_device(self.handle, seq_ids, n_draft, accepted, stream), self.handle)
+
+    def sync(self):
+        """Apply pending device rollbacks to the host state (waits for them)."""
+        return _check(kv_sync(self.handle), self.handle)
 
     def encode(self, src, is_key, dst=None, stream=None):
         import torch

@@ -48,7 +48,42 @@ hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- device-side rollback --------------------------------------------------------
+
+// One thread per entry; sequence ids are distinct within a call, so no two
+// threads touch one counter.
+__global__ void rollback_kernel(RollbackArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.count) return;
+  const int n = a.n_draft[i];
+  const int r = n - min(max(a.accepted[i], 0), n);
+  a.roll[a.seq[i]] += r;
+}
+
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rollback_kernel, dim3((a.count + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// A fill kernel rather than hipMemsetAsync, so that callers may capture it.
+__global__ void fill_zero_kernel(int32_t* p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(int32_t* p, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 // ---- helpers --------------------------------------------------------------------
+
+// First position of segment seg after any pending device rollback.
+__device__ inline int seg_pos0(const AppendArgs& a, int seg) {
+  return a.roll ? a.pos0[seg] - a.roll[a.seq[seg]] : a.pos0[seg];
+}
 
 __device__ inline int find_seg(const int32_t* unit0, int n_segs, int unit) {
   int lo = 0, hi = n_segs - 1;
@@ -227,7 +262,7 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
   const int h = blockIdx.y;
   const int seg = find_seg(a.unit0, a.n_segs, unit);
   const int r = unit - a.unit0[seg];
-  const int pos = a.pos0[seg] + r;
+  const int pos = seg_pos0(a, seg) + r;
   const int64_t src_row = (int64_t)a.row0[seg] + r;
   const int d = a.lay.d;
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (pos >> 8)];
@@ -263,10 +298,11 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sat_any = 0;
   const int seg = find_seg(a.unit0, a.n_segs, unit);
-  const int pos0 = a.pos0[seg];
+  const int pos0 = seg_pos0(a, seg);
   const int grp = (pos0 >> 5) + (unit - a.unit0[seg]);  // 32-token sub-tile of the sequence
   const int t0 = max(pos0, grp * 32);
   const int t1 = min(pos0 + a.n[seg], grp * 32 + 32);
+  if (t0 >= t1) return;  // the spare unit of a rolled-back segment (whole workgroup)
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
   uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
   uint32_t sat = 0;

@@ -46,12 +46,14 @@ template <int FMT, int D>
 struct Tr;
 template <int D>
 struct Tr<1, D> {  // bf16: v_mfma_f32_32x32x16_bf16
+  using Elem = uint16_t;
   static constexpr int NSUB = 128 / D > 1 ? 128 / D : 1;
   static constexpr int LK = D / 16;  // k-steps of QK
   static constexpr int LV = D / 16;  // 2 PV k-steps x D/32 output tiles
 };
 template <int D>
 struct Tr<0, D> {  // fp32: v_mfma_f32_32x32x2f32
+  using Elem = float;
   static constexpr int NSUB = 1;
   static constexpr int LK = D / 8;  // groups of 4 QK k-steps
   static constexpr int LV = D / 8;  // 4 groups of 4 PV k-steps x D/32 output tiles
@@ -261,7 +263,7 @@ __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& 
   pv_tile<D>(cs.acc, b, p);
 }
 
-template <int FMT, int D, int NCT, bool CAP>
+template <int FMT, int D, int NCT, bool CAP, bool APPEND>
 __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1) void attn_kernel(AttnArgs a) {
   constexpr int TL = 4 / NCT;  // token lanes
   constexpr int NDT = D / 32;
@@ -283,21 +285,66 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   const int w = blockIdx.x;
   const Chunk ch = chunk_of(a, w);
   const int s = ch.s, h = ch.h, tlo = ch.tlo;
-  const int L = a.len[s], n = a.nrows[s];
+  const int L = ch.L, n = a.nrows[s];
   const int R = n * a.g;
   const bool col_ok = c < R;
   const int row_i = col_ok ? c / a.g : 0;
   const int head_j = col_ok ? c - row_i * a.g : 0;
   const int ppos = L - n + row_i;  // position of this column's query row
 
-  const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
+  // The table is read through the constant address space: scalar loads
+  // even in the fused-append variant, whose pool stores would otherwise make
+  // the compiler turn every table read into a vector load (and a wait on
+  // the tile loads in flight).  Nothing writes the table during a launch.
+  typedef __attribute__((address_space(4))) const int32_t cint32_t;
+  cint32_t* trow = (cint32_t*)(a.table + (int64_t)a.seq[s] * a.max_bps);
   const int64_t head_off = (int64_t)h * 256 * D * E;
+  auto block_of = [&](int key) { return trow[key >> 8]; };
   auto bases = [&](int t, const uint8_t*& kb, const uint8_t*& vb) {
     const int key0 = (tlo + t) * TK;
-    const uint8_t* blk = a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + head_off + (key0 & 255) * D * E;
+    const uint8_t* blk = a.pool + (int64_t)block_of(key0) * a.lay.block_bytes + head_off + (key0 & 255) * D * E;
     kb = blk + a.lay.k_off;
     vb = blk + a.lay.v_off;
   };
+  if constexpr (APPEND) {
+    // Fused append: write the verified rows of kv head h that fall in this
+    // chunk's keys into the pool, then make them visible to the whole
+    // workgroup before any tile load; every row lies in exactly one chunk of
+    // the pair.  One thread per 8 consecutive dimensions of a row (at most
+    // 8 rows x 32 groups = 256 items): one 16-byte load round trip, then
+    // fire-and-forget stores.  Blocks the append pops are in the table
+    // already (the host updates it before this launch).
+    using T = typename Tr<FMT, D>::Elem;
+    constexpr int G = 8;
+    static_assert(8 * (D / G) <= 256, "one item per thread");
+    const int lo = max((tlo + ch.t_begin) * TK, L - n), hi = min((tlo + ch.t_end) * TK, L);
+    if (lo < hi) {
+      const int b_lo = block_of(lo), b_hi = block_of(hi - 1);  // the rows span at most two blocks
+      const int item = threadIdx.x;
+      if (item < (hi - lo) * (D / G)) {
+        const int p = lo + item / (D / G), d0 = (item % (D / G)) * G;
+        const int64_t src = ((int64_t)(a.qrow0[s] + p - (L - n)) * a.lay.hkv + h) * D + d0;
+        T kx[G], vx[G];
+        const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.new_k) + src);
+        const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.new_v) + src);
+#pragma unroll
+        for (int j = 0; j < (int)(G * sizeof(T) / 16); ++j) {
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(kx) + 16 * j) = ks[j];
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(vx) + 16 * j) = vs[j];
+        }
+        uint8_t* blk = const_cast<uint8_t*>(a.pool) + (int64_t)((p >> 8) == (lo >> 8) ? b_lo : b_hi) * a.lay.block_bytes;
+        T* kd = reinterpret_cast<T*>(blk + a.lay.k_off) + (int64_t)h * 256 * D;
+        T* vd = reinterpret_cast<T*>(blk + a.lay.v_off) + (int64_t)h * 256 * D;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          kd[plain_k_index(FMT, D, p & 255, d0 + e)] = kx[e];
+          vd[plain_v_index(FMT, D, p & 255, d0 + e)] = vx[e];
+        }
+      }
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
   const int t_first = ch.t_begin + tl;
   const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
 
@@ -432,18 +479,23 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
 
 // ---- launchers ----------------------------------------------------------------------
 
-template <int FMT, int D>
-static hipError_t launch_attn_fd(const AttnArgs& a, int nct, hipStream_t s) {
+template <int FMT, int D, bool APPEND>
+static hipError_t launch_attn_fda(const AttnArgs& a, int nct, hipStream_t s) {
   const bool cap = a.softcap > 0.0f;
   if (nct == 1 && !cap)
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, false>), dim3(a.n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, false, APPEND>), dim3(a.n_wg), dim3(256), 0, s, a);
   else if (nct == 1)
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, true>), dim3(a.n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 1, true, APPEND>), dim3(a.n_wg), dim3(256), 0, s, a);
   else if (!cap)
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, false>), dim3(a.n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, false, APPEND>), dim3(a.n_wg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, true>), dim3(a.n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<FMT, D, 2, true, APPEND>), dim3(a.n_wg), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int FMT, int D>
+static hipError_t launch_attn_fd(const AttnArgs& a, int nct, hipStream_t s) {
+  return a.new_k ? launch_attn_fda<FMT, D, true>(a, nct, s) : launch_attn_fda<FMT, D, false>(a, nct, s);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int nct, hipStream_t s) {

@@ -112,10 +112,17 @@ __device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB]
   cs.l += lsum;
 }
 
-// Chunk of workgroup w: sequence index s, kv head h, tiles [t_begin, t_end)
-// of the pair, out of nt, split into k chunks.
+// Positions of sequence s the kernels see: the host's count minus any
+// rollback applied on the device and not yet read back by the host.
+__device__ __forceinline__ int seq_len_now(const AttnArgs& a, int s) {
+  return a.roll ? a.len[s] - a.roll[a.seq[s]] : a.len[s];
+}
+
+// Chunk of workgroup w: sequence index s (L positions), kv head h, chunk
+// `part` of k, tiles [t_begin, t_end) of the pair's nt (empty when pending
+// device rollbacks left fewer tiles than the host planned for).
 struct Chunk {
-  int s, h, k, nt, tlo, t_begin, t_end;
+  int s, h, k, part, L, nt, tlo, t_begin, t_end;
 };
 
 __device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
@@ -125,7 +132,9 @@ __device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
   const int local = w - a.wg_base[c.s];
   c.h = local / c.k;
   const int part = local - c.h * c.k;
-  const int L = a.len[c.s], n = a.nrows[c.s];
+  c.part = part;
+  const int L = seq_len_now(a, c.s), n = a.nrows[c.s];
+  c.L = L;
   const int tk = a.tile_keys;
   const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;
   c.tlo = klo / tk;

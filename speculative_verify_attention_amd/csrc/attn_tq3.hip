@@ -336,7 +336,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
   const int w = blockIdx.x;
   const Chunk ch = chunk_of(a, w);
   const int s = ch.s, h = ch.h, tlo = ch.tlo;
-  const int L = a.len[s], n = a.nrows[s];
+  const int L = ch.L, n = a.nrows[s];
   const int R = n * a.g;
   const bool col_ok = c < R;
   const int row_i = col_ok ? c / a.g : 0;

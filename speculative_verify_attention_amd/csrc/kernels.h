@@ -94,6 +94,21 @@ struct TableUpdateArgs {
 };
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s);
 
+// ---- device-side rollback ------------------------------------------------------
+// roll[seq] += clamp(n_draft[i] - accepted[i], 0, n_draft[i]) for each entry:
+// the lengths the kernels use are the host's minus roll[seq] until the host
+// reads roll back and applies it (then roll is cleared).
+constexpr int kMaxRollback = 256;
+struct RollbackArgs {
+  int32_t* roll;            // [max_seqs]
+  const int32_t* accepted;  // device [count], this launch's entries
+  int32_t count;
+  int32_t seq[kMaxRollback];
+  int32_t n_draft[kMaxRollback];
+};
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(int32_t* p, int32_t n, hipStream_t s);
+
 // ---- append (slice-update of new positions into their blocks) ----------------
 constexpr int kMaxAppendSegs = 96;
 struct AppendArgs {
@@ -110,6 +125,9 @@ struct AppendArgs {
   int32_t pos0[kMaxAppendSegs];
   int32_t n[kMaxAppendSegs];
   int32_t row0[kMaxAppendSegs];    // first source row of the segment
+  // pending device rollbacks: a segment starts at pos0 - roll[seq] (null: none);
+  // with them, TQ3 segments carry one spare sub-tile unit for the unknown alignment
+  const int32_t* roll;
   // TQ3 codec (device constants in the pool's metadata region)
   const int8_t* signs;  // [d]
   const float* s_t;     // S transposed: [d][d], s_t[j*d + i] = S[i][j]
@@ -170,6 +188,15 @@ struct AttnArgs {
   int32_t force_partial;  // 1: every pair goes through the merge
   int32_t tile_keys;      // keys per tile (tile_keys(fmt, d))
   uint16_t lev16_bits[8];
+  // pending device rollbacks: sequence s has len[s] - roll[seq[s]] positions
+  // (null: none pending)
+  const int32_t* roll;
+  // fused append (plain formats): the K/V rows of the verified rows, in the
+  // pool's element type, [rows][hkv][d] in query-row order; the workgroups
+  // whose chunk holds a row write it into the pool before reading the chunk.
+  // new_k == null: no append.
+  const void* new_k;
+  const void* new_v;
   int32_t seq[kMaxAttnSeqs];
   int32_t len[kMaxAttnSeqs];
   int32_t qrow0[kMaxAttnSeqs];

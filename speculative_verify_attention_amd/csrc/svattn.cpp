@@ -24,11 +24,19 @@ struct kv_cache {
   size_t pool_bytes = 0;
   int32_t* dtable = nullptr;   // device block table [max_seqs][max_blocks_per_seq]
   uint32_t* dstatus = nullptr; // device status word
+  int32_t* droll = nullptr;    // device rollbacks not yet applied on the host [max_seqs]
   int8_t* dsigns = nullptr;    // TQ3: D
   float* ds_t = nullptr;       // TQ3: S transposed
   std::vector<int8_t> h_signs;
   std::vector<float> h_s_t;
   std::vector<uint32_t> h_zero;
+  // Device rollbacks (kv_rollback_device) not yet read back: the host's
+  // lengths are upper bounds, the device's are len - droll[seq], and
+  // pend[seq] bounds droll[seq] from above.
+  std::vector<int32_t> pend;
+  std::vector<int32_t> h_roll;
+  bool any_pend = false;
+  hipStream_t pend_stream = nullptr;
   hipEvent_t trace_before = nullptr, trace_after = nullptr;
   std::string err;
 };
@@ -53,7 +61,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MetaLayout {
-  size_t blocks_bytes, table_off, status_off, signs_off, st_off, total;
+  size_t blocks_bytes, table_off, status_off, roll_off, signs_off, st_off, total;
 };
 
 MetaLayout meta_layout(const kv_params& p, const PoolLayout& lay) {
@@ -61,15 +69,19 @@ MetaLayout meta_layout(const kv_params& p, const PoolLayout& lay) {
   m.blocks_bytes = (size_t)p.num_blocks * (size_t)lay.block_bytes;
   m.table_off = align_up(m.blocks_bytes);
   m.status_off = align_up(m.table_off + (size_t)p.max_seqs * p.max_blocks_per_seq * 4);
-  m.signs_off = m.status_off + kAlign;
+  m.roll_off = m.status_off + kAlign;
+  m.signs_off = align_up(m.roll_off + (size_t)p.max_seqs * 4);
   m.st_off = m.signs_off;
-  m.total = m.status_off + kAlign;
+  m.total = m.signs_off;
   if (p.format == KV_TQ3) {
     m.st_off = align_up(m.signs_off + (size_t)p.head_dim);
     m.total = align_up(m.st_off + (size_t)p.head_dim * p.head_dim * 4);
   }
   return m;
 }
+
+int sync_pending(kv_cache* c);
+int enqueue_table_updates(kv_cache* c, const AppendPlan& plan, hipStream_t s);
 
 int set_err(kv_cache* c, int code, const std::string& msg) {
   if (c) c->err = msg;
@@ -79,7 +91,7 @@ int set_err(kv_cache* c, int code, const std::string& msg) {
 int check_device(kv_cache* c) {
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess) {
-    hipGetLastError();
+    (void)hipGetLastError();
     return set_err(c, KV_EDEVICE, std::string("HIP error before call: ") + hipGetErrorString(e));
   }
   return KV_OK;
@@ -121,8 +133,20 @@ struct VerifyPlan {
   std::vector<VerifyLaunch> launches;
 };
 
+// Lengths a verify call plans with: the host's length (plus rows a fused
+// append adds first) is an upper bound of what the kernels will see; minus
+// the pending device rollbacks it is a lower bound.  Tiles are planned from
+// the lower bound's window start to the upper bound's end; the kernels cut
+// their chunks to the lengths they read on the device.
+void verify_lengths(const kv_cache* c, int32_t seq, int32_t added, int32_t* up, int32_t* low) {
+  int32_t len;
+  c->core.seq_len(seq, &len);
+  *up = len + added;
+  *low = *up - c->pend[seq];
+}
+
 int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
-                int32_t num_q_heads, int32_t window, VerifyPlan* vp, std::string* err) {
+                int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp, std::string* err) {
   const CoreParams& P = c->core.params();
   auto fail = [&](int code, const std::string& m) {
     if (err) *err = m;
@@ -136,10 +160,12 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
   int max_rows = 0;
   for (int i = 0; i < n_seqs; ++i) {
     if (!c->core.valid_seq(seq_ids[i])) return fail(KV_ENOSEQ, "sequence id " + std::to_string(seq_ids[i]) + " out of range");
-    int32_t len;
-    c->core.seq_len(seq_ids[i], &len);
+    int32_t up, low;
+    verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
     if (n_rows[i] < 1 || n_rows[i] > KV_MAX_ROWS) return fail(KV_EINVAL, "n_rows must be in [1, 8]");
-    if (n_rows[i] > len) return fail(KV_ERANGE, "n_rows exceeds seq_len of sequence " + std::to_string(seq_ids[i]));
+    if (n_rows[i] > low)
+      return fail(KV_ERANGE, "n_rows exceeds seq_len of sequence " + std::to_string(seq_ids[i]) +
+                                 (up > low ? " (device rollbacks pending: the lower bound counts)" : ""));
     max_rows = std::max(max_rows, (int)n_rows[i]);
     vp->rows += n_rows[i];
   }
@@ -155,10 +181,10 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
   std::vector<int> nt(n_seqs);
   int64_t total_tiles = 0;
   for (int i = 0; i < n_seqs; ++i) {
-    int32_t len;
-    c->core.seq_len(seq_ids[i], &len);
-    const int klo = window > 0 ? std::max(0, len - n_rows[i] - window + 1) : 0;
-    nt[i] = (len + tk - 1) / tk - klo / tk;
+    int32_t up, low;
+    verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
+    const int klo = window > 0 ? std::max(0, low - n_rows[i] - window + 1) : 0;
+    nt[i] = (up + tk - 1) / tk - klo / tk;
     total_tiles += (int64_t)nt[i] * P.num_kv_heads;
   }
   // Uniform batches: one round of workgroups (one per CU).  Ragged batches
@@ -251,9 +277,14 @@ int kv_create(const kv_params* p, void* stream, kv_cache** out) {
   c->pool_bytes = p->pool_bytes;
   c->dtable = reinterpret_cast<int32_t*>(c->pool + m.table_off);
   c->dstatus = reinterpret_cast<uint32_t*>(c->pool + m.status_off);
+  c->droll = reinterpret_cast<int32_t*>(c->pool + m.roll_off);
+  c->pend.assign(p->max_seqs, 0);
+  c->h_roll.assign(p->max_seqs, 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  c->h_zero.assign(kAlign / 4, 0u);
+  c->h_zero.assign(std::max<size_t>(kAlign / 4, (size_t)p->max_seqs), 0u);
   hipError_t e = hipMemcpyAsync(c->dstatus, c->h_zero.data(), kAlign, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->droll, c->h_zero.data(), (size_t)p->max_seqs * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && p->format == KV_TQ3) {
     const Codec& cd = c->core.codec();
     const int d = p->head_dim;
@@ -293,17 +324,8 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
   if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   // 1. new blocks become visible in the device table
-  for (size_t i = 0; i < plan.popped.size(); i += kMaxTableUpdates) {
-    TableUpdateArgs ta;
-    ta.table = c->dtable;
-    ta.count = (int32_t)std::min<size_t>(kMaxTableUpdates, plan.popped.size() - i);
-    for (int j = 0; j < ta.count; ++j) {
-      ta.index[j] = plan.table_index[i + j];
-      ta.block[j] = plan.popped[i + j];
-    }
-    hipError_t e = launch_table_update(ta, s);
-    if (e != hipSuccess) return hip_fail(c, e, "table update launch");
-  }
+  rc = enqueue_table_updates(c, plan, s);
+  if (rc != KV_OK) return rc;
   // 2. slice-update / quantize-on-append, in launches of <= kMaxAppendSegs segments
   const CoreParams& P = c->core.params();
   std::vector<const AppendSeg*> segs;
@@ -323,7 +345,12 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
     int64_t units = 0;
     while (i < segs.size() && a.n_segs < kMaxAppendSegs) {
       const AppendSeg& g = *segs[i];
-      const int64_t u = tq3 ? (int64_t)((g.pos0 + g.n - 1) / 32 - g.pos0 / 32 + 1) : g.n;
+      // TQ3 units are 32-token sub-tiles; with a device rollback pending the
+      // start's alignment is unknown here, so the span's worst case is taken
+      // (the kernel skips a unit left empty)
+      const int64_t u = !tq3 ? g.n
+                        : c->pend[g.seq] > 0 ? (int64_t)((g.n + 30) / 32 + 1)
+                                             : (int64_t)((g.pos0 + g.n - 1) / 32 - g.pos0 / 32 + 1);
       if (units + u > (int64_t)INT32_MAX / 2 && a.n_segs > 0) break;
       a.unit0[a.n_segs] = (int32_t)units;
       a.seq[a.n_segs] = g.seq;
@@ -336,6 +363,7 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
     }
     a.unit0[a.n_segs] = (int32_t)units;
     a.total_units = (int32_t)units;
+    a.roll = c->any_pend ? c->droll : nullptr;
     if (tq3) {
       const Codec& cd = c->core.codec();
       a.signs = c->dsigns;
@@ -353,12 +381,16 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
 
 int kv_rollback(kv_cache* c, int32_t seq_id, int32_t n_tokens) {
   if (!c) return KV_EINVAL;
+  int rc = sync_pending(c);
+  if (rc != KV_OK) return rc;
   return c->core.rollback(seq_id, n_tokens, &c->err);
 }
 
 int kv_rollback_batch(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens) {
   if (!c) return KV_EINVAL;
   if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_tokens))) return set_err(c, KV_EINVAL, "bad arrays");
+  int rc = sync_pending(c);
+  if (rc != KV_OK) return rc;
   std::vector<char> seen(c->core.params().max_seqs, 0);
   for (int i = 0; i < n_seqs; ++i) {
     const int32_t s = seq_ids[i];
@@ -384,6 +416,8 @@ int kv_trace_events(kv_cache* c, void* before, void* after) {
 
 int kv_seq_free(kv_cache* c, int32_t seq_id) {
   if (!c) return KV_EINVAL;
+  int rc = sync_pending(c);
+  if (rc != KV_OK) return rc;
   return c->core.free_seq(seq_id, &c->err);
 }
 
@@ -414,25 +448,33 @@ int kv_encode(const kv_cache* cc, int64_t n_vecs, const float* src, int32_t is_k
   return KV_OK;
 }
 
-int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
-                       int32_t num_q_heads, int32_t window, size_t* out) {
-  if (!c || !out) return KV_EINVAL;
-  VerifyPlan vp;
-  int rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp, &const_cast<kv_cache*>(c)->err);
-  if (rc != KV_OK) return rc;
-  *out = vp.total;
+}  // extern "C"
+
+namespace {
+
+// Read the device rollbacks back and apply them to the host state; blocks
+// until the stream of the last kv_rollback_device call gets here.
+int sync_pending(kv_cache* c) {
+  if (!c->any_pend) return KV_OK;
+  const int32_t ms = c->core.params().max_seqs;
+  hipError_t e = hipMemcpyAsync(c->h_roll.data(), c->droll, (size_t)ms * 4, hipMemcpyDeviceToHost, c->pend_stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->pend_stream);
+  if (e != hipSuccess) return hip_fail(c, e, "reading device rollbacks");
+  for (int s = 0; s < ms; ++s)
+    if (c->h_roll[s] < 0 || c->h_roll[s] > c->pend[s]) return set_err(c, KV_EDEVICE, "device rollback count out of range");
+  for (int s = 0; s < ms; ++s)
+    if (c->h_roll[s] > 0) c->core.rollback(s, c->h_roll[s], &c->err);
+  e = launch_fill_zero(c->droll, ms, c->pend_stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->pend_stream);
+  if (e != hipSuccess) return hip_fail(c, e, "clearing device rollbacks");
+  std::fill(c->pend.begin(), c->pend.end(), 0);
+  c->any_pend = false;
   return KV_OK;
 }
 
-int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const float* q,
-                     int32_t num_q_heads, float scale, float softcap, int32_t window, float* out, void* workspace,
-                     size_t ws_bytes, void* stream) {
-  if (!c) return KV_EINVAL;
-  int rc = check_device(c);
-  if (rc != KV_OK) return rc;
-  VerifyPlan vp;
-  rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp, &c->err);
-  if (rc != KV_OK) return rc;
+// Checks of a verify call beyond its plan.
+int check_verify_args(kv_cache* c, const VerifyPlan& vp, const float* q, float scale, float softcap, float* out,
+                      void* workspace, size_t ws_bytes) {
   if (!q || !out) return set_err(c, KV_EINVAL, "null q / out");
   if (!std::isfinite(scale)) return set_err(c, KV_EINVAL, "scale must be finite");
   if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return set_err(c, KV_EINVAL, "softcap must be finite and >= 0");
@@ -440,9 +482,34 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   if (vp.total > 0 && (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return set_err(c, KV_EINVAL, "workspace must be non-null and 256-byte aligned");
   const CoreParams& P = c->core.params();
+  if (P.format == KV_TQ3 && P.head_dim > 128) return set_err(c, KV_EINVAL, "KV_TQ3 attention supports head_dim 64 and 128");
+  return KV_OK;
+}
+
+// Enqueue table updates for the blocks an append plan pops.
+int enqueue_table_updates(kv_cache* c, const AppendPlan& plan, hipStream_t s) {
+  for (size_t i = 0; i < plan.popped.size(); i += kMaxTableUpdates) {
+    TableUpdateArgs ta;
+    ta.table = c->dtable;
+    ta.count = (int32_t)std::min<size_t>(kMaxTableUpdates, plan.popped.size() - i);
+    for (int j = 0; j < ta.count; ++j) {
+      ta.index[j] = plan.table_index[i + j];
+      ta.block[j] = plan.popped[i + j];
+    }
+    hipError_t e = launch_table_update(ta, s);
+    if (e != hipSuccess) return hip_fail(c, e, "table update launch");
+  }
+  return KV_OK;
+}
+
+// Enqueue a planned verify call.  added / new_k / new_v: a fused append of
+// the verified rows (plain formats; the table already holds their blocks),
+// else null.
+int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                   const int32_t* added, const float* q, int32_t num_q_heads, float scale, float softcap,
+                   int32_t window, float* out, void* workspace, hipStream_t s, const void* new_k, const void* new_v) {
+  const CoreParams& P = c->core.params();
   const bool tq3 = P.format == KV_TQ3;
-  if (tq3 && P.head_dim > 128) return set_err(c, KV_EINVAL, "KV_TQ3 attention supports head_dim 64 and 128");
-  hipStream_t s = static_cast<hipStream_t>(stream);
   // TQ3: the rotated queries q' = Pi q and q'' = S q' live after the partials
   float* q1 = nullptr;
   float* q2 = nullptr;
@@ -454,10 +521,10 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     // one-part products average out over the keys)
     int min_keys = INT32_MAX;
     for (int i = 0; i < n_seqs; ++i) {
-      int32_t len;
-      c->core.seq_len(seq_ids[i], &len);
-      const int lo = window > 0 ? std::max(0, len - n_rows[i] - window + 1) : 0;
-      min_keys = std::min(min_keys, len - n_rows[i] + 1 - lo);
+      int32_t up, low;
+      verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
+      const int lo = window > 0 ? std::max(0, low - n_rows[i] - window + 1) : 0;
+      min_keys = std::min(min_keys, low - n_rows[i] + 1 - lo);
     }
     precise = min_keys < SVATTN_TQ3_FAST_KEYS;
     QPrepArgs qa;
@@ -506,14 +573,17 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     a.rpad = vp.rpad;
     a.force_partial = tq3 ? 1 : 0;  // the merge rotates TQ3 outputs back
     a.tile_keys = tile_keys(P.format, P.head_dim);
+    a.roll = c->any_pend ? c->droll : nullptr;
+    a.new_k = new_k;
+    a.new_v = new_v;
     bool any_split = tq3;
     for (int i = 0; i < L.count; ++i) {
       const int ci = vp.order[L.first + i];
       const int sid = seq_ids[ci];
-      int32_t len;
-      c->core.seq_len(sid, &len);
+      int32_t up, low;
+      verify_lengths(c, sid, added ? added[ci] : 0, &up, &low);
       a.seq[i] = sid;
-      a.len[i] = len;
+      a.len[i] = up;
       a.qrow0[i] = vp.qrow0[ci];
       a.nrows[i] = n_rows[ci];
       a.ksplit[i] = L.ksplit[i];
@@ -536,15 +606,145 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   return KV_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                       int32_t num_q_heads, int32_t window, size_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  VerifyPlan vp;
+  int rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, nullptr, &vp,
+                       &const_cast<kv_cache*>(c)->err);
+  if (rc != KV_OK) return rc;
+  *out = vp.total;
+  return KV_OK;
+}
+
+int kv_append_verify_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids,
+                                     const int32_t* n_rows, int32_t num_q_heads, int32_t window, size_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  VerifyPlan vp;
+  int rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, n_rows, &vp,
+                       &const_cast<kv_cache*>(c)->err);
+  if (rc != KV_OK) return rc;
+  *out = vp.total;
+  return KV_OK;
+}
+
+int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const float* q,
+                     int32_t num_q_heads, float scale, float softcap, int32_t window, float* out, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  VerifyPlan vp;
+  rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, nullptr, &vp, &c->err);
+  if (rc != KV_OK) return rc;
+  rc = check_verify_args(c, vp, q, scale, softcap, out, workspace, ws_bytes);
+  if (rc != KV_OK) return rc;
+  return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out,
+                        workspace, static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const void* k,
+                     const void* v, const float* q, int32_t num_q_heads, float scale, float softcap, int32_t window,
+                     float* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  AppendPlan plan;
+  rc = c->core.plan_append(n_seqs, seq_ids, n_rows, &plan, &c->err);
+  if (rc != KV_OK) return rc;
+  VerifyPlan vp;
+  rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, n_rows, &vp, &c->err);
+  if (rc != KV_OK) return rc;
+  rc = check_verify_args(c, vp, q, scale, softcap, out, workspace, ws_bytes);
+  if (rc != KV_OK) return rc;
+  if (!k || !v) return set_err(c, KV_EINVAL, "null k / v");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CoreParams& P = c->core.params();
+  // Plain formats: the attention kernel writes the rows (no launch of its
+  // own; a table update goes first when blocks are popped, about once per
+  // 256 / rows steps of a sequence).  TQ3 encodes in its own launch.
+  const bool fused = P.format != KV_TQ3 && reinterpret_cast<uintptr_t>(k) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(v) % 16 == 0;  // the kernel reads rows in 16-byte pieces
+  if (!fused) {
+    rc = kv_append(c, n_seqs, seq_ids, n_rows, k, v, stream);
+    if (rc != KV_OK) return rc;
+    return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out,
+                          workspace, s, nullptr, nullptr);
+  }
+  rc = enqueue_table_updates(c, plan, s);
+  if (rc != KV_OK) return rc;
+  rc = enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, n_rows, q, num_q_heads, scale, softcap, window, out, workspace,
+                      s, k, v);
+  if (rc != KV_OK) return rc;
+  c->core.commit_append(plan);
+  return KV_OK;
+}
+
+int kv_rollback_device(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_draft,
+                       const int32_t* accepted, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_draft || !accepted)))
+    return set_err(c, KV_EINVAL, "bad arrays");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->any_pend && s != c->pend_stream)
+    return set_err(c, KV_EINVAL, "pending device rollbacks were enqueued on another stream; call kv_sync first");
+  std::vector<char> seen(c->core.params().max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int32_t sid = seq_ids[i];
+    if (!c->core.valid_seq(sid)) return set_err(c, KV_ENOSEQ, "sequence id out of range");
+    if (seen[sid]) return set_err(c, KV_EINVAL, "sequence id repeated");
+    seen[sid] = 1;
+    if (n_draft[i] < 0) return set_err(c, KV_EINVAL, "n_draft < 0");
+    int32_t up, low;
+    verify_lengths(c, sid, 0, &up, &low);
+    if (n_draft[i] > low) return set_err(c, KV_ERANGE, "n_draft exceeds the sequence's length");
+  }
+  for (int first = 0; first < n_seqs; first += kMaxRollback) {
+    RollbackArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.roll = c->droll;
+    a.accepted = accepted + first;
+    a.count = std::min(kMaxRollback, n_seqs - first);
+    for (int i = 0; i < a.count; ++i) {
+      a.seq[i] = seq_ids[first + i];
+      a.n_draft[i] = n_draft[first + i];
+    }
+    hipError_t e = launch_rollback(a, s);
+    if (e != hipSuccess) return hip_fail(c, e, "rollback launch");
+  }
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_draft[i] == 0) continue;
+    c->pend[seq_ids[i]] += n_draft[i];
+    c->any_pend = true;
+    c->pend_stream = s;
+  }
+  return KV_OK;
+}
+
+int kv_sync(kv_cache* c) {
+  if (!c) return KV_EINVAL;
+  return sync_pending(c);
+}
+
 int kv_seq_len(const kv_cache* c, int32_t seq_id, int32_t* out) {
   if (!c || !out) return KV_EINVAL;
+  int rc = sync_pending(const_cast<kv_cache*>(c));
+  if (rc != KV_OK) return rc;
   return c->core.seq_len(seq_id, out);
 }
 
 int kv_block_table(const kv_cache* c, int32_t seq_id, int32_t* out, int32_t cap, int32_t* n_owned) {
   if (!c || !n_owned || cap < 0 || (cap > 0 && !out)) return KV_EINVAL;
+  int rc = sync_pending(const_cast<kv_cache*>(c));
+  if (rc != KV_OK) return rc;
   int32_t owned;
-  int rc = c->core.owned(seq_id, &owned);
+  rc = c->core.owned(seq_id, &owned);
   if (rc != KV_OK) return rc;
   const int32_t* row = c->core.table_row(seq_id);
   for (int i = 0; i < std::min(cap, owned); ++i) out[i] = row[i];
