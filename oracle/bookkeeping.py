@@ -25,6 +25,19 @@ Readings where the pages are silent:
 * freeing a sequence pushes its blocks back onto the front of the free list in
   reverse ownership order, so its first block is the next one handed out.
 
+Ring caches for sliding-window layers (the same blog's 512-token local
+layers; the window bounds what a layer can ever read again).  With window W
+a sequence keeps only the blocks holding its last W + H positions, H = 8
+(the most rows one verify call appends, so the rows just appended can still
+be verified and rolled back):
+* after an append to length L, blocks wholly below position
+  max(0, L - H - W + 1) are released (table entry -1) and pushed onto the
+  front of the free list in increasing index order, before the entry's new
+  blocks are popped; positions in released blocks are never stored again;
+* a rollback to length L' must keep every position a later window can see:
+  max(0, L' - W + 1) >= the first kept position, else ERANGE;
+* freeing a sequence returns only its kept blocks (same order rule).
+
 The logical store keeps, per sequence, one payload per position (whatever the
 caller appended: K/V rows or encoded records), without any paging, so paging
 mistakes on the other side show up as mismatches.
@@ -41,15 +54,18 @@ ERANGE = -3
 ENOSEQ = -4
 
 BLOCK = 256
+HISTORY = 8  # positions kept beyond the window in a ring cache
 
 
 class KVModel:
-    def __init__(self, num_blocks, max_seqs, max_blocks_per_seq, alloc_seed=0):
+    def __init__(self, num_blocks, max_seqs, max_blocks_per_seq, alloc_seed=0, ring_window=0):
         self.num_blocks = num_blocks
         self.max_seqs = max_seqs
         self.max_blocks_per_seq = max_blocks_per_seq
+        self.ring_window = ring_window
         self.free = free_list_order(num_blocks, alloc_seed)
-        self.table = [[] for _ in range(max_seqs)]
+        self.table = [[] for _ in range(max_seqs)]  # -1: released (ring caches)
+        self.first = [0] * max_seqs  # index of the first kept block
         self.seq_len = [0] * max_seqs
         self.store = [[] for _ in range(max_seqs)]
 
@@ -58,8 +74,15 @@ class KVModel:
         return math.ceil(length / BLOCK)
 
     def live_table(self, s):
-        """Blocks that hold positions below seq_len (the part reads can reach)."""
+        """Table entries of the blocks below seq_len (-1 where a ring cache
+        released the block)."""
         return list(self.table[s][: self.blocks_needed(self.seq_len[s])])
+
+    def kept_blocks(self, s):
+        return [b for b in self.table[s][self.first[s]:] if b >= 0]
+
+    def first_position(self, s):
+        return self.first[s] * BLOCK
 
     def slot_of(self, s, p):
         """Physical (block, slot) of logical position p of sequence s."""
@@ -69,12 +92,17 @@ class KVModel:
         """Logical payloads at positions 0..seq_len-1."""
         return list(self.store[s][: self.seq_len[s]])
 
+    def _keep_from(self, s, length):
+        """First block a ring cache must keep at this length."""
+        if not self.ring_window:
+            return self.first[s]
+        return max(self.first[s], max(0, length - HISTORY - self.ring_window + 1) // BLOCK)
+
     # -- mutations -------------------------------------------------------
     def append(self, seqs, payloads):
         """Append payloads[i] (a list, one entry per new token) to seqs[i]."""
         if len(seqs) != len(payloads):
             return EINVAL
-        need = []
         seen = set()
         for s, items in zip(seqs, payloads):  # entries checked in call order
             if not (0 <= s < self.max_seqs):
@@ -82,15 +110,33 @@ class KVModel:
             if s in seen:
                 return EINVAL
             seen.add(s)
-            total = self.blocks_needed(self.seq_len[s] + len(items))
-            if total > self.max_blocks_per_seq:
+            if self.blocks_needed(self.seq_len[s] + len(items)) > self.max_blocks_per_seq:
                 return ERANGE
-            need.append(max(0, total - len(self.table[s])))
-        if sum(need) > len(self.free):
-            return ENOMEM
-        for s, items, k in zip(seqs, payloads, need):
-            for _ in range(k):
-                self.table[s].append(self.free.pop(0))
+        # all or nothing: walk the entries on a copy of the free list first
+        free = list(self.free)
+        for s, items in zip(seqs, payloads):
+            new_len = self.seq_len[s] + len(items)
+            keep = self._keep_from(s, new_len)
+            for i in range(self.first[s], min(keep, len(self.table[s]))):
+                if self.table[s][i] >= 0:
+                    free.insert(0, self.table[s][i])
+            need = self.blocks_needed(new_len) - max(len(self.table[s]), keep)
+            if need > len(free):
+                return ENOMEM
+            del free[: max(0, need)]
+        for s, items in zip(seqs, payloads):
+            new_len = self.seq_len[s] + len(items)
+            keep = self._keep_from(s, new_len)
+            row = self.table[s]
+            for i in range(self.first[s], min(keep, len(row))):
+                if row[i] >= 0:
+                    self.free.insert(0, row[i])
+                    row[i] = -1
+            while len(row) < keep:
+                row.append(-1)  # never held a block
+            while len(row) < self.blocks_needed(new_len):
+                row.append(self.free.pop(0))
+            self.first[s] = keep
             base = self.seq_len[s]
             for i, item in enumerate(items):
                 p = base + i
@@ -98,7 +144,7 @@ class KVModel:
                     self.store[s][p] = item
                 else:
                     self.store[s].append(item)
-            self.seq_len[s] = base + len(items)
+            self.seq_len[s] = new_len
         return OK
 
     def rollback(self, s, r):
@@ -108,15 +154,18 @@ class KVModel:
             return EINVAL
         if r > self.seq_len[s]:
             return ERANGE
+        if self.ring_window and max(0, self.seq_len[s] - r - self.ring_window + 1) < self.first_position(s):
+            return ERANGE  # a later window would reach a released block
         self.seq_len[s] -= r
         return OK
 
     def free_seq(self, s):
         if not (0 <= s < self.max_seqs):
             return ENOSEQ
-        for b in reversed(self.table[s]):
+        for b in reversed(self.kept_blocks(s)):
             self.free.insert(0, b)
         self.table[s] = []
+        self.first[s] = 0
         self.seq_len[s] = 0
         self.store[s] = []
         return OK
