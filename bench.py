@@ -151,7 +151,7 @@ def describe(name, wl, layers):
     kv = {0: "fp32", 1: "bf16", 2: "tq3 (3-bit Lloyd-Max + QJL keys, 3-bit values)"}[wl.fmt]
     lens = sorted(set(wl.prefill))
     ctx = f"{lens[0]}" if len(lens) == 1 else f"{min(lens)}..{max(lens)} (log-uniform)"
-    lay = ", ".join(f"window={w or 'full'} cap={c or 'off'}" for w, c in layers)
+    lay = ", ".join(f"window={w or 'full'}{' (ring cache)' if w else ''} cap={c or 'off'}" for w, c in layers)
     return (f"{name}: {wl.n_seqs} seqs, context {ctx} + drafts, Hq={wl.hq} Hkv={wl.hkv} d={wl.d}, {kv} KV in "
             f"256-token blocks, rows {'1..5 per seq' if wl.vary_rows else wl.rows[0]}, layers [{lay}]")
 
@@ -268,7 +268,7 @@ def run(args, name):
     reps = max(1, math.ceil((1 << 30) / max(1, per_layer * len(layers))))
     runners = []
     for _ in range(reps):
-        r = Runner(wl, layers=layers, device=dev)
+        r = Runner(wl, layers=layers, device=dev, ring=True)  # window layers keep their last W + 8 positions
         r.fill()
         runners.append(r)
     # the steps' plans and inputs, generated before timing

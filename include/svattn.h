@@ -76,7 +76,7 @@ typedef struct {
   int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1 */
   int32_t max_blocks_per_seq; /* table width: positions < 256 * this */
   int32_t format;             /* KV_FP32, KV_BF16 or KV_TQ3 */
-  int32_t reserved;           /* must be 0 */
+  int32_t ring_window;        /* 0: plain cache; W > 0: ring cache for window layers (below) */
   uint64_t alloc_seed;        /* free-list order: 0 = identity, else a SplitMix64 Fisher-Yates shuffle */
   uint64_t codec_seed;        /* KV_TQ3 only: seeds the rotation signs and the QJL matrix */
   void* pool;                 /* device memory owned by the caller, 256-byte aligned */
@@ -116,6 +116,27 @@ typedef struct {
  *      norm g16, V norm n16; half h, index i <-> token 8(i>>2) + 4h + (i&3).
  */
 int kv_pool_bytes(const kv_params* p, size_t* out);
+
+/*
+ * Ring caches (ring_window = W > 0) serve sliding-window layers (mlx-engine
+ * blog, model-architecture section: 512-token local layers), whose rows
+ * never look further back than W - 1 positions: a sequence keeps only the
+ * blocks that hold its last W + KV_MAX_ROWS positions, so its memory stays
+ * at ceil((W + KV_MAX_ROWS + 255) / 256) blocks whatever its length, and
+ * the rows one verify call appends can still be verified and rolled back.
+ *  - After an append to length L, blocks wholly below position
+ *    max(0, L - KV_MAX_ROWS - W + 1) are released (their table entries read
+ *    -1) and pushed onto the front of the free list in increasing index
+ *    order before the call's new blocks are popped, so they are reused
+ *    first.  Appended positions below that point are not stored.  With
+ *    device rollbacks pending, L is the lower bound of the length.
+ *  - A rollback (host or device) that would leave a later window reaching a
+ *    released position fails with KV_ERANGE: to length L' is allowed while
+ *    max(0, L' - W + 1) is at or above the first kept position.
+ *  - Verify calls must pass 1 <= window <= W.
+ *  - max_blocks_per_seq still bounds the length (the table is indexed by
+ *    position / 256); num_blocks bounds the memory.
+ */
 
 /*
  * Create a handle over a caller-owned pool.  Every sequence starts empty.
@@ -346,7 +367,8 @@ int kv_trace_events(kv_cache* c, void* before, void* after);
 int kv_seq_len(const kv_cache* c, int32_t seq_id, int32_t* out);
 
 /* Copy up to cap entries of a sequence's block table to out (host) and the
- * number of blocks it owns to *n_owned.  Errors: KV_ENOSEQ, KV_EINVAL. */
+ * number of table entries in use to *n_owned (ring caches: released entries
+ * read -1).  Errors: KV_ENOSEQ, KV_EINVAL. */
 int kv_block_table(const kv_cache* c, int32_t seq_id, int32_t* out, int32_t cap, int32_t* n_owned);
 
 /* Number of blocks on the free list. */

@@ -28,7 +28,8 @@ extern "C" {
 typedef struct svcore svcore; /* opaque */
 
 typedef struct {
-  int32_t num_kv_heads, head_dim, block_size, num_blocks, max_seqs, max_blocks_per_seq, format, reserved;
+  int32_t num_kv_heads, head_dim, block_size, num_blocks, max_seqs, max_blocks_per_seq, format;
+  int32_t ring_window; /* as kv_params.ring_window */
   uint64_t alloc_seed, codec_seed;
 } svcore_params;
 
@@ -42,7 +43,8 @@ int svcore_rollback(svcore* c, int32_t seq, int32_t n);
 /* kv_seq_free. */
 int svcore_seq_free(svcore* c, int32_t seq);
 int svcore_seq_len(const svcore* c, int32_t seq, int32_t* out);
-/* Copy up to cap table entries; *n_owned = blocks owned by the sequence. */
+/* Copy up to cap table entries; *n_owned = table entries in use (ring
+ * caches: entries of released blocks read -1). */
 int svcore_block_table(const svcore* c, int32_t seq, int32_t* out, int32_t cap, int32_t* n_owned);
 int svcore_free_blocks(const svcore* c, int32_t* out);
 /* Codec constants of a KV_TQ3 core (see kv_codec in svattn.h). */

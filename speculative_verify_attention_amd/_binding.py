@@ -37,7 +37,7 @@ class kv_params(ctypes.Structure):
         ("max_seqs", _i32),
         ("max_blocks_per_seq", _i32),
         ("format", _i32),
-        ("reserved", _i32),
+        ("ring_window", _i32),
         ("alloc_seed", ctypes.c_uint64),
         ("codec_seed", ctypes.c_uint64),
         ("pool", _p),
@@ -54,7 +54,7 @@ class svcore_params(ctypes.Structure):
         ("max_seqs", _i32),
         ("max_blocks_per_seq", _i32),
         ("format", _i32),
-        ("reserved", _i32),
+        ("ring_window", _i32),
         ("alloc_seed", ctypes.c_uint64),
         ("codec_seed", ctypes.c_uint64),
     ]
@@ -354,12 +354,13 @@ class KVCache:
     """One layer's cache: a handle plus the torch tensor owning its pool."""
 
     def __init__(self, num_kv_heads, head_dim, num_blocks, max_seqs, max_blocks_per_seq, fmt, alloc_seed=0,
-                 codec_seed=0, device="cuda", stream=None):
+                 codec_seed=0, device="cuda", stream=None, ring_window=0):
         import torch
 
         self.num_kv_heads, self.head_dim, self.fmt = num_kv_heads, head_dim, fmt
+        self.ring_window = ring_window
         self.params = kv_params(num_kv_heads, head_dim, KV_BLOCK_SIZE, num_blocks, max_seqs, max_blocks_per_seq,
-                                fmt, 0, alloc_seed, codec_seed, None, 0)
+                                fmt, ring_window, alloc_seed, codec_seed, None, 0)
         nbytes = kv_pool_bytes(self.params)
         self.pool = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.params.pool = self.pool.data_ptr()

@@ -263,6 +263,7 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
   const int seg = find_seg(a.unit0, a.n_segs, unit);
   const int r = unit - a.unit0[seg];
   const int pos = seg_pos0(a, seg) + r;
+  if (pos < a.keep[seg]) return;  // a ring cache no longer holds this position
   const int64_t src_row = (int64_t)a.row0[seg] + r;
   const int d = a.lay.d;
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (pos >> 8)];
@@ -300,9 +301,9 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   const int seg = find_seg(a.unit0, a.n_segs, unit);
   const int pos0 = seg_pos0(a, seg);
   const int grp = (pos0 >> 5) + (unit - a.unit0[seg]);  // 32-token sub-tile of the sequence
-  const int t0 = max(pos0, grp * 32);
+  const int t0 = max(max(pos0, grp * 32), a.keep[seg]);  // ring caches store nothing below keep
   const int t1 = min(pos0 + a.n[seg], grp * 32 + 32);
-  if (t0 >= t1) return;  // the spare unit of a rolled-back segment (whole workgroup)
+  if (t0 >= t1) return;  // a spare unit, or one a ring cache drops (whole workgroup)
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
   uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
   uint32_t sat = 0;

@@ -125,6 +125,7 @@ struct AppendArgs {
   int32_t pos0[kMaxAppendSegs];
   int32_t n[kMaxAppendSegs];
   int32_t row0[kMaxAppendSegs];    // first source row of the segment
+  int32_t keep[kMaxAppendSegs];    // positions below this are not stored (ring caches)
   // pending device rollbacks: a segment starts at pos0 - roll[seq] (null: none);
   // with them, TQ3 segments carry one spare sub-tile unit for the unknown alignment
   const int32_t* roll;

@@ -116,6 +116,7 @@ int Core::init(const CoreParams& p, std::string* err) {
   if (p.max_blocks_per_seq < 1) return bad("max_blocks_per_seq must be >= 1");
   if ((int64_t)p.max_blocks_per_seq * kBlock > (int64_t)INT32_MAX) return bad("max_blocks_per_seq too large");
   if (p.format != FMT_FP32 && p.format != FMT_BF16 && p.format != FMT_TQ3) return bad("unknown format");
+  if (p.ring_window < 0) return bad("ring_window must be >= 0");
   p_ = p;
   // Free list order: identity for seed 0, else Fisher-Yates with SplitMix64.
   std::vector<int32_t> order(p.num_blocks);
@@ -130,13 +131,14 @@ int Core::init(const CoreParams& p, std::string* err) {
   free_.assign(order.rbegin(), order.rend());  // back() = order[0]
   table_.assign((size_t)p.max_seqs * p.max_blocks_per_seq, -1);
   owned_.assign(p.max_seqs, 0);
+  first_.assign(p.max_seqs, 0);
   len_.assign(p.max_seqs, 0);
   if (p.format == FMT_TQ3) make_codec(p.head_dim, p.codec_seed, &codec_);
   return OK;
 }
 
-int Core::plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
-                      AppendPlan* plan, std::string* err) const {
+int Core::plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, AppendPlan* plan,
+                      std::string* err, const int32_t* slack) const {
   auto fail = [&](int code, const std::string& m) {
     if (err) *err = m;
     return code;
@@ -146,10 +148,11 @@ int Core::plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_n
   plan->segs.clear();
   plan->popped.clear();
   plan->table_index.clear();
+  plan->released.clear();
+  plan->released_index.clear();
   plan->total_rows = 0;
   std::vector<char> seen(p_.max_seqs, 0);
-  int64_t need_total = 0;
-  for (int i = 0; i < n_seqs; ++i) {
+  for (int i = 0; i < n_seqs; ++i) {  // entries checked in call order
     int32_t s = seq_ids[i];
     if (!valid_seq(s)) return fail(ENOSEQ_, "sequence id " + std::to_string(s) + " out of range");
     if (seen[s]) return fail(EINVAL_, "sequence id " + std::to_string(s) + " repeated");
@@ -159,33 +162,64 @@ int Core::plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_n
     int64_t blocks = (len + kBlock - 1) / kBlock;
     if (blocks > p_.max_blocks_per_seq)
       return fail(ERANGE_, "sequence " + std::to_string(s) + " would exceed max_blocks_per_seq");
-    int64_t need = blocks > owned_[s] ? blocks - owned_[s] : 0;
-    need_total += need;
-    plan->segs.push_back(AppendSeg{s, len_[s], n_new[i], (int32_t)plan->total_rows, (int32_t)need});
-    plan->total_rows += n_new[i];
   }
-  if (need_total > (int64_t)free_.size())
-    return fail(ENOMEM_, "pool exhausted: need " + std::to_string(need_total) + " blocks, " +
-                             std::to_string(free_.size()) + " free");
+  // Walk the entries on a virtual free list: a ring cache's released blocks
+  // go to its front (the vector's back) before the entry's pops.
+  std::vector<int32_t> pushed;
   size_t k = free_.size();
-  for (const AppendSeg& g : plan->segs) {
-    for (int b = 0; b < g.new_blocks; ++b) {
-      plan->popped.push_back(free_[--k]);
-      plan->table_index.push_back(g.seq * p_.max_blocks_per_seq + owned_[g.seq] + b);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    const int64_t len = (int64_t)len_[s] + n_new[i];
+    const int32_t blocks = (int32_t)((len + kBlock - 1) / kBlock);
+    int32_t keep = first_[s];
+    if (p_.ring_window > 0) {
+      const int64_t low = len - (slack ? slack[i] : 0);
+      keep = std::max<int32_t>(keep, (int32_t)(std::max<int64_t>(0, low - kRingHistory - p_.ring_window + 1) / kBlock));
     }
+    AppendSeg g{s, len_[s], n_new[i], (int32_t)plan->total_rows, 0, 0, keep};
+    for (int32_t b = first_[s]; b < std::min(keep, owned_[s]); ++b) {
+      const int32_t blk = table_[(size_t)s * p_.max_blocks_per_seq + b];
+      pushed.push_back(blk);
+      plan->released.push_back(blk);
+      plan->released_index.push_back(s * p_.max_blocks_per_seq + b);
+      ++g.released;
+    }
+    for (int32_t b = std::max(owned_[s], keep); b < blocks; ++b) {
+      int32_t blk;
+      if (!pushed.empty()) {
+        blk = pushed.back();
+        pushed.pop_back();
+      } else if (k > 0) {
+        blk = free_[--k];
+      } else {
+        return fail(ENOMEM_, "pool exhausted: not enough free blocks for the call (" +
+                                 std::to_string(free_.size()) + " free)");
+      }
+      plan->popped.push_back(blk);
+      plan->table_index.push_back(s * p_.max_blocks_per_seq + b);
+      ++g.new_blocks;
+    }
+    plan->segs.push_back(g);
+    plan->total_rows += n_new[i];
   }
   return OK;
 }
 
 void Core::commit_append(const AppendPlan& plan) {
-  size_t i = 0;
+  size_t i = 0, r = 0;
   for (const AppendSeg& g : plan.segs) {
+    for (int b = 0; b < g.released; ++b, ++r) {
+      free_.push_back(plan.released[r]);
+      table_[plan.released_index[r]] = -1;
+    }
     for (int b = 0; b < g.new_blocks; ++b, ++i) {
       free_.pop_back();
       table_[plan.table_index[i]] = plan.popped[i];
     }
-    owned_[g.seq] += g.new_blocks;
-    len_[g.seq] = g.pos0 + g.n;
+    const int64_t len = (int64_t)g.pos0 + g.n;
+    owned_[g.seq] = std::max<int32_t>(owned_[g.seq], (int32_t)((len + kBlock - 1) / kBlock));
+    first_[g.seq] = g.keep_first;
+    len_[g.seq] = (int32_t)len;
   }
 }
 
@@ -202,6 +236,10 @@ int Core::rollback(int32_t seq, int32_t r, std::string* err) {
     if (err) *err = "rollback beyond seq_len";
     return ERANGE_;
   }
+  if (!window_intact(seq, (int64_t)len_[seq] - r)) {
+    if (err) *err = "rollback would reach positions a ring cache released";
+    return ERANGE_;
+  }
   len_[seq] -= r;
   return OK;
 }
@@ -212,11 +250,12 @@ int Core::free_seq(int32_t seq, std::string* err) {
     return ENOSEQ_;
   }
   int32_t* row = &table_[(size_t)seq * p_.max_blocks_per_seq];
-  for (int b = owned_[seq] - 1; b >= 0; --b) {
-    free_.push_back(row[b]);  // last pushed = row[0] = next handed out
+  for (int b = owned_[seq] - 1; b >= first_[seq]; --b) {
+    free_.push_back(row[b]);  // last pushed = the first held block = next handed out
     row[b] = -1;
   }
   owned_[seq] = 0;
+  first_[seq] = 0;
   len_[seq] = 0;
   return OK;
 }

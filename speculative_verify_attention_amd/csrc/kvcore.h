@@ -9,6 +9,7 @@
 // mlx-engine blog's prompt-caching section (256-token blocks).
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -18,6 +19,9 @@ namespace svattn {
 
 constexpr int kBlock = 256;
 constexpr int kMaxRows = 8;
+// A ring cache keeps the last window + kRingHistory positions of a sequence:
+// the rows one verify call appends can still be verified and rolled back.
+constexpr int kRingHistory = kMaxRows;
 
 enum Status { OK = 0, EINVAL_ = -1, ENOMEM_ = -2, ERANGE_ = -3, ENOSEQ_ = -4, EDEVICE_ = -5 };
 enum Format { FMT_FP32 = 0, FMT_BF16 = 1, FMT_TQ3 = 2 };
@@ -30,6 +34,7 @@ struct CoreParams {
   int32_t max_seqs = 0;
   int32_t max_blocks_per_seq = 0;
   int32_t format = FMT_BF16;
+  int32_t ring_window = 0;  // > 0: ring cache for layers whose window is at most this
   uint64_t alloc_seed = 0;
   uint64_t codec_seed = 0;
 };
@@ -76,12 +81,16 @@ struct AppendSeg {
   int32_t n;          // new positions
   int32_t src_row0;   // first source row in the caller's K/V
   int32_t new_blocks; // blocks popped for this sequence
+  int32_t released;   // blocks a ring cache releases first
+  int32_t keep_first; // first kept block after the append (0 for plain caches)
 };
 
 struct AppendPlan {
   std::vector<AppendSeg> segs;
   std::vector<int32_t> popped;           // blocks popped, in order, all sequences
   std::vector<int32_t> table_index;      // flat table index for each popped block
+  std::vector<int32_t> released;         // ring caches: blocks released, in order
+  std::vector<int32_t> released_index;   // flat table index of each
   int64_t total_rows = 0;
 };
 
@@ -91,8 +100,11 @@ class Core {
   const CoreParams& params() const { return p_; }
 
   // Validate an append and compute what it would do, without changing state.
+  // slack (optional, per entry): how far below the host's length the true
+  // length may be (rollbacks still pending on the device); a ring cache then
+  // keeps that much more history.
   int plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, AppendPlan* plan,
-                  std::string* err) const;
+                  std::string* err, const int32_t* slack = nullptr) const;
   // Apply a plan made against the current state.
   void commit_append(const AppendPlan& plan);
 
@@ -100,7 +112,15 @@ class Core {
   int free_seq(int32_t seq, std::string* err);
 
   int seq_len(int32_t seq, int32_t* out) const;
+  // Table entries in use (the index one past the last held block; ring
+  // caches hold only entries from first_block on, the rest read -1).
   int owned(int32_t seq, int32_t* out) const;
+  int32_t first_block(int32_t seq) const { return first_[seq]; }
+  // Ring caches: can a window still see everything it needs once the
+  // sequence is at `len` positions?  (Always true for plain caches.)
+  bool window_intact(int32_t seq, int64_t len) const {
+    return p_.ring_window == 0 || std::max<int64_t>(0, len - p_.ring_window + 1) >= (int64_t)first_[seq] * kBlock;
+  }
   const int32_t* table_row(int32_t seq) const { return &table_[(size_t)seq * p_.max_blocks_per_seq]; }
   int32_t free_count() const { return (int32_t)free_.size(); }
   bool valid_seq(int32_t seq) const { return seq >= 0 && seq < p_.max_seqs; }
@@ -110,7 +130,8 @@ class Core {
   CoreParams p_;
   std::vector<int32_t> free_;   // stack: free_.back() is the front of the free list
   std::vector<int32_t> table_;  // max_seqs x max_blocks_per_seq
-  std::vector<int32_t> owned_;  // blocks owned per sequence
+  std::vector<int32_t> owned_;  // table entries in use per sequence
+  std::vector<int32_t> first_;  // first held table entry (ring caches)
   std::vector<int32_t> len_;    // seq_len per sequence
   Codec codec_;
 };

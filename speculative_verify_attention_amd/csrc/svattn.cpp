@@ -83,6 +83,10 @@ MetaLayout meta_layout(const kv_params& p, const PoolLayout& lay) {
 int sync_pending(kv_cache* c);
 int enqueue_table_updates(kv_cache* c, const AppendPlan& plan, hipStream_t s);
 
+// Per call entry: the pending device rollbacks of its sequence (0 for bad ids,
+// which the plan rejects).
+std::vector<int32_t> pending_slack(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids);
+
 int set_err(kv_cache* c, int code, const std::string& msg) {
   if (c) c->err = msg;
   return code;
@@ -110,6 +114,7 @@ CoreParams core_params(const kv_params& p) {
   cp.max_seqs = p.max_seqs;
   cp.max_blocks_per_seq = p.max_blocks_per_seq;
   cp.format = p.format;
+  cp.ring_window = p.ring_window;
   cp.alloc_seed = p.alloc_seed;
   cp.codec_seed = p.codec_seed;
   return cp;
@@ -156,6 +161,8 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
   if (!seq_ids || !n_rows) return fail(KV_EINVAL, "null seq_ids / n_rows");
   if (num_q_heads < 1 || num_q_heads % P.num_kv_heads) return fail(KV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
   if (window < 0) return fail(KV_EINVAL, "window < 0");
+  if (P.ring_window > 0 && (window < 1 || window > P.ring_window))
+    return fail(KV_EINVAL, "a ring cache serves windows of 1 .. " + std::to_string(P.ring_window) + " positions");
   const int g = num_q_heads / P.num_kv_heads;
   int max_rows = 0;
   for (int i = 0; i < n_seqs; ++i) {
@@ -166,6 +173,8 @@ int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
     if (n_rows[i] > low)
       return fail(KV_ERANGE, "n_rows exceeds seq_len of sequence " + std::to_string(seq_ids[i]) +
                                  (up > low ? " (device rollbacks pending: the lower bound counts)" : ""));
+    if (P.ring_window > 0 && std::max(0, low - n_rows[i] - window + 1) < c->core.first_block(seq_ids[i]) * kBlock)
+      return fail(KV_ERANGE, "the rows' windows reach positions the ring cache released");
     max_rows = std::max(max_rows, (int)n_rows[i]);
     vp->rows += n_rows[i];
   }
@@ -251,7 +260,6 @@ int kv_record_bytes(int32_t head_dim, int32_t is_key, int32_t* out) {
 int kv_create(const kv_params* p, void* stream, kv_cache** out) {
   if (!p || !out) return KV_EINVAL;
   *out = nullptr;
-  if (p->reserved != 0) return KV_EINVAL;
   kv_cache* c = new kv_cache();
   std::string err;
   int rc = c->core.init(core_params(*p), &err);
@@ -318,7 +326,8 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
   int rc = check_device(c);
   if (rc != KV_OK) return rc;
   AppendPlan plan;
-  rc = c->core.plan_append(n_seqs, seq_ids, n_new, &plan, &c->err);
+  std::vector<int32_t> slack = pending_slack(c, n_seqs, seq_ids);
+  rc = c->core.plan_append(n_seqs, seq_ids, n_new, &plan, &c->err, slack.data());
   if (rc != KV_OK) return rc;
   if (plan.total_rows > 0 && (!k || !v)) return set_err(c, KV_EINVAL, "null k / v");
   if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
@@ -328,8 +337,23 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
   if (rc != KV_OK) return rc;
   // 2. slice-update / quantize-on-append, in launches of <= kMaxAppendSegs segments
   const CoreParams& P = c->core.params();
+  // A ring cache stores nothing below its first kept block: with no device
+  // rollback pending the rows are trimmed here, else the kernels skip them
+  // (the true positions are known on the device only).
+  std::vector<AppendSeg> stored;
+  for (size_t i = 0; i < plan.segs.size(); ++i) {
+    AppendSeg g = plan.segs[i];
+    const int32_t keep = g.keep_first * kBlock;
+    if (slack[i] == 0 && g.pos0 < keep) {
+      const int32_t cut = std::min(g.n, keep - g.pos0);
+      g.pos0 += cut;
+      g.n -= cut;
+      g.src_row0 += cut;
+    }
+    stored.push_back(g);
+  }
   std::vector<const AppendSeg*> segs;
-  for (const AppendSeg& g : plan.segs)
+  for (const AppendSeg& g : stored)
     if (g.n > 0) segs.push_back(&g);
   const bool tq3 = P.format == KV_TQ3;
   for (size_t i = 0; i < segs.size();) {
@@ -357,6 +381,7 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
       a.pos0[a.n_segs] = g.pos0;
       a.n[a.n_segs] = g.n;
       a.row0[a.n_segs] = g.src_row0;
+      a.keep[a.n_segs] = g.keep_first * kBlock;
       units += u;
       ++a.n_segs;
       ++i;
@@ -401,6 +426,8 @@ int kv_rollback_batch(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const
     int32_t len;
     c->core.seq_len(s, &len);
     if (n_tokens[i] > len) return set_err(c, KV_ERANGE, "rollback beyond seq_len");
+    if (!c->core.window_intact(s, (int64_t)len - n_tokens[i]))
+      return set_err(c, KV_ERANGE, "rollback would reach positions a ring cache released");
   }
   for (int i = 0; i < n_seqs; ++i) c->core.rollback(seq_ids[i], n_tokens[i], &c->err);
   return KV_OK;
@@ -451,6 +478,13 @@ int kv_encode(const kv_cache* cc, int64_t n_vecs, const float* src, int32_t is_k
 }  // extern "C"
 
 namespace {
+
+std::vector<int32_t> pending_slack(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids) {
+  std::vector<int32_t> out(std::max(1, n_seqs), 0);
+  for (int i = 0; i < n_seqs && seq_ids; ++i)
+    if (c->core.valid_seq(seq_ids[i])) out[i] = c->pend[seq_ids[i]];
+  return out;
+}
 
 // Read the device rollbacks back and apply them to the host state; blocks
 // until the stream of the last kv_rollback_device call gets here.
@@ -654,7 +688,8 @@ int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   int rc = check_device(c);
   if (rc != KV_OK) return rc;
   AppendPlan plan;
-  rc = c->core.plan_append(n_seqs, seq_ids, n_rows, &plan, &c->err);
+  std::vector<int32_t> slack = pending_slack(c, n_seqs, seq_ids);
+  rc = c->core.plan_append(n_seqs, seq_ids, n_rows, &plan, &c->err, slack.data());
   if (rc != KV_OK) return rc;
   VerifyPlan vp;
   rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, n_rows, &vp, &c->err);
@@ -704,6 +739,8 @@ int kv_rollback_device(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, cons
     int32_t up, low;
     verify_lengths(c, sid, 0, &up, &low);
     if (n_draft[i] > low) return set_err(c, KV_ERANGE, "n_draft exceeds the sequence's length");
+    if (!c->core.window_intact(sid, (int64_t)low - n_draft[i]))
+      return set_err(c, KV_ERANGE, "rollback could reach positions a ring cache released");
   }
   for (int first = 0; first < n_seqs; first += kMaxRollback) {
     RollbackArgs a;

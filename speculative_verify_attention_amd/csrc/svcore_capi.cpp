@@ -29,6 +29,7 @@ int svcore_create(const svcore_params* p, svcore** out) {
   cp.max_seqs = p->max_seqs;
   cp.max_blocks_per_seq = p->max_blocks_per_seq;
   cp.format = p->format;
+  cp.ring_window = p->ring_window;
   cp.alloc_seed = p->alloc_seed;
   cp.codec_seed = p->codec_seed;
   int rc = c->core.init(cp, &c->err);

@@ -16,16 +16,26 @@ from . import synth
 from ._binding import KVCache
 
 
+def ring_blocks_per_seq(window):
+    """Blocks a ring cache with this window keeps per sequence at most: the
+    last window + 8 positions, from a block boundary."""
+    return ceil_div(window + 8 - 1 + 255, 256)
+
+
 class Runner:
-    def __init__(self, wl, layers=None, device="cuda", track=False, extra_blocks=0):
+    def __init__(self, wl, layers=None, device="cuda", track=False, extra_blocks=0, ring=False):
         """layers: list of (window, softcap) per layer handle; default one
-        layer with the workload's own window and cap."""
+        layer with the workload's own window and cap.  ring: window layers
+        get ring caches (memory for their last window + 8 positions only)."""
         self.wl = wl
         self.device = device
         self.layers = layers or [(wl.window, wl.softcap)]
-        nb = wl.num_blocks() + extra_blocks
-        self.caches = [KVCache(wl.hkv, wl.d, nb, wl.n_seqs, wl.max_blocks_per_seq(), wl.fmt, wl.alloc_seed,
-                               wl.codec_seed, device=device) for _ in self.layers]
+        self.caches = []
+        for window, _ in self.layers:
+            rw = window if (ring and window > 0) else 0
+            nb = (wl.n_seqs * ring_blocks_per_seq(rw) if rw else wl.num_blocks()) + extra_blocks
+            self.caches.append(KVCache(wl.hkv, wl.d, nb, wl.n_seqs, wl.max_blocks_per_seq(), wl.fmt, wl.alloc_seed,
+                                       wl.codec_seed, device=device, ring_window=rw))
         self.track = track
         self.prov = [np.zeros(0, dtype=np.int64) for _ in range(wl.n_seqs)]  # -1-p: prefill p; r >= 0: step row r
         self.step_k, self.step_v = [], []  # host copies of step rows (tracked runs)
@@ -136,4 +146,4 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-__all__ = ["Runner", "alg_bytes_per_call", "ceil_div", "math"]
+__all__ = ["Runner", "alg_bytes_per_call", "ceil_div", "math", "ring_blocks_per_seq"]

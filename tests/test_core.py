@@ -29,11 +29,11 @@ def _core():
 
 
 class Core:
-    def __init__(self, num_blocks, max_seqs, max_bps, alloc_seed=0, fmt=1, d=128, codec_seed=0):
+    def __init__(self, num_blocks, max_seqs, max_bps, alloc_seed=0, fmt=1, d=128, codec_seed=0, ring_window=0):
         from speculative_verify_attention_amd import svcore_params
 
         self.lib = _core()
-        p = svcore_params(2, d, 256, num_blocks, max_seqs, max_bps, fmt, 0, alloc_seed, codec_seed)
+        p = svcore_params(2, d, 256, num_blocks, max_seqs, max_bps, fmt, ring_window, alloc_seed, codec_seed)
         self.h = ctypes.c_void_p()
         rc = self.lib.svcore_create(ctypes.byref(p), ctypes.byref(self.h))
         assert rc == 0
@@ -159,6 +159,32 @@ class CoreVsModel(RuleBasedStateMachine):
 
 TestCoreVsModel = CoreVsModel.TestCase
 TestCoreVsModel.settings = settings(max_examples=80, stateful_step_count=40, deadline=None)
+
+
+class RingCoreVsModel(CoreVsModel):
+    """The same walk on ring caches (window 300): released entries (-1), the
+    release-then-pop order and the rollback limit must agree too."""
+
+    def __init__(self):
+        RuleBasedStateMachine.__init__(self)
+        self.core = Core(24, 4, 6, alloc_seed=0xB10C5, ring_window=300)
+        self.model = B.KVModel(24, 4, 6, alloc_seed=0xB10C5, ring_window=300)
+
+
+TestRingCoreVsModel = RingCoreVsModel.TestCase
+TestRingCoreVsModel.settings = settings(max_examples=80, stateful_step_count=40, deadline=None)
+
+
+def test_ring_worked_example_matches_model():
+    c = Core(12, 1, 8, ring_window=300)
+    m = B.KVModel(12, 1, 8, ring_window=300)
+    for n in (600, 200, 100, 300):
+        assert c.append([0], [n]) == m.append([0], [[0] * n]) == 0
+        assert c.table(0) == m.table[0]
+    assert c.table(0) == [-1, -1, -1, 2, 1]
+    assert c.rollback(0, 134) == B.ERANGE and c.rollback(0, 133) == 0
+    assert c.free(0) == 0 and c.append([0], [1]) == 0
+    assert c.table(0) == [2]  # the first kept block came back first
 
 
 def test_free_list_permutation_matches_model():
