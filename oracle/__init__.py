@@ -22,6 +22,8 @@ Modules
 ``accept``       acceptance of the drafts after the verify forward: greedy
                  argmax and rejection sampling against the draft
                  distribution, with the caller's uniforms.
+``ngram``        the n-gram self-drafter that proposes the drafts (bigram /
+                 trigram continuation tables, EMA acceptance gate).
 
 Every function cites the passage of the pages it follows; where the pages are
 silent the plainest reading is taken and named in the docstring.
@@ -30,4 +32,4 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, library routines or published tables.
 """
 
-from . import splitmix, bookkeeping, attention, tq3, accept  # noqa: F401
+from . import splitmix, bookkeeping, attention, tq3, accept, ngram  # noqa: F401
