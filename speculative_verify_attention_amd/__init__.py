@@ -23,9 +23,11 @@ from ._binding import (  # noqa: F401
     KV_OK,
     KV_TQ3,
     KVCache,
+    NgramDrafter,
     SvattnError,
     accept,
     core_lib,
+    ngram_params,
     kv_append,
     kv_block_table,
     kv_codec,

@@ -45,6 +45,15 @@ class kv_params(ctypes.Structure):
     ]
 
 
+class ngram_params(ctypes.Structure):
+    _fields_ = [
+        ("max_seqs", _i32),
+        ("max_drafts", _i32),
+        ("ema_tau", ctypes.c_double),
+        ("ema_threshold", ctypes.c_double),
+    ]
+
+
 class svcore_params(ctypes.Structure):
     _fields_ = [
         ("num_kv_heads", _i32),
@@ -98,6 +107,19 @@ _SIGS = {
     "spec_accept_last_error": [],
 }
 
+_NGRAM_SIGS = {
+    "ngram_create": [ctypes.POINTER(ngram_params), ctypes.POINTER(_p)],
+    "ngram_destroy": [_p],
+    "ngram_observe": [_p, _i32, _i32p, _i32],
+    "ngram_draft": [_p, _i32, _i32p, _i32, _i32p],
+    "ngram_draft_batch": [_p, _i32, _i32p, _i32p, _i32p],
+    "ngram_observe_batch": [_p, _i32, _i32p, _i32p, _i32p],
+    "ngram_state": [_p, _i32, ctypes.POINTER(ctypes.c_double), _i32p, ctypes.POINTER(_i64)],
+    "ngram_reset": [_p, _i32],
+    "ngram_last_error": [_p],
+}
+_SIGS.update(_NGRAM_SIGS)
+
 _CORE_SIGS = {
     "svcore_create": [ctypes.POINTER(svcore_params), ctypes.POINTER(_p)],
     "svcore_destroy": [_p],
@@ -110,6 +132,7 @@ _CORE_SIGS = {
     "svcore_codec": [_p, _p, _p, _p, _p, _p],
     "svcore_half_bits": [ctypes.c_double, ctypes.POINTER(ctypes.c_uint16), _i32p],
     "svcore_last_error": [_p],
+    **_NGRAM_SIGS,
 }
 
 
@@ -496,3 +519,61 @@ class KVCache:
 
     def codec(self):
         return kv_codec(self.handle, self.head_dim)
+
+
+class NgramDrafter:
+    """The n-gram self-drafter (include/svdraft.h): host-side, so it runs from
+    either library; ``lib`` defaults to libsvattn.so."""
+
+    def __init__(self, max_seqs, max_drafts=4, ema_tau=0.1, ema_threshold=0.5, lib=None):
+        self.lib = lib or globals()["lib"]()
+        self.max_drafts = max_drafts
+        p = ngram_params(max_seqs, max_drafts, ema_tau, ema_threshold)
+        self.h = ctypes.c_void_p()
+        rc = self.lib.ngram_create(ctypes.byref(p), ctypes.byref(self.h))
+        if rc != KV_OK:
+            raise SvattnError(rc, "bad drafter parameters")
+
+    def close(self):
+        if self.h:
+            self.lib.ngram_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc):
+        if rc != KV_OK:
+            raise SvattnError(rc, self.lib.ngram_last_error(self.h).decode())
+
+    def observe(self, seq, tokens):
+        tokens = [int(t) for t in tokens]
+        self._check(self.lib.ngram_observe(self.h, seq, _arr(tokens), len(tokens)))
+
+    def draft(self, seq):
+        out = (ctypes.c_int32 * self.max_drafts)()
+        n = ctypes.c_int32()
+        self._check(self.lib.ngram_draft(self.h, seq, out, self.max_drafts, ctypes.byref(n)))
+        return list(out[: n.value])
+
+    def draft_batch(self, seqs):
+        out = (ctypes.c_int32 * max(1, len(seqs) * self.max_drafts))()
+        n = (ctypes.c_int32 * max(1, len(seqs)))()
+        self._check(self.lib.ngram_draft_batch(self.h, len(seqs), _arr(seqs), out, n))
+        return [list(out[i * self.max_drafts: i * self.max_drafts + n[i]]) for i in range(len(seqs))]
+
+    def observe_batch(self, seqs, token_lists):
+        flat = [int(t) for ts in token_lists for t in ts]
+        self._check(self.lib.ngram_observe_batch(self.h, len(seqs), _arr(seqs), _arr([len(t) for t in token_lists]),
+                                                 _arr(flat)))
+
+    def state(self, seq):
+        ema, en, seen = ctypes.c_double(), ctypes.c_int32(), ctypes.c_int64()
+        self._check(self.lib.ngram_state(self.h, seq, ctypes.byref(ema), ctypes.byref(en), ctypes.byref(seen)))
+        return ema.value, bool(en.value), seen.value
+
+    def reset(self, seq):
+        self._check(self.lib.ngram_reset(self.h, seq))
