@@ -153,7 +153,10 @@ struct EncodeArgs {
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
 // ---- verify attention ------------------------------------------------------------
-constexpr int kMaxAttnSeqs = 128;
+#ifndef SVATTN_MAX_ATTN_SEQS
+#define SVATTN_MAX_ATTN_SEQS 128
+#endif
+constexpr int kMaxAttnSeqs = SVATTN_MAX_ATTN_SEQS;
 
 // A call's work is cut into chunks of consecutive tiles of one (sequence, kv
 // head) pair; workgroup w takes one chunk.  Sequence i's pairs are split into
