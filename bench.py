@@ -120,7 +120,7 @@ def run_accept(args, name):
                    "input_sets": reps, "step": "spec_accept (row statistics, decisions, final draws)"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "spec_accept (all four kernels)",
+            "kernel": "spec_accept (all three kernels)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -411,9 +411,25 @@ def _csv_rows(directory, suffix):
     return rows
 
 
+def _layer_pick(workload):
+    """(layers, dominant index) of a workload: attention dispatches alternate
+    over the layers in step order, so the dominant layer's are every
+    layers-th one from that index."""
+    if workload not in workloads():
+        return 1, 0
+    wl, layers = workloads()[workload]()
+    layers = layers or [(wl.window, wl.softcap)]
+    return len(layers), max(range(len(layers)), key=lambda i: layers[i][0] == 0)
+
+
+def _is_attn(name):
+    return "attn_kernel" in name or "attn_tq3_kernel" in name
+
+
 def summarize_trace(directory, workload, cmd, out_path=None):
     """profiles/attn_kernel_<workload>_trace.txt from a rocprofv3 --kernel-trace
-    --stats run: the library's kernels with calls and durations."""
+    --stats run: the library's kernels with calls and durations, and the
+    attention dispatches of the dominant (full-attention) layer alone."""
     rows = _csv_rows(directory, "kernel_stats.csv")
     out = [f"# rocprofv3 --kernel-trace --stats summary, workload {workload}",
            f"# command: {cmd}", "# name | calls | average_us | min_us | max_us | percent_of_gpu_time"]
@@ -423,6 +439,14 @@ def summarize_trace(directory, workload, cmd, out_path=None):
             continue
         out.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}")
+    n_layers, dom = _layer_pick(workload)
+    disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                  for r in _csv_rows(directory, "kernel_trace.csv") if _is_attn(r["Kernel_Name"]))
+    if disp:
+        d = [t / 1e3 for _, t in disp[dom::n_layers]]
+        out.append(f"# attention dispatches of the dominant layer (every {n_layers}. from {dom}): calls | average_us | "
+                   "min_us | max_us")
+        out.append(f"dominant_layer_attention | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f}")
     path = out_path or os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_trace.txt")
     open(path, "w").write("\n".join(out) + "\n")
     return path
@@ -432,20 +456,23 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     """profiles/attn_kernel_<workload>_pmc.txt from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
     same counter reads for the 1 GiB copy probe."""
+    n_layers, dom = _layer_pick(workload)
+
     def per_kernel(directory, counter):
         acc = {}
         for r in _csv_rows(directory, "counter_collection.csv"):
             if r.get("Counter_Name") != counter:
                 continue
             k = r["Kernel_Name"]
-            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+            acc.setdefault(k, []).append((int(r.get("Dispatch_Id", 0)), float(r["Counter_Value"])))
         return acc
 
     kib = (1 << 30) / 1024.0
     res = {}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(directory, counter)
-        attn = [v for k, vs in acc.items() if "attn_kernel" in k or "attn_tq3_kernel" in k for v in vs]
+        attn = [v for _, v in sorted(x for k, vs in acc.items() if _is_attn(k) for x in vs)][dom::n_layers]
+        acc = {k: [v for _, v in vs] for k, vs in acc.items()}
         copy = [v for k, vs in acc.items() if "MulFunctor" in k or "mul" in k.lower() and "elementwise" in k
                 for v in vs if v > kib / 4]
         res[counter] = (sum(attn) / max(1, len(attn)), max(copy) if copy else float("nan"), len(attn))
@@ -455,7 +482,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     traffic = (f_attn * f_scale + w_attn * w_scale) * 1024.0
     out = [f"# rocprofv3 --pmc summary for the attention kernel, workload {workload}",
            f"# fetch command: {cmd_fetch}", f"# write command: {cmd_write}",
-           "# counters are KiB per dispatch; each is scaled by its reading for a plain copy of 1 GiB",
+           "# counters are KiB per dispatch; each is scaled by its reading for a plain copy of 1 GiB;",
+           "# attention dispatches of the dominant (full-attention) layer only",
            f"kernel_sources_sha256_16: {source_hash()}",
            f"attn_dispatches_fetch: {n_f}", f"attn_dispatches_write: {n_w}",
            f"attn_fetch_kib_avg: {f_attn:.1f}", f"copy_fetch_kib: {f_copy:.1f}", f"fetch_scale: {f_scale:.4f}",
