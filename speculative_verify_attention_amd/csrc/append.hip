@@ -142,7 +142,7 @@ struct EncOut {
 // Encode x (global, fp32, D values) with one full wavefront.  rbuf: this
 // wave's D doubles of LDS.
 template <int D>
-__device__ void encode_vector(const float* __restrict__ x, bool is_key, const int8_t* __restrict__ signs,
+__device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool is_key, const int8_t* __restrict__ signs,
                               const float* __restrict__ s_t, const double* thr, const double* lev16,
                               double* rbuf, EncOut<D>& o, uint32_t* sat) {
   constexpr int E = D / 64;
@@ -211,6 +211,9 @@ __device__ void encode_vector(const float* __restrict__ x, bool is_key, const in
     double proj[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) proj[e] = 0.0;
+    // unrolled so that many rows of S^T are in flight at once (the loop is
+    // a chain of dependent L2 round trips otherwise)
+#pragma unroll 16
     for (int j = 0; j < D; ++j) {
       const double rj = rbuf[j];
 #pragma unroll
@@ -290,8 +293,12 @@ template <int D>
 __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   constexpr int E = D / 64;
   constexpr int SB = tq3_sub_bytes(D);
+  // S^T staged in LDS once per workgroup for d <= 128 (64 KiB), so the
+  // projections of the key residuals read LDS instead of L2
+  constexpr bool kStage = D <= 128;
   __shared__ double rbuf[4][D];
   __shared__ uint8_t vcode[32][D];
+  __shared__ __align__(16) float st_lds[kStage ? D * D : 4];
   __shared__ uint32_t sat_any;
   const int unit = blockIdx.x;
   const int h = blockIdx.y;
@@ -304,6 +311,13 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   const int t0 = max(max(pos0, grp * 32), a.keep[seg]);  // ring caches store nothing below keep
   const int t1 = min(pos0 + a.n[seg], grp * 32 + 32);
   if (t0 >= t1) return;  // a spare unit, or one a ring cache drops (whole workgroup)
+  if constexpr (kStage) {
+    const float4* src = reinterpret_cast<const float4*>(a.s_t);
+    float4* dst = reinterpret_cast<float4*>(st_lds);
+#pragma unroll 4
+    for (int i = threadIdx.x; i < D * D / 4; i += 256) dst[i] = src[i];
+  }
+  const float* s_t = kStage ? st_lds : a.s_t;
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
   uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
   uint32_t sat = 0;
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
     const float* kx = reinterpret_cast<const float*>(a.k) + (src_row * a.lay.hkv + h) * D;
     const float* vx = reinterpret_cast<const float*>(a.v) + (src_row * a.lay.hkv + h) * D;
     EncOut<D> ko, vo;
-    encode_vector<D>(kx, true, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
+    encode_vector<D>(kx, true, a.signs, s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
     // key nibbles: dims 2b, 2b+1 share a byte
     if constexpr (E == 1) {
       const uint32_t nib = (uint32_t)(ko.code[0] | (ko.bit[0] << 3));
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
         sub[tq3_k_byte(D, m, lane * E + e, &nb)] = (uint8_t)(lo | (hi << 4));
       }
     }
-    encode_vector<D>(vx, false, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
+    encode_vector<D>(vx, false, a.signs, s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
 #pragma unroll
     for (int e = 0; e < E; ++e) vcode[m][lane * E + e] = vo.code[e];
     if (lane == 0) {
