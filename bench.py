@@ -178,11 +178,15 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+# the sources the attention kernels are built from: counters taken before any
+# of them changed no longer describe the kernel
+ATTN_SOURCES = ("attn.hip", "attn_tq3.hip", "attn_common.h", "kernels.h")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.dirname(ATTN_SRC))):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(os.path.dirname(ATTN_SRC), f), "rb").read())
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(os.path.dirname(ATTN_SRC), f), "rb").read())
     return h.hexdigest()[:16]
 
 
