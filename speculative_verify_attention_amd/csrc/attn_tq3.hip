@@ -163,7 +163,7 @@ struct TQ3Smem {
   static constexpr int SCL_OFF = 256;  // per wave: two slots of 48 dwords, alternating between sub-tiles
   static constexpr int QF_OFF = 4096;
   static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
-  static constexpr int KLUT_OFF = 65536;  // row = code byte: [levels x 32 slots][signs x 32 slots]
+  static constexpr int KLUT_OFF = 65536;  // row = code byte: 32 slots of (levels, signs)
   // a second column group's fragments go above the key table when both do
   // not fit below it (two-part fragments of 64 KiB for d = 128)
   static constexpr bool LOW2 = QF_OFF + NCT * QF_CT_BYTES <= KLUT_OFF;
@@ -237,11 +237,13 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       // byte b of the nibble word selects the table row, the lane's slot the
-      // column: address = 65536 + byte * 256 + slot * 4 (+ 128 for the signs),
-      // assembled from the bytes of (kslot, w) by one permute each
+      // column: address = 65536 + byte * 256 + slot * 8, assembled from the
+      // bytes of (kslot, w) by one permute; one 8-byte read returns the two
+      // codes' levels and their signs
       const uint32_t sel = 0x0C020000u | ((4u + b) << 8);
-      mse[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot, sel));
-      qjl[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot + 128, sel));
+      const uint2 ls = *reinterpret_cast<const uint2*>(lds + __builtin_amdgcn_perm(w, kslot, sel));
+      mse[b] = ls.x;
+      qjl[b] = ls.y;
     }
     const f16x8_t km = __builtin_bit_cast(f16x8_t, mse), kq = __builtin_bit_cast(f16x8_t, qjl);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(0, kk), s1, 0, 0, 0);
@@ -369,9 +371,9 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
     const uint32_t lo = i & 15, hi = i >> 4;
     const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
     const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-    uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half * 32;
+    uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half;  // slot sl at dwords 2 sl, 2 sl + 1
 #pragma unroll
-    for (int sl = 0; sl < 32; ++sl) row[sl] = half ? sg : lev;
+    for (int sl = 0; sl < 32; ++sl) row[2 * sl] = half ? sg : lev;
     if (threadIdx.x < 64) vlut[threadIdx.x] = lv[threadIdx.x & 7] | (lv[threadIdx.x >> 3] << 16);
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
       }
     }
   }
-  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
+  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 8);  // table base (byte 2) | slot (byte 0)
   __syncthreads();
 
   QFrags<D, P2> qr;
