@@ -496,8 +496,9 @@ int sync_pending(kv_cache* c) {
   if (e != hipSuccess) return hip_fail(c, e, "reading device rollbacks");
   for (int s = 0; s < ms; ++s)
     if (c->h_roll[s] < 0 || c->h_roll[s] > c->pend[s]) return set_err(c, KV_EDEVICE, "device rollback count out of range");
-  for (int s = 0; s < ms; ++s)
-    if (c->h_roll[s] > 0) c->core.rollback(s, c->h_roll[s], &c->err);
+  for (int s = 0; s < ms; ++s)  // cannot fail: every count was bounded when it was enqueued
+    if (c->h_roll[s] > 0 && c->core.rollback(s, c->h_roll[s], &c->err) != KV_OK)
+      return set_err(c, KV_EDEVICE, "device rollback past what the host allowed");
   e = launch_fill_zero(c->droll, ms, c->pend_stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->pend_stream);
   if (e != hipSuccess) return hip_fail(c, e, "clearing device rollbacks");

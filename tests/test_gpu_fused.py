@@ -228,3 +228,52 @@ def test_device_rollback_errors_change_nothing():
         c.verify([0], [8], q, wl.hq, wl.scale)
     assert e.value.code == KV_ERANGE
     assert c.seq_len(0) == 6 and c.seq_len(1) == 20
+
+
+def test_append_verify_errors_change_nothing():
+    banner("append_verify argument errors")
+    from speculative_verify_attention_amd import KV_ENOMEM
+
+    wl = workload(KV_BF16, 8, 2, 64, [250, 40])
+    r = Runner(wl)
+    r.fill()
+    c = r.caches[0]
+    snap = lambda: ([c.seq_len(s) for s in (0, 1)], [c.block_table(s) for s in (0, 1)], c.free_blocks())  # noqa: E731
+    before = snap()
+    k, v = synth.step_kv(wl, 0, 8, "cuda")
+    q = synth.queries(wl, 0, 8, "cuda")
+    with pytest.raises(SvattnError) as e:
+        c.append_verify([0, 1], [5, 0], k, v, q, wl.hq, wl.scale)  # a verify needs >= 1 row
+    assert e.value.code == KV_EINVAL
+    k16, v16 = synth.step_kv(wl, 1, 16, "cuda")
+    q16 = synth.queries(wl, 1, 16, "cuda")
+    with pytest.raises(SvattnError) as e:
+        c.append_verify([0, 1], [5, 9], k16, v16, q16, wl.hq, wl.scale)  # more rows than a call verifies
+    assert e.value.code == KV_EINVAL
+    tiny = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(SvattnError) as e:
+        c.append_verify([0, 1], [5, 3], k, v, q, wl.hq, wl.scale, workspace=tiny)
+    assert e.value.code == KV_ENOMEM
+    assert snap() == before  # no append was committed by any failed call
+
+
+def test_append_verify_unaligned_rows_take_the_two_launch_path():
+    banner("append_verify with K/V not 16-byte aligned")
+    wl = workload(KV_BF16, 8, 2, 64, [250, 40])
+    a, b = Runner(wl), Runner(wl)
+    a.fill()
+    b.fill()
+    k, v = synth.step_kv(wl, 0, 8, "cuda")
+    q = synth.queries(wl, 0, 8, "cuda")
+    flat_k = torch.empty(k.numel() + 1, dtype=k.dtype, device="cuda")
+    flat_v = torch.empty_like(flat_k)
+    ku = flat_k[1:].view(k.shape)  # 2 bytes past a 16-byte boundary
+    vu = flat_v[1:].view(v.shape)
+    ku.copy_(k)
+    vu.copy_(v)
+    oa = a.caches[0].append_verify([0, 1], [5, 3], k, v, q, wl.hq, wl.scale)
+    ob = b.caches[0].append_verify([0, 1], [5, 3], ku, vu, q, wl.hq, wl.scale)
+    assert torch.equal(oa, ob)
+    for s, L in ((0, 255), (1, 43)):
+        xa, xb = stored(a.caches[0], s, L), stored(b.caches[0], s, L)
+        assert all(np.array_equal(xa[key], xb[key]) for key in xa)
