@@ -149,11 +149,16 @@ __device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
 // write the normalized output (the pair was one chunk) or the chunk's
 // partial (m, l, acc) into its slot for the merge.
 // NW waves per workgroup: NCT column groups of NW / NCT token-lane waves.
+// Token lanes that are not a power of two first fold the lanes past the
+// largest power of two P into the first TL - P, then halve P down to 1.
 template <int D, int NCT, int NW = 4>
 struct CombineBuf {
   static constexpr int TL = NW / NCT;
+  static constexpr int P = TL >= 8 ? 8 : TL >= 4 ? 4 : TL >= 2 ? 2 : 1;  // TL <= 15
+  static constexpr int SLOTS = (TL - P > P / 2 ? TL - P : P / 2) > 0 ? (TL - P > P / 2 ? TL - P : P / 2) : 1;
   static constexpr int CSTRIDE = D * 32 + 64;  // floats per combine slot
-  static constexpr int FLOATS = NCT * (TL / 2) * CSTRIDE;
+  static constexpr int FLOATS = NCT * SLOTS * CSTRIDE;
+  static_assert(TL >= 1 && TL < 16, "token lanes");
 };
 
 template <int D, int NCT, int NW = 4>
@@ -161,38 +166,48 @@ __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, 
                                                   int s, int h, int row_i, int head_j, bool col_ok, int lane,
                                                   int ct, int tl) {
   constexpr int TL = NW / NCT;
+  constexpr int P = CombineBuf<D, NCT, NW>::P;
+  constexpr int SLOTS = CombineBuf<D, NCT, NW>::SLOTS;
   constexpr int NDT = D / 32;
   constexpr int CSTRIDE = CombineBuf<D, NCT, NW>::CSTRIDE;
   const int col = lane & 31, hh = lane >> 5;
   const int c = ct * 32 + col;
   cs.l += xor32(cs.l);
-#pragma unroll
-  for (int half = TL / 2; half >= 1; half >>= 1) {
-    if (tl >= half && tl < 2 * half) {
-      float* slot = cbuf + (ct * (TL / 2) + (tl - half)) * CSTRIDE;
-      if (hh == 0) {
-        slot[col] = cs.m;
-        slot[32 + col] = cs.l;
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
+  auto put = [&](int idx) {
+    float* slot = cbuf + (ct * SLOTS + idx) * CSTRIDE;
+    if (hh == 0) {
+      slot[col] = cs.m;
+      slot[32 + col] = cs.l;
     }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) slot[64 + (dt * 16 + r) * 64 + lane] = cs.acc[dt][r];
+  };
+  auto fold = [&](int idx) {
+    const float* slot = cbuf + (ct * SLOTS + idx) * CSTRIDE;
+    const float mp = slot[col], lp = slot[32 + col];
+    const float mm = fmaxf(cs.m, mp);
+    const float mu = mm == NEG_INF ? 0.0f : mm;
+    const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
+    cs.l = cs.l * fs + lp * fp;
+    cs.m = mm;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
+  };
+  if constexpr (TL > P) {
+    if (tl >= P) put(tl - P);
     __syncthreads();
-    if (tl < half) {
-      const float* slot = cbuf + (ct * (TL / 2) + tl) * CSTRIDE;
-      const float mp = slot[col], lp = slot[32 + col];
-      const float mm = fmaxf(cs.m, mp);
-      const float mu = mm == NEG_INF ? 0.0f : mm;
-      const float fs = fast_exp2(cs.m - mu), fp = fast_exp2(mp - mu);
-      cs.l = cs.l * fs + lp * fp;
-      cs.m = mm;
+    if (tl < TL - P) fold(tl);
+    __syncthreads();
+  }
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cs.acc[dt][r] = cs.acc[dt][r] * fs + slot[64 + (dt * 16 + r) * 64 + lane] * fp;
-    }
+  for (int half = P / 2; half >= 1; half >>= 1) {
+    if (tl >= half && tl < 2 * half) put(tl - half);
+    __syncthreads();
+    if (tl < half) fold(tl);
     if (half > 1) __syncthreads();
   }
 

@@ -41,6 +41,10 @@
 #ifndef SVATTN_TQ3_NBUF_PRECISE
 #define SVATTN_TQ3_NBUF_PRECISE 3
 #endif
+// Waves per workgroup (one workgroup per CU: the tables fill the LDS).
+#ifndef SVATTN_TQ3_WAVES
+#define SVATTN_TQ3_WAVES 8
+#endif
 
 namespace svattn {
 
@@ -141,7 +145,7 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
   t.sc = *reinterpret_cast<const uint32_t*>(sub + 28 * D + (lane < 48 ? lane : lane - 16) * 4);
 }
 
-// Shared memory of the partial kernel (NW = 8 waves, two per SIMD).
+// Shared memory of the partial kernel (NW waves; 8 = two per SIMD).
 //  * key table, indexed by (byte of two key nibbles, lane slot): every lane of
 //    a 32-lane group reads its own 8-byte column, so table reads never
 //    conflict on LDS banks whatever the codes are;
@@ -152,7 +156,7 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
 // The combine buffer reuses the key table and fragments after the loop.
 template <int D, int NCT, int P2>
 struct TQ3Smem {
-  static constexpr int NW = 8;
+  static constexpr int NW = SVATTN_TQ3_WAVES;
   static constexpr int TL = NW / NCT;
   static constexpr int NPART = 2 * P2;  // q' hi, q'' hi (, q' lo, q'' lo)
   // below 64 KiB: value table, scale slices, query fragments; the key table
@@ -161,7 +165,7 @@ struct TQ3Smem {
   // 16-bit offset field
   static constexpr int VLUT_OFF = 0;
   static constexpr int SCL_OFF = 256;  // per wave: two slots of 48 dwords, alternating between sub-tiles
-  static constexpr int QF_OFF = 4096;
+  static constexpr int QF_OFF = (SCL_OFF + NW * 2 * 48 * 4 + 4095) / 4096 * 4096;
   static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
   static constexpr int KLUT_OFF = 65536;  // row = code byte: 32 slots of (levels, signs)
   // a second column group's fragments go above the key table when both do
@@ -314,7 +318,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 }
 
 template <int D, int NCT, int P2, bool CAP>
-__global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
+__global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArgs a) {
   using SM = TQ3Smem<D, NCT, P2>;
   constexpr int NW = SM::NW;
   constexpr int TL = SM::TL;
@@ -367,13 +371,15 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
     // key table: byte (two nibbles code | sign << 3) -> (levels, signs), one
     // copy per lane slot; value table: 6 bits of codes -> 2 levels
     const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
-    const int i = threadIdx.x & 255, half = threadIdx.x >> 8;
-    const uint32_t lo = i & 15, hi = i >> 4;
-    const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
-    const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-    uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half;  // slot sl at dwords 2 sl, 2 sl + 1
+    for (int idx = threadIdx.x; idx < 512; idx += NW * 64) {
+      const int i = idx & 255, half = idx >> 8;
+      const uint32_t lo = i & 15, hi = i >> 4;
+      const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
+      const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
+      uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half;  // slot sl at dwords 2 sl, 2 sl + 1
 #pragma unroll
-    for (int sl = 0; sl < 32; ++sl) row[2 * sl] = half ? sg : lev;
+      for (int sl = 0; sl < 32; ++sl) row[2 * sl] = half ? sg : lev;
+    }
     if (threadIdx.x < 64) vlut[threadIdx.x] = lv[threadIdx.x & 7] | (lv[threadIdx.x >> 3] << 16);
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(512) void attn_tq3_kernel(AttnArgs a) {
 template <int D, int NCT>
 static hipError_t launch_tq3_dn(const AttnArgs& a, bool precise, hipStream_t s) {
   const bool cap = a.softcap > 0.0f;
-  dim3 grid(a.n_wg), block(512);
+  dim3 grid(a.n_wg), block(SVATTN_TQ3_WAVES * 64);
   if (precise) {
     if (cap)
       hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, true>), grid, block, 0, s, a);
