@@ -59,6 +59,12 @@ ACCEPT_WORKLOADS = {
 }
 
 
+def percentiles(ms):
+    """Nearest-rank p10, p50 and p90 of per-call durations (ms)."""
+    ks = sorted(ms)
+    return [round(ks[min(len(ks) - 1, max(0, math.ceil(f * len(ks)) - 1))], 5) for f in (0.1, 0.5, 0.9)]
+
+
 def run_accept(args, name):
     """Times spec_accept on seeded logits resident in HBM (replicated past
     1 GiB so that every call reads HBM, not the MALL)."""
@@ -99,7 +105,8 @@ def run_accept(args, name):
         ev[j][1].record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    call_list = [a.elapsed_time(b) for a, b in ev]
+    call_ms = sum(call_list) / args.steps
     value = rows_d * args.steps / el
     achieved = alg / (call_ms * 1e-3) / 1e9
     res = {
@@ -128,6 +135,7 @@ def run_accept(args, name):
             "traffic": None,
             "alg_bytes_per_launch": alg,
             "avg_launch_ms": round(call_ms, 5),
+            "launch_ms_p10_p50_p90": percentiles(call_list),
         },
     }
     if not args.no_cpu_baseline:
@@ -376,7 +384,7 @@ def run(args, name):
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_kernel",
+            "kernel": "attn_tq3_kernel" if wl.fmt == 2 else "attn_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -384,6 +392,7 @@ def run(args, name):
             "traffic": traffic,
             "alg_bytes_per_launch": round(dom_bytes_avg),
             "avg_launch_ms": round(kern_avg, 5),
+            "launch_ms_p10_p50_p90": percentiles(kern_ms),
         },
     }
     if not args.no_cpu_baseline:

@@ -147,12 +147,15 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
 
 // Shared memory of the partial kernel (NW waves; 8 = two per SIMD).
 //  * key table, indexed by (byte of two key nibbles, lane slot): every lane of
-//    a 32-lane group reads its own 8-byte column, so table reads never
-//    conflict on LDS banks whatever the codes are;
+//    a 32-lane group reads its own dword column (levels in the row's first
+//    half, signs in the second), so table reads never conflict on LDS banks
+//    whatever the codes are;
 //  * query fragments: per column group, the fp16 parts of q' and q'' in the
 //    matrix-core operand order, [part][k-step][lane] x 16 bytes, shared by
 //    the column group's waves;
-//  * value table (6 bits of codes -> 2 levels), per-wave scale slices.
+//  * value table (6 bits of codes -> 2 levels), also one copy per lane slot
+//    (a single copy puts entries e and e + 32 on one bank), and per-wave
+//    scale slices.
 // The combine buffer reuses the key table and fragments after the loop.
 template <int D, int NCT, int P2>
 struct TQ3Smem {
@@ -163,11 +166,11 @@ struct TQ3Smem {
   // fills the next 64 KiB, so that a key-table address is one byte permute
   // of (slot, code byte, 1) and every other address fits an instruction's
   // 16-bit offset field
-  static constexpr int VLUT_OFF = 0;
-  static constexpr int SCL_OFF = 256;  // per wave: two slots of 48 dwords, alternating between sub-tiles
+  static constexpr int VLUT_OFF = 0;     // 64 entries x 32 lane slots x 4 bytes
+  static constexpr int SCL_OFF = 8192;  // per wave: two slots of 48 dwords, alternating between sub-tiles
   static constexpr int QF_OFF = (SCL_OFF + NW * 2 * 48 * 4 + 4095) / 4096 * 4096;
   static constexpr int QF_CT_BYTES = NPART * (D / 16) * 64 * 16;
-  static constexpr int KLUT_OFF = 65536;  // row = code byte: 32 slots of (levels, signs)
+  static constexpr int KLUT_OFF = 65536;  // row = code byte: 32 level slots, then 32 sign slots
   // a second column group's fragments go above the key table when both do
   // not fit below it (two-part fragments of 64 KiB for d = 128)
   static constexpr bool LOW2 = QF_OFF + NCT * QF_CT_BYTES <= KLUT_OFF;
@@ -232,24 +235,28 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     return (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (w >> 16) : (w & 0xFFFF)));
   };
 
-  // S1 = <q', c16[code]>, S2 = <q'', b> for the 32 keys of the sub-tile
-  f32x16_t s1 = {}, s2 = {};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
+  // S1 = <q', c16[code]>, S2 = <q'', b> for the 32 keys of the sub-tile.
+  // Byte b of a nibble word selects the table row, the lane's slot the
+  // column: address = 65536 + byte * 256 + slot * 4 (+ 128 for the signs),
+  // assembled from the bytes of (kslot, w) by one permute per read, so the
+  // reads land directly in the operand registers.  The reads of k-step
+  // kk + 1 are issued before the products of k-step kk.
+  auto fetch = [&](int kk, u32x4_t& mse, u32x4_t& qjl) {
     const uint32_t w = t.kc[kk >> 2][kk & 3];
-    u32x4_t mse, qjl;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      // byte b of the nibble word selects the table row, the lane's slot the
-      // column: address = 65536 + byte * 256 + slot * 8, assembled from the
-      // bytes of (kslot, w) by one permute; one 8-byte read returns the two
-      // codes' levels and their signs
       const uint32_t sel = 0x0C020000u | ((4u + b) << 8);
-      const uint2 ls = *reinterpret_cast<const uint2*>(lds + __builtin_amdgcn_perm(w, kslot, sel));
-      mse[b] = ls.x;
-      qjl[b] = ls.y;
+      mse[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot, sel));
+      qjl[b] = *reinterpret_cast<const uint32_t*>(lds + __builtin_amdgcn_perm(w, kslot | 0x80u, sel));
     }
-    const f16x8_t km = __builtin_bit_cast(f16x8_t, mse), kq = __builtin_bit_cast(f16x8_t, qjl);
+  };
+  f32x16_t s1 = {}, s2 = {};
+  u32x4_t mse[2], qjl[2];
+  fetch(0, mse[0], qjl[0]);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (kk + 1 < D / 16) fetch(kk + 1, mse[(kk + 1) & 1], qjl[(kk + 1) & 1]);
+    const f16x8_t km = __builtin_bit_cast(f16x8_t, mse[kk & 1]), kq = __builtin_bit_cast(f16x8_t, qjl[kk & 1]);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(0, kk), s1, 0, 0, 0);
     s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(1, kk), s2, 0, 0, 0);
     if constexpr (P2 == 2) {
@@ -266,7 +273,8 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     scale_words(1, gw);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f)) * a.q1_mul;
+      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f));
+      if constexpr (P2 == 2) x *= a.q1_mul;  // one-part fragments carry it already
       if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
       p[0][r] = x;
     }
@@ -309,7 +317,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
         g = v == 0 ? __builtin_amdgcn_alignbit(w3[2], w3[1], 16) : (w3[2] >> 8);
       u32x4_t vv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vv[q] = vlut[(g >> (6 * q)) & 63];
+      for (int q = 0; q < 4; ++q) vv[q] = vlut[((g >> (6 * q)) & 63) << 5];
       const f16x8_t vop = __builtin_bit_cast(f16x8_t, vv);
       cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, phi, cs.acc[dt], 0, 0, 0);
       if constexpr (P2 == 2) cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
@@ -369,18 +377,20 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   __syncthreads();
   {
     // key table: byte (two nibbles code | sign << 3) -> (levels, signs), one
-    // copy per lane slot; value table: 6 bits of codes -> 2 levels
+    // copy per lane slot; value table: 6 bits of codes -> 2 levels, likewise
     const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
-    for (int idx = threadIdx.x; idx < 512; idx += NW * 64) {
-      const int i = idx & 255, half = idx >> 8;
-      const uint32_t lo = i & 15, hi = i >> 4;
-      const uint32_t lev = lv[lo & 7] | (lv[hi & 7] << 16);
-      const uint32_t sg = ((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16);
-      uint32_t* row = reinterpret_cast<uint32_t*>(klut + i * 256) + half;  // slot sl at dwords 2 sl, 2 sl + 1
-#pragma unroll
-      for (int sl = 0; sl < 32; ++sl) row[2 * sl] = half ? sg : lev;
+    // dword j of the key table is row j >> 6, half (j >> 5) & 1, slot j & 31:
+    // consecutive lanes store consecutive dwords
+    for (int j = threadIdx.x; j < 256 * 64; j += NW * 64) {
+      const uint32_t i = j >> 6, lo = i & 15, hi = i >> 4;
+      reinterpret_cast<uint32_t*>(klut)[j] =
+          (j & 32) ? (((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16))
+                   : (lv[lo & 7] | (lv[hi & 7] << 16));
     }
-    if (threadIdx.x < 64) vlut[threadIdx.x] = lv[threadIdx.x & 7] | (lv[threadIdx.x >> 3] << 16);
+    for (int idx = threadIdx.x; idx < 64 * 32; idx += NW * 64) {
+      const int e = idx >> 5;  // entry; idx & 31 is the lane slot
+      vlut[idx] = lv[e & 7] | (lv[e >> 3] << 16);
+    }
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
     for (int kk = tl; kk < D / 16; kk += TL) {
@@ -392,10 +402,15 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
         const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
         const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
         const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
+        // one-part fragments also carry the score multiplier (fp16 rounds
+        // relative to the value, so this costs no precision); two-part ones
+        // do not, which keeps their low-order parts out of the fp16
+        // subnormal range
+        const float m1 = P2 == 1 ? a.q1_mul : 1.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = e < 4 ? x0[e] : x1[e - 4];
-          const float y = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
+          const float x = (e < 4 ? x0[e] : x1[e - 4]) * m1;
+          const float y = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul * m1;
           h1[e] = (_Float16)x;
           l1[e] = (_Float16)(x - (float)h1[e]);
           h2[e] = (_Float16)y;
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
       }
     }
   }
-  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 8);  // table base (byte 2) | slot (byte 0)
+  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
   __syncthreads();
 
   QFrags<D, P2> qr;
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
         if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
         if (k + 1 < cnt && lane < 48) scl[((k + 1) & 1) * 48 + lane] = buf[(u + 1) % NBUF].sc;
         __builtin_amdgcn_wave_barrier();
-        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut, scl + (k & 1) * 48, a, (tlo + t_first + k * TL) * 32, L,
+        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a, (tlo + t_first + k * TL) * 32, L,
                                 n, ppos, lane, kslot);
         __builtin_amdgcn_wave_barrier();
       }
