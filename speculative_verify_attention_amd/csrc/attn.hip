@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   const int w = blockIdx.x;
   const Chunk ch = chunk_of(a, w);
   const int s = ch.s, h = ch.h, tlo = ch.tlo;
-  const int L = ch.L, n = a.nrows[s];
+  const int L = ch.L, n = ch.n;
   const int R = n * a.g;
   const bool col_ok = c < R;
   const int row_i = col_ok ? c / a.g : 0;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   // the compiler turn every table read into a vector load (and a wait on
   // the tile loads in flight).  Nothing writes the table during a launch.
   typedef __attribute__((address_space(4))) const int32_t cint32_t;
-  cint32_t* trow = (cint32_t*)(a.table + (int64_t)a.seq[s] * a.max_bps);
+  cint32_t* trow = (cint32_t*)(a.table + (int64_t)ch.seq * a.max_bps);
   const int64_t head_off = (int64_t)h * 256 * D * E;
   auto block_of = [&](int key) { return trow[key >> 8]; };
   auto bases = [&](int t, const uint8_t*& kb, const uint8_t*& vb) {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
       const int item = threadIdx.x;
       if (item < (hi - lo) * (D / G)) {
         const int p = lo + item / (D / G), d0 = (item % (D / G)) * G;
-        const int64_t src = ((int64_t)(a.qrow0[s] + p - (L - n)) * a.lay.hkv + h) * D + d0;
+        const int64_t src = ((int64_t)(ch.qrow0 + p - (L - n)) * a.lay.hkv + h) * D + d0;
         T kx[G], vx[G];
         const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.new_k) + src);
         const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(static_cast<const T*>(a.new_v) + src);
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
     }
   }
 
-  const float* qsrc = a.q + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+  const float* qsrc = a.q + ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
   QOperand<FMT, D> qop;
   if constexpr (FMT == 1) {
     if (tl == 0) QOperand<1, D>::store(qlds + ct * (D / 16) * 64, qsrc, col_ok, lane);
@@ -381,20 +381,27 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
 
-  for (int i = 0; i < cnt; i += NBUF) {
+  // Whole rounds of NBUF tiles, then the last tiles (fewer than NBUF, all in
+  // flight already).  Inside a round the prefetch is unconditional: past the
+  // end it reloads the last tile into the ring slot that no tile uses any
+  // more.  A conditional prefetch would join two paths with different
+  // numbers of loads in flight, and the compiler's wait counts then assume
+  // the worse one: the wait for tile k would also wait for the tile just
+  // requested.
+  int i = 0;
+  for (; i + NBUF <= cnt; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int k = i + u;
-      if (k < cnt) {
-        if (k + NBUF - 1 < cnt) {
-          const uint8_t *kb, *vb;
-          bases(t_first + (k + NBUF - 1) * TL, kb, vb);
-          load_tile<FMT, D>(buf[(u + NBUF - 1) % NBUF], kb, vb, lane);
-        }
-        process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane);
-      }
+      const uint8_t *kb, *vb;
+      bases(t_first + min(k + NBUF - 1, cnt - 1) * TL, kb, vb);
+      load_tile<FMT, D>(buf[(u + NBUF - 1) % NBUF], kb, vb, lane);
+      process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane);
     }
   }
+#pragma unroll
+  for (int u = 0; u + 1 < NBUF; ++u)
+    if (i + u < cnt) process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + (i + u) * TL) * TK, L, n, ppos, lane);
 
   combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
@@ -412,31 +419,64 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   const int rmax = a.rpad;
   const int pair = blockIdx.x / rmax, c = blockIdx.x - pair * rmax;
   const int s = pair / hkv, h = pair - s * hkv;
-  const int n = a.nrows[s];
+  // the sequence's fields, read together (one round trip) before any branch
+  const int n = a.nrows[s], k = a.ksplit[s], wb = a.wg_base[s], q0 = a.qrow0[s];
   const int R = n * a.g;
-  const int k = a.ksplit[s];
   if (c >= R || (k == 1 && !a.force_partial)) return;
-  const int w0 = a.wg_base[s] + h * k;  // the pair's chunks are workgroups w0 .. w0+k-1
+  const int w0 = wb + h * k;  // the pair's chunks are workgroups w0 .. w0+k-1
   const int lane = threadIdx.x;
   const float* base = a.part + (int64_t)w0 * a.slot_stride;
-  float M = NEG_INF;
-  for (int j = lane; j < k; j += 64) M = fmaxf(M, base[(int64_t)j * a.slot_stride + c]);
+  // One memory round trip for k <= KB: lane j holds chunk j's (m, l), and
+  // the first KB chunks' accumulator parts are loaded beside them (they do
+  // not depend on the maximum).
+  constexpr int KB = 8;
+  float mj = NEG_INF, lj = 0.0f;
+  if (lane < k) {
+    mj = base[(int64_t)lane * a.slot_stride + c];
+    lj = base[(int64_t)lane * a.slot_stride + a.rpad + c];
+  }
+  float accj[KB][EL];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    if (j < k) {
+      const float* src = base + (int64_t)j * a.slot_stride + 2 * a.rpad + (int64_t)c * D + lane * EL;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) accj[j][e] = src[e];
+    }
+  }
+  const float m_own = mj;  // chunk `lane`'s own maximum, read back by shuffles below
+  // more than 64 chunks: each lane folds chunks lane + 64, lane + 128, ...
+  // into its (m, l) online
+  for (int j = lane + 64; j < k; j += 64) {
+    const float* slot = base + (int64_t)j * a.slot_stride;
+    const float m2 = slot[c], l2 = slot[a.rpad + c];
+    const float mn = fmaxf(mj, m2);
+    if (mn != NEG_INF) {
+      lj = lj * fast_exp2(mj - mn) + l2 * fast_exp2(m2 - mn);
+      mj = mn;
+    }
+  }
+  float M = mj;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   const float mu = M == NEG_INF ? 0.0f : M;
-  float lsum = 0.0f;
-  for (int j = lane; j < k; j += 64) {
-    const float* slot = base + (int64_t)j * a.slot_stride;
-    lsum += slot[a.rpad + c] * fast_exp2(slot[c] - mu);
-  }
+  float lsum = lj * fast_exp2(mj - mu);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
   float acc[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    if (j < k) {
+      const float f = fast_exp2(__shfl(m_own, j) - mu);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[e] += accj[j][e] * f;
+    }
+  }
+  for (int j = KB; j < k; ++j) {
     const float* slot = base + (int64_t)j * a.slot_stride;
-    const float f = fast_exp2(slot[c] - mu);
+    const float f = fast_exp2((j < 64 ? __shfl(m_own, j) : slot[c]) - mu);
     const float* src = slot + 2 * a.rpad + (int64_t)c * D + lane * EL;
 #pragma unroll
     for (int e = 0; e < EL; ++e) acc[e] += src[e] * f;
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
     for (int e = 0; e < EL; ++e) acc[e] *= (a.signs[lane * EL + e] < 0 ? -inv_d : inv_d);
   }
   const int row_i = c / a.g, head_j = c - row_i * a.g;
-  float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;
+  float* o = a.out + ((int64_t)(q0 + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;
 #pragma unroll
   for (int e = 0; e < EL; ++e) o[e] = acc[e];
 }

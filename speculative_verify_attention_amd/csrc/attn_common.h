@@ -54,18 +54,6 @@ __device__ __forceinline__ float xor32(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-__device__ __forceinline__ int find_seq(const int32_t* base, int n, int f) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (base[mid] <= f)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 // Online-softmax state of one lane: column c's running reference max m (log2
 // units, equal in both half-waves), this lane's partial sum l, and its part
 // of the column's O^T accumulator.
@@ -112,28 +100,58 @@ __device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB]
   cs.l += lsum;
 }
 
-// Positions of sequence s the kernels see: the host's count minus any
-// rollback applied on the device and not yet read back by the host.
-__device__ __forceinline__ int seq_len_now(const AttnArgs& a, int s) {
-  return a.roll ? a.len[s] - a.roll[a.seq[s]] : a.len[s];
-}
-
-// Chunk of workgroup w: sequence index s (L positions), kv head h, chunk
-// `part` of k, tiles [t_begin, t_end) of the pair's nt (empty when pending
-// device rollbacks left fewer tiles than the host planned for).
+// Chunk of workgroup w: sequence index s (cache sequence seq, n query rows
+// from query row qrow0, L positions), kv head h, chunk `part` of k, tiles
+// [t_begin, t_end) of the pair's nt (empty when pending device rollbacks
+// left fewer tiles than the host planned for).
 struct Chunk {
-  int s, h, k, part, L, nt, tlo, t_begin, t_end;
+  int s, seq, qrow0, n, h, k, part, L, nt, tlo, t_begin, t_end;
 };
 
+// The per-sequence fields sit in the kernel arguments, which the first
+// reads fetch from memory.  Every lane reads the fields of sequences lane
+// and lane + 64 at once (coalesced, one round trip); the workgroup's
+// sequence is the number of sequences whose first workgroup is <= w, less
+// one (wg_base ascends), and its fields are then taken from the lane that
+// read them.  A search over wg_base with scalar reads would wait for one
+// round trip per step, then one more for the fields.
 __device__ __forceinline__ Chunk chunk_of(const AttnArgs& a, int w) {
+  constexpr int NF = 6;  // wg_base, ksplit, len, nrows, seq, qrow0
+  static_assert(kMaxAttnSeqs >= 64, "one sequence per lane");
+  const int lane = threadIdx.x & 63;
+  const int ns = a.n_seqs;
+  int f0[NF], f1[NF];
+  // unconditional reads inside the arrays (entries past n_seqs are ignored),
+  // so that the compiler issues them together
+  auto fetch = [&](int i, int (&f)[NF]) {
+    f[0] = a.wg_base[i];
+    f[1] = a.ksplit[i];
+    f[2] = a.len[i];
+    f[3] = a.nrows[i];
+    f[4] = a.seq[i];
+    f[5] = a.qrow0[i];
+  };
+  fetch(lane, f0);
+  const bool two = ns > 64;
+  if (two) fetch(min(lane + 64, kMaxAttnSeqs - 1), f1);
+  const uint64_t b0 = __ballot(lane < ns && f0[0] <= w);
+  const uint64_t b1 = two ? __ballot(lane + 64 < ns && f1[0] <= w) : 0ull;
+  const int s = __popcll(b0) + __popcll(b1) - 1;
+  int v[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j)
+    v[j] = s < 64 ? __builtin_amdgcn_readlane(f0[j], s) : __builtin_amdgcn_readlane(f1[j], s - 64);
   Chunk c;
-  c.s = find_seq(a.wg_base, a.n_seqs, w);
-  c.k = a.ksplit[c.s];
-  const int local = w - a.wg_base[c.s];
+  c.s = s;
+  c.k = v[1];
+  c.seq = v[4];
+  c.qrow0 = v[5];
+  c.n = v[3];
+  const int local = w - v[0];
   c.h = local / c.k;
   const int part = local - c.h * c.k;
   c.part = part;
-  const int L = seq_len_now(a, c.s), n = a.nrows[c.s];
+  const int L = a.roll ? v[2] - a.roll[c.seq] : v[2], n = c.n;
   c.L = L;
   const int tk = a.tile_keys;
   const int klo = a.window > 0 ? max(0, L - n - a.window + 1) : 0;

@@ -350,14 +350,18 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   const int w = blockIdx.x;
   const Chunk ch = chunk_of(a, w);
   const int s = ch.s, h = ch.h, tlo = ch.tlo;
-  const int L = ch.L, n = a.nrows[s];
+  const int L = ch.L, n = ch.n;
   const int R = n * a.g;
   const bool col_ok = c < R;
   const int row_i = col_ok ? c / a.g : 0;
   const int head_j = col_ok ? c - row_i * a.g : 0;
   const int ppos = L - n + row_i;
 
-  const int32_t* trow = a.table + (int64_t)a.seq[s] * a.max_bps;
+  // the table is read through the constant address space, so that its reads
+  // are scalar loads; a vector load here would be followed by a wait for
+  // every load in flight, the prefetched sub-tiles included
+  typedef __attribute__((address_space(4))) const int32_t cint32_t;
+  cint32_t* trow = (cint32_t*)(a.table + (int64_t)ch.seq * a.max_bps);
   auto sub_of = [&](int t) {
     const int key0 = (tlo + t) * 32;
     return a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + ((int64_t)h * 8 + ((key0 & 255) >> 5)) * SB;
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
       vlut[idx] = lv[e & 7] | (lv[e >> 3] << 16);
     }
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
-    const int64_t qrow = ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+    const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
     for (int kk = tl; kk < D / 16; kk += TL) {
       f16x8_t h1{}, l1{}, h2{}, l2{};
       if (col_ok) {
@@ -436,23 +440,42 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) cs.acc[dt] = f32x16_t{};
 
-  // a wave's LDS accesses execute in order: the scales of sub-tile k+1 go to
-  // the other slot while sub-tile k's are read from this one
-  if (cnt > 0 && lane < 48) scl[lane] = buf[0].sc;
-  for (int i = 0; i < cnt; i += NBUF) {
+  // A wave's LDS accesses execute in order: sub-tile k reads its scales from
+  // slot k & 1, and the scales of sub-tile k + 1 go to the other slot after
+  // sub-tile k is processed.  Staging them before would wait for the load
+  // just issued (with a two-deep ring, sub-tile k + 1's) and so expose the
+  // whole memory latency once per sub-tile.  Lanes 48..63 hold copies of
+  // lanes 32..47's scale words and store them to the same places, so the
+  // stores need no branch.
+  const int sl = lane < 48 ? lane : lane - 16;
+  auto stage = [&](int k, const TQ3Regs<D>& b) { scl[(k & 1) * 48 + sl] = b.sc; };
+  auto step = [&](int k, const TQ3Regs<D>& cur, const TQ3Regs<D>& next) {
+    __builtin_amdgcn_wave_barrier();
+    process_tq3<D, P2, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
+                            (tlo + t_first + k * TL) * 32, L, n, ppos, lane, kslot);
+    stage(k + 1, next);
+    __builtin_amdgcn_wave_barrier();
+  };
+  if (cnt > 0) stage(0, buf[0]);
+  // Whole rounds of NBUF sub-tiles, then the last ones (fewer than NBUF, all
+  // in flight already).  Inside a round the prefetch is unconditional: past
+  // the end it reloads the last sub-tile into the ring slot that no
+  // sub-tile uses any more (and its scales go to a slot nothing reads).  A
+  // conditional prefetch would join two paths with different numbers of
+  // loads in flight, and the compiler's wait counts then assume the worse
+  // one: the wait for sub-tile k would also wait for the loads just issued.
+  int i = 0;
+  for (; i + NBUF <= cnt; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int k = i + u;
-      if (k < cnt) {
-        if (k + NBUF - 1 < cnt) load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + (k + NBUF - 1) * TL), lane);
-        if (k + 1 < cnt && lane < 48) scl[((k + 1) & 1) * 48 + lane] = buf[(u + 1) % NBUF].sc;
-        __builtin_amdgcn_wave_barrier();
-        process_tq3<D, P2, CAP>(cs, buf[u], qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a, (tlo + t_first + k * TL) * 32, L,
-                                n, ppos, lane, kslot);
-        __builtin_amdgcn_wave_barrier();
-      }
+      load_tq3<D>(buf[(u + NBUF - 1) % NBUF], sub_of(t_first + min(k + NBUF - 1, cnt - 1) * TL), lane);
+      step(k, buf[u], buf[(u + 1) % NBUF]);
     }
   }
+#pragma unroll
+  for (int u = 0; u + 1 < NBUF; ++u)
+    if (i + u < cnt) step(i + u, buf[u], buf[(u + 1) % NBUF]);
   __syncthreads();  // the combine buffer overlays the tables
   combine_and_store<D, NCT, NW>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
