@@ -51,6 +51,20 @@ namespace svattn {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Two-part fp16 split of a pair of floats, x = hi + lo to ~2^-21: hi is one
+// explicit conversion (toward zero), and the residual is taken from that
+// same value.  Written as (_Float16)x and x - (float)(_Float16)x the compiler
+// may emit two conversions for hi (a scalar one for the residual and a
+// packed one for the operand) that round exact fp16 ties differently, and
+// the two parts then miss x by one fp16 ulp.
+__device__ __forceinline__ u32x2_t split_f16_pair(float a, float b) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const float ra = a - (float)h[0], rb = b - (float)h[1];
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t l = {(_Float16)ra, (_Float16)rb};
+  return u32x2_t{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};  // (hi pair, lo pair)
+}
+
 // ---- query rotation --------------------------------------------------------------
 
 // One wave per query vector: q' = H (D q) / sqrt(d) with an in-register
@@ -297,15 +311,23 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
-    f16x8_t phi, plo;
+    u32x4_t phw, plw;  // fp16 pairs
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 8; e += 2) {
       const int r = 8 * v + e;
-      const float nvr = half_at(vw, r);
-      const _Float16 hx = (_Float16)fmaf(p[0][r], nvr, 0.0f);
-      phi[e] = hx;
-      if constexpr (P2 == 2) plo[e] = (_Float16)fmaf(p[0][r], nvr, -(float)hx);
+      if constexpr (P2 == 2) {
+        const u32x2_t sp = split_f16_pair(p[0][r] * half_at(vw, r), p[0][r + 1] * half_at(vw, r + 1));
+        phw[e / 2] = sp[0];
+        plw[e / 2] = sp[1];
+      } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        phw[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)fmaf(p[0][r], half_at(vw, r), 0.0f),
+                                                          (_Float16)fmaf(p[0][r + 1], half_at(vw, r + 1), 0.0f)});
+      }
     }
+    const f16x8_t phi = __builtin_bit_cast(f16x8_t, phw);
+    f16x8_t plo{};
+    if constexpr (P2 == 2) plo = __builtin_bit_cast(f16x8_t, plw);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const uint32_t* w3 = t.vc[dt >> 1];
@@ -398,7 +420,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
     for (int kk = tl; kk < D / 16; kk += TL) {
-      f16x8_t h1{}, l1{}, h2{}, l2{};
+      u32x4_t h1{}, l1{}, h2{}, l2{};  // fp16 pairs
       if (col_ok) {
         const float* q1p = a.q + qrow + 16 * kk + 8 * hh;
         const float* q2p = a.q2 + qrow + 16 * kk + 8 * hh;
@@ -412,20 +434,28 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
         // subnormal range
         const float m1 = P2 == 1 ? a.q1_mul : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (e < 4 ? x0[e] : x1[e - 4]) * m1;
-          const float y = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul * m1;
-          h1[e] = (_Float16)x;
-          l1[e] = (_Float16)(x - (float)h1[e]);
-          h2[e] = (_Float16)y;
-          l2[e] = (_Float16)(y - (float)h2[e]);
+        for (int e = 0; e < 8; e += 2) {
+          const float xa = (e < 4 ? x0[e] : x1[e - 4]) * m1, xb = (e < 4 ? x0[e + 1] : x1[e - 3]) * m1;
+          const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul * m1;
+          const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul * m1;
+          if constexpr (P2 == 2) {
+            const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
+            h1[e / 2] = sx[0];
+            l1[e / 2] = sx[1];
+            h2[e / 2] = sy[0];
+            l2[e / 2] = sy[1];
+          } else {
+            typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+            h1[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)xa, (_Float16)xb});
+            h2[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)ya, (_Float16)yb});
+          }
         }
       }
-      *reinterpret_cast<f16x8_t*>(qf + (0 * (D / 16) + kk) * 1024 + lane * 16) = h1;
-      *reinterpret_cast<f16x8_t*>(qf + (1 * (D / 16) + kk) * 1024 + lane * 16) = h2;
+      *reinterpret_cast<u32x4_t*>(qf + (0 * (D / 16) + kk) * 1024 + lane * 16) = h1;
+      *reinterpret_cast<u32x4_t*>(qf + (1 * (D / 16) + kk) * 1024 + lane * 16) = h2;
       if constexpr (P2 == 2) {
-        *reinterpret_cast<f16x8_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
-        *reinterpret_cast<f16x8_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
+        *reinterpret_cast<u32x4_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
+        *reinterpret_cast<u32x4_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
       }
     }
   }

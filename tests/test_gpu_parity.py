@@ -158,6 +158,9 @@ EDGE = [
     ("d256_fp32", 8, 2, 256, KV_FP32, [300], [5], 0, 0.0, 1.0),
     ("d64_bf16", 16, 4, 64, KV_BF16, [5000, 1], [5, 1], 0, 0.0, 1.0),
     ("many_seqs", 8, 2, 128, KV_BF16, [int(x) for x in np.linspace(1, 3000, 150)], [2] * 150, 0, 0.0, 1.0),
+    # one (sequence, kv head) pair split into more than 64 chunks: the merge
+    # folds chunks past the wave's 64 lanes
+    ("single_pair_long", 8, 1, 128, KV_BF16, [60000], [5], 0, 0.0, 1.0),
 ]
 
 

@@ -164,6 +164,10 @@ EDGE = [
     ("softcap", 8, 2, 128, [800], [5], 0, 5.0, 3.0),
     ("short", 4, 1, 64, [0, 3], [5, 1], 0, 0.0, 1.0),
     ("ragged_many", 8, 2, 128, [int(x) for x in np.linspace(1, 2000, 40)], [3] * 40, 0, 0.0, 1.0),
+    # more than 64 sequences in a launch (two lanes' worth of per-sequence
+    # fields) and more than one launch
+    ("many_seqs", 8, 2, 64, [int(x) for x in np.linspace(1, 700, 140)], [2] * 140, 0, 0.0, 1.0),
+    ("single_pair_long", 8, 1, 128, [30000], [5], 0, 0.0, 1.0),
 ]
 
 
