@@ -78,6 +78,11 @@ class Runner:
         seqs = list(range(wl.n_seqs))
         for c in self.caches:
             c.append(seqs, rows, k, v)
+        self._record(k, v, rows)
+        return k, v
+
+    def _record(self, k, v, rows):
+        """Provenance of appended rows (tracked runs)."""
         if self.track:
             self.step_k.append(k.float().cpu().numpy())
             self.step_v.append(v.float().cpu().numpy())
@@ -86,7 +91,6 @@ class Runner:
                 self.prov[s] = np.concatenate([self.prov[s], off + np.arange(n, dtype=np.int64)])
                 off += n
             self.step_rows0 = off
-        return k, v
 
     def queries(self, step, rows, scale=1.0):
         return synth.queries(self.wl, step, int(sum(rows)), self.device, scale)
@@ -97,13 +101,23 @@ class Runner:
         return c.verify(list(range(self.wl.n_seqs)), rows, q, self.wl.hq, self.wl.scale, cap, window, out=out,
                         workspace=workspace, stream=stream)
 
-    def step(self, step, scale_q=1.0):
-        """rollback -> append -> verify on every layer; returns (rows, q, outs)."""
+    def step(self, step, scale_q=1.0, fused=False):
+        """rollback -> append -> verify on every layer (fused: kv_append_verify);
+        returns (rows, q, outs)."""
         rb, rows = self.plan(step)
         self.rollback(rb)
-        self.append_rows(step, rows)
+        if not fused:
+            self.append_rows(step, rows)
+            q = self.queries(step, rows, scale_q)
+            outs = [self.verify(i, rows, q) for i in range(len(self.layers))]
+            return rows, q, outs
+        wl = self.wl
+        k, v = synth.step_kv(wl, step, int(sum(rows)), self.device)
         q = self.queries(step, rows, scale_q)
-        outs = [self.verify(i, rows, q) for i in range(len(self.layers))]
+        seqs = list(range(wl.n_seqs))
+        outs = [c.append_verify(seqs, rows, k, v, q, wl.hq, wl.scale, cap, window)
+                for c, (window, cap) in zip(self.caches, self.layers)]
+        self._record(k, v, rows)
         return rows, q, outs
 
     # -- logical contents (tracked runs) ----------------------------------------------------
