@@ -131,3 +131,20 @@ def test_invalid_arguments():
                torch.zeros(9, device="cuda"), 1.0)
     with pytest.raises(SvattnError):
         accept([2], target, tokens, u, -1.0, draft_logits=draft)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_sweep(i):
+    """Seeded random cases: sequences, drafts per sequence (0..7), vocabulary
+    (97..300000, odd sizes included), temperature (greedy or 0.3..2), draft
+    logits or point masses."""
+    rng = np.random.default_rng(3000 + i)
+    n = int(rng.integers(1, 40))
+    n_draft = rng.integers(0, 8, size=n).tolist()
+    vocab = int(np.exp(rng.uniform(np.log(97), np.log(300000))))
+    temperature = 0.0 if i % 4 == 0 else float(rng.uniform(0.3, 2.0))
+    with_draft = bool(i % 3 != 0)
+    banner(f"accept sweep {i}: seqs={n} vocab={vocab} T={temperature:.3f} draft={with_draft}")
+    acc, tok, ora = run(n_draft, vocab, temperature, with_draft, 4000 + i, boost=float(rng.uniform(0.0, 6.0)))
+    excluded = compare(acc, tok, ora, sampled=temperature > 0)
+    assert excluded <= 2, excluded

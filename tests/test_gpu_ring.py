@@ -223,3 +223,20 @@ def test_ring_errors_change_nothing():
     assert c.block_table(0) == table and c.seq_len(0) == L
     c.rollback(0, 1000 - 867)
     assert c.seq_len(0) == 867
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_ring_sweep(i):
+    """Seeded random window layers on ring caches (window 1..600, format,
+    head dim, GQA group, 1..6 sequences of 8..2000 positions), host
+    rollbacks for even cases and device rollbacks for odd ones."""
+    rng = np.random.default_rng(7000 + i)
+    fmt = (KV_FP32, KV_BF16, KV_TQ3)[i % 3]
+    d = int(rng.choice([64, 128] if fmt == KV_TQ3 else [64, 128, 256]))
+    hkv = int(rng.choice([1, 2]))
+    g = int(rng.choice([1, 4, 8]))
+    prefill = np.exp(rng.uniform(np.log(8.0), np.log(2000.0), int(rng.integers(1, 7)))).astype(int).tolist()
+    window = int(rng.integers(1, 601))
+    cap = float(rng.choice([0.0, 30.0]))
+    banner(f"ring sweep {i}: fmt={fmt} d={d} hq={hkv * g} hkv={hkv} window={window} cap={cap} prefill={prefill}")
+    check(workload(fmt, hkv * g, hkv, d, prefill, window, cap, seed=50 + i), device_rb=bool(i % 2))
