@@ -508,6 +508,72 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     return path
 
 
+SQ_PASSES = ("SQ_WAVES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS "
+             "SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_LDS",
+             "SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
+             "SQ_LDS_ADDR_CONFLICT SQ_ACTIVE_INST_ANY")
+
+
+def summarize_sq(dirs, workload, cmds, out_path=None):
+    """profiles/attn_kernel_<workload>_sq.txt from rocprofv3 --pmc runs of SQ
+    counters (instruction mix, waits, matrix-core busy cycles; SQ_PASSES):
+    per-dispatch averages of the attention kernel (the dominant layer's
+    dispatches) and of the library's other kernels, and per-wave figures of
+    the attention kernel."""
+    n_layers, dom = _layer_pick(workload)
+    attn, other = {}, {}
+    for d in dirs:
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = r["Kernel_Name"]
+            if "svattn::" not in k:
+                continue
+            key = (k, r["Counter_Name"])
+            per.setdefault(key, {})
+            did = int(r["Dispatch_Id"])
+            per[key][did] = per[key].get(did, 0.0) + float(r["Counter_Value"])
+        counters = sorted({c for _, c in per})
+        for c in counters:
+            xs = sorted((did, v) for (k, cc), dv in per.items() if cc == c and _is_attn(k) for did, v in dv.items())
+            xs = [v for _, v in xs][dom::n_layers]
+            if xs:
+                attn[c] = (sum(xs) / len(xs), len(xs))
+            for (k, cc), dv in per.items():
+                if cc == c and not _is_attn(k):
+                    name = k.split("(")[0].replace("void ", "").replace("svattn::", "")
+                    other.setdefault(name, {})[c] = (sum(dv.values()) / len(dv), len(dv))
+    out = [f"# rocprofv3 --pmc SQ counter summary, workload {workload}"]
+    out += [f"# pass {i + 1} command: {c}" for i, c in enumerate(cmds)]
+    out += ["# per-dispatch averages in the units rocprofv3 reports (SQ_ACTIVE_INST_* and SQ_WAVE_CYCLES in",
+            "# quad-cycles per wave, summed; SQ_VALU_MFMA_BUSY_CYCLES in cycles summed over the SIMDs);",
+            "# attention rows: the dominant (full-attention) layer's dispatches",
+            f"kernel_sources_sha256_16: {source_hash()}"]
+    if attn:
+        out.append(f"== attention kernel ({next(iter(attn.values()))[1]} dispatches)")
+        out += [f"  {c:28s} {v:18.1f}" for c, (v, _) in sorted(attn.items())]
+        g = {c: v for c, (v, _) in attn.items()}
+        waves = g.get("SQ_WAVES", 0.0)
+        if waves > 0:
+            out.append("== attention kernel, per wave")
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+                if c in g:
+                    out.append(f"  {c.lower()[9:] + '_insts_per_wave':28s} {g[c] / waves:18.1f}")
+        wc = g.get("SQ_WAVE_CYCLES", 0.0)
+        if wc > 0:
+            for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+                      "SQ_WAIT_INST_LDS"):
+                if c in g:
+                    out.append(f"  {c.lower()[3:] + '_over_wave_cycles':28s} {g[c] / wc:18.4f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in g:
+            out.append(f"  {'mfma_busy_cycles_per_simd':28s} {g['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:18.1f}")
+    for name, cs in sorted(other.items()):
+        out.append(f"== {name} ({next(iter(cs.values()))[1]} dispatches)")
+        out += [f"  {c:28s} {v:18.1f}" for c, (v, _) in sorted(cs.items())]
+    path = out_path or os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_sq.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,12 +587,17 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the profiles/ summary of a kernel-trace run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary of two --pmc runs")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="write the profiles/ summary of --pmc runs of SQ counters (one directory per pass)")
     ap.add_argument("--cmd", nargs="*", default=[], help="the profiled command(s), recorded in the summary")
     ap.add_argument("--alg-bytes", type=float, default=0.0)
     ap.add_argument("--out", help="summary path (default: profiles/attn_kernel_<workload>_*.txt)")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.workload, " ".join(args.cmd), args.out))
+        return
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq, args.workload, args.cmd, args.out))
         return
     if args.summarize_pmc:
         cmds = args.cmd + ["", ""]
