@@ -30,6 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+EVENT_STRIDE = 7  # timed steps per HIP-event sample (see event_stride)
 METRIC = "verified query-tokens/s + effective KV GB/s (% HBM peak), spec-verify attention"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "speculative_verify_attention_amd", "csrc", "attn.hip")
@@ -57,6 +58,15 @@ ACCEPT_WORKLOADS = {
     "accept_qwen3_sampled": dict(n_draft=[4] * 16, vocab=151936, temperature=0.8, with_draft=True),
     "accept_qwen3_greedy": dict(n_draft=[4] * 16, vocab=151936, temperature=0.0, with_draft=True),
 }
+
+
+def event_stride(steps):
+    """Timed steps per HIP-event sample.  A pair of events around a launch
+    adds ~5 us of GPU time to its step (measured on the dense workload: 66.1
+    us per step with events on every step, 60.5 us with none), so the events
+    bracket the attention launch of every EVENT_STRIDE-th timed step only
+    (all of them when there are few steps); the step rate counts every step."""
+    return EVENT_STRIDE if steps >= 10 * EVENT_STRIDE else 1
 
 
 def percentiles(ms):
@@ -97,16 +107,20 @@ def run_accept(args, name):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    stride = event_stride(args.steps)
+    ev = {j: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for j in range(0, args.steps, stride)}
     t0 = time.perf_counter()
     for j in range(args.steps):
-        ev[j][0].record(stream)
+        if j in ev:
+            ev[j][0].record(stream)
         step(args.warmup + j)
-        ev[j][1].record(stream)
+        if j in ev:
+            ev[j][1].record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    call_list = [a.elapsed_time(b) for a, b in ev]
-    call_ms = sum(call_list) / args.steps
+    call_list = [a.elapsed_time(b) for a, b in ev.values()]
+    call_ms = sum(call_list) / len(call_list)
     value = rows_d * args.steps / el
     achieved = alg / (call_ms * 1e-3) / 1e9
     res = {
@@ -136,6 +150,7 @@ def run_accept(args, name):
             "alg_bytes_per_launch": alg,
             "avg_launch_ms": round(call_ms, 5),
             "launch_ms_p10_p50_p90": percentiles(call_list),
+            "launches_timed": len(call_list), "event_stride": stride,
         },
     }
     if not args.no_cpu_baseline:
@@ -302,7 +317,8 @@ def run(args, name):
     ws = [[torch.empty(2 * ws_need, dtype=torch.uint8, device=dev) for _ in layers] for _ in range(reps)]
     hip = Hip()
     dom = max(range(len(layers)), key=lambda i: layers[i][0] == 0)  # dominant layer: full attention
-    ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    stride = event_stride(args.steps)
+    ev = {j: (hip.event(), hip.event()) for j in range(0, args.steps, stride)}
     lens = [list(wl.prefill) for _ in range(reps)]  # host-side mirror of seq_len per replica
     last_rows = [None] * reps
     step_bytes = []
@@ -325,14 +341,14 @@ def run(args, name):
                 c.append(seqs, rows, k, v)
         lens[rep] = [L - b + n for L, b, n in zip(lens[rep], back, rows)]
         for li, c in enumerate(r.caches):
-            if li == dom and timed_idx is not None:
+            if li == dom and timed_idx in ev:
                 c.trace_events(*ev[timed_idx])
             window, cap = layers[li][0], layers[li][1]
             if args.separate:
                 c.verify(seqs, rows, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
             else:
                 c.append_verify(seqs, rows, k, v, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
-            if li == dom and timed_idx is not None:
+            if li == dom and timed_idx in ev:
                 c.trace_events(None, None)
         last_rows[rep] = rows
         if timed_idx is not None:
@@ -351,12 +367,13 @@ def run(args, name):
     # sanity: the host mirror of the lengths matches the library's
     for rep in range(reps):
         assert lens[rep] == [runners[rep].caches[0].seq_len(s) for s in seqs]
-    kern_ms = [hip.elapsed_ms(a, b) for a, b in ev]
-    for a, b in ev:
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in ev.values()]
+    for a, b in ev.values():
         hip.destroy(a)
         hip.destroy(b)
     kern_avg = sum(kern_ms) / len(kern_ms)
-    dom_bytes_avg = sum(b[dom] for b in step_bytes) / len(step_bytes)
+    # bytes of the launches the events timed
+    dom_bytes_avg = sum(step_bytes[j][dom] for j in ev) / len(ev)
     byt = sum(sum(b) for b in step_bytes)
     ms_per_step = el * 1e3 / args.steps
     value = tok / el
@@ -393,6 +410,7 @@ def run(args, name):
             "alg_bytes_per_launch": round(dom_bytes_avg),
             "avg_launch_ms": round(kern_avg, 5),
             "launch_ms_p10_p50_p90": percentiles(kern_ms),
+            "launches_timed": len(kern_ms), "event_stride": stride,
         },
     }
     if not args.no_cpu_baseline:
@@ -577,7 +595,7 @@ def summarize_sq(dirs, workload, cmds, out_path=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=210)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_4b_dense", choices=sorted(workloads()) + sorted(ACCEPT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
