@@ -237,10 +237,11 @@ __device__ __forceinline__ RowStats row_stats(const AcceptArgs& a, int row) {
 template <bool VEC>
 __device__ void draw_token(const AcceptArgs& a, const AcceptPlan& pl, int sidx, const float* fs) {
   __shared__ float wsum[kWaves];
-  __shared__ int s_tok, s_last;
+  __shared__ int s_tok, s_first, s_last;  // crossing, first positive weight past it, last positive weight
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) {
     s_tok = 0x7FFFFFFF;
+    s_first = 0x7FFFFFFF;
     s_last = -1;
   }
   // inclusive scan of the chunk sums in chunk order, 64 at a time; total =
@@ -298,12 +299,15 @@ __device__ void draw_token(const AcceptArgs& a, const AcceptPlan& pl, int sidx, 
   load_run<VEC>(a.target + (int64_t)pl.row_t * a.vocab, x0, a.vocab, lt);
   if (pl.row_q >= 0) load_run<VEC>(a.draft + (int64_t)pl.row_q * a.vocab, x0, a.vocab, lq);
   float ts = 0.0f;
-  int mylast = -1;
+  int myfirst = -1, mylast = -1;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     w[e] = x0 + e < a.vocab ? draw_weight(pl, a.inv_t, lt[e], pl.row_q >= 0 ? lq[e] : 0.0f, x0 + e) : 0.0f;
     ts += w[e];
-    if (w[e] > 0.0f) mylast = x0 + e;
+    if (w[e] > 0.0f) {
+      if (myfirst < 0) myfirst = x0 + e;
+      mylast = x0 + e;
+    }
   }
   // exclusive block scan of the runs' sums in thread order
   float inc = ts;
@@ -314,21 +318,37 @@ __device__ void draw_token(const AcceptArgs& a, const AcceptPlan& pl, int sidx, 
   }
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();  // also orders the s_tok / s_last initialisation before the atomics
-  float cum = inc - ts;
-  for (int w2 = 0; w2 < wave; ++w2) cum += wsum[w2];
-  if (mylast >= 0) atomicMax(&s_last, mylast);
-  if (cum <= rem) {
+  // Each run's start is exactly the previous run's end (the same fp32
+  // values), so the runs tile [0, chunk sum) without gaps: the run whose
+  // start is <= rem < end holds the crossing.  Its sequential sum may still
+  // stop short of rem by rounding (the crossing within an ulp of a run
+  // boundary); the crossing is then its last positive weight.
+  float pre = 0.0f;  // sum of the earlier waves, in the order every wave adds it
+  for (int w2 = 0; w2 < wave; ++w2) pre += wsum[w2];
+  const float end = inc + pre;
+  const float up = __shfl_up(end, 1);
+  const float start = lane == 0 ? pre : up;
+  // one atomic per wave: runs ascend with the lane, so the wave's last
+  // positive weight is in its highest such lane, the first past the crossing
+  // in its lowest
+  const uint64_t has = __builtin_amdgcn_ballot_w64(mylast >= 0);
+  if (has && lane == 63 - __builtin_clzll(has)) atomicMax(&s_last, mylast);
+  const uint64_t past = __builtin_amdgcn_ballot_w64(start > rem && myfirst >= 0);
+  if (past && lane == __builtin_ctzll(past)) atomicMin(&s_first, myfirst);
+  if (start <= rem) {
+    float cum = start;
+    int t = -1;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       cum += w[e];
-      if (cum > rem) {
-        atomicMin(&s_tok, x0 + e);
-        break;
-      }
+      if (t < 0 && cum > rem) t = x0 + e;
     }
+    if (t < 0 && end > rem) t = mylast;
+    if (t >= 0) atomicMin(&s_tok, t);
   }
   __syncthreads();
-  if (threadIdx.x == 0) a.out_tok[sidx] = s_tok != 0x7FFFFFFF ? s_tok : (s_last >= 0 ? s_last : c0);
+  if (threadIdx.x == 0)
+    a.out_tok[sidx] = s_tok != 0x7FFFFFFF ? s_tok : s_first != 0x7FFFFFFF ? s_first : (s_last >= 0 ? s_last : c0);
 }
 
 // 2. Decide each sequence of the group; sum the draw's weights over a chunk.
