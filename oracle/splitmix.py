@@ -50,35 +50,55 @@ class SplitMix64:
         return z ^ (z >> 31)
 
 
-def free_list_order(num_blocks, alloc_seed):
-    """Order in which a fresh pool hands out its blocks (first element first)."""
-    order = list(range(num_blocks))
-    if alloc_seed == 0:
-        return order
-    g = SplitMix64(alloc_seed)
-    for i in range(num_blocks - 1, 0, -1):
-        j = g.next() % (i + 1)
+def fisher_yates(n, draw):
+    """Shuffle of [0, n): for i from n-1 down to 1, j = draw() mod (i+1),
+    swap positions i and j.  ``draw`` returns 64-bit unsigned integers."""
+    order = list(range(n))
+    for i in range(n - 1, 0, -1):
+        j = draw() % (i + 1)
         order[i], order[j] = order[j], order[i]
     return order
 
 
+def free_list_order(num_blocks, alloc_seed):
+    """Order in which a fresh pool hands out its blocks (first element first)."""
+    if alloc_seed == 0:
+        return list(range(num_blocks))
+    return fisher_yates(num_blocks, SplitMix64(alloc_seed).next)
+
+
+def box_muller(x1, x2):
+    """Two N(0,1) values (float64) from two 64-bit outputs:
+    u1 = ((x1 >> 11) + 1) 2^-53 in (0, 1], u2 = (x2 >> 11) 2^-53 in [0, 1),
+    rho = sqrt(-2 ln u1); returns (rho cos 2 pi u2, rho sin 2 pi u2)."""
+    u1 = ((x1 >> 11) + 1) * 2.0 ** -53
+    u2 = (x2 >> 11) * 2.0 ** -53
+    rho = math.sqrt(-2.0 * math.log(u1))
+    return rho * math.cos(2.0 * math.pi * u2), rho * math.sin(2.0 * math.pi * u2)
+
+
+def codec_draws_stream(d, draw):
+    """Rotation signs D and QJL matrix S from a stream of 64-bit outputs: d
+    outputs for the signs (top bit set -> -1), then pairs for S in row-major
+    order, each Box-Muller value rounded to float32."""
+    signs = np.empty(d, dtype=np.int8)
+    for i in range(d):
+        signs[i] = -1 if (draw() >> 63) else 1
+    flat = np.empty(d * d, dtype=np.float32)
+    for t in range(0, d * d, 2):
+        x1 = draw()
+        x2 = draw()
+        a, b = box_muller(x1, x2)
+        flat[t] = np.float32(a)
+        flat[t + 1] = np.float32(b)
+    return signs, flat.reshape(d, d)
+
+
 def codec_draws(d, codec_seed):
-    """Rotation signs D (int8 +-1, length d) and QJL matrix S (float32, d x d).
+    """Rotation signs D (int8 +-1, length d) and QJL matrix S (float32, d x d)
+    from SplitMix64 seeded with the codec seed.
 
     Scalar ``math`` calls are used on purpose: one value at a time, as the
     definition reads.
     """
-    g = SplitMix64(codec_seed)
-    signs = np.empty(d, dtype=np.int8)
-    for i in range(d):
-        signs[i] = -1 if (g.next() >> 63) else 1
-    flat = np.empty(d * d, dtype=np.float32)
-    for t in range(0, d * d, 2):
-        x1 = g.next()
-        x2 = g.next()
-        u1 = ((x1 >> 11) + 1) * 2.0 ** -53
-        u2 = (x2 >> 11) * 2.0 ** -53
-        rho = math.sqrt(-2.0 * math.log(u1))
-        flat[t] = np.float32(rho * math.cos(2.0 * math.pi * u2))
-        flat[t + 1] = np.float32(rho * math.sin(2.0 * math.pi * u2))
-    return signs, flat.reshape(d, d)
+    return codec_draws_stream(d, SplitMix64(codec_seed).next)

@@ -200,11 +200,156 @@ def test_splitmix64_reference_outputs(golden):
         assert g.next() == int(row[0], 16)
 
 
+# Pins of the seeded draws.  Each takes the function under test, so that the
+# planted mistakes below can be run through the same pins.
+
+GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+
+
+def _pin_fisher_yates_scripted(fy):
+    # hand-worked Fisher-Yates over [0, 5) with scripted draws 7, 7, 7, 7:
+    # i=4: 7 mod 5 = 2, swap 4,2 -> 0 1 4 3 2; i=3: 7 mod 4 = 3, stays;
+    # i=2: 7 mod 3 = 1, swap 2,1 -> 0 4 1 3 2; i=1: 7 mod 2 = 1, stays
+    it = iter([7, 7, 7, 7])
+    assert fy(5, lambda: next(it)) == [0, 4, 1, 3, 2]
+    # draws 1, 2, 3, 4: i=4: 1 mod 5 = 1 -> 0 4 2 3 1; i=3: 2 mod 4 = 2 ->
+    # 0 4 3 2 1; i=2: 3 mod 3 = 0 -> 3 4 0 2 1; i=1: 4 mod 2 = 0 -> 4 3 0 2 1
+    it = iter([1, 2, 3, 4])
+    assert fy(5, lambda: next(it)) == [4, 3, 0, 2, 1]
+
+
+def _pin_free_list_golden(fy):
+    # seeded with the golden gamma, SplitMix64's state after its first step is
+    # that of seed 0 after one output, so the shuffle draws the golden outputs
+    # 2..4 of seed 0: j = 0x...65f4 mod 4 = 0 (last hex digit 4), then
+    # 0x06c45d188009454f mod 3 = 1 (16 = 1 mod 3, hex digit sum 94), then
+    # 0x...81ec mod 2 = 0: 0 1 2 3 -> 3 1 2 0 -> 3 2 1 0 -> 2 3 1 0
+    assert fy(4, splitmix.SplitMix64(GOLDEN_GAMMA).next) == [2, 3, 1, 0]
+
+
+def _pin_box_muller_closed_forms(bm):
+    top = (1 << 64) - 1
+    # u1 = 1 exactly (the +1 keeps u1 in (0, 1]): rho = 0
+    assert bm(top, 0) == (0.0, 0.0)
+    # u1 = 2^-53, u2 = 0: (sqrt(-2 ln 2^-53), 0) = (sqrt(106 ln 2), 0)
+    a, b = bm(0, 0)
+    assert abs(a - math.sqrt(106.0 * math.log(2.0))) <= 1e-12 and b == 0.0
+    # u1 = 1/2 (x1 >> 11 = 2^52 - 1), u2 = 1/4: a quarter turn, (0, sqrt(2 ln 2))
+    r = math.sqrt(2.0 * math.log(2.0))
+    a, b = bm((1 << 63) - (1 << 11), 1 << 62)
+    assert abs(a) <= 1e-15 and abs(b - r) <= 1e-15
+    # u2 = 1/2: a half turn, (-sqrt(2 ln 2), 0)
+    a, b = bm((1 << 63) - (1 << 11), 1 << 63)
+    assert abs(a + r) <= 1e-15 and abs(b) <= 1e-15
+
+
+def _pin_codec_draws_scripted(cd):
+    # d = 2: two sign outputs (top bit set and clear, low bits the other way
+    # round), then the pairs of S in row-major order: (u1 = 1/2, u2 = 1/4) for
+    # row 0, (u1 = 1, u2 = 0) for row 1
+    top = (1 << 64) - 1
+    it = iter([1 << 63, 1, (1 << 63) - (1 << 11), 1 << 62, top, 0])
+    signs, s = cd(2, lambda: next(it))
+    assert signs.tolist() == [-1, 1]
+    assert abs(float(s[0, 0])) <= 1e-15
+    assert s[0, 1] == np.float32(math.sqrt(2.0 * math.log(2.0)))
+    assert s[1, 0] == 0.0 and s[1, 1] == 0.0
+
+
+def _pin_codec_signs_golden(cd):
+    # the top bits of the golden outputs of seed 0: 0xe2.., 0x6e.., 0x06.., 0xf8..
+    signs, _ = cd(4, splitmix.SplitMix64(0).next)
+    assert signs.tolist() == [-1, 1, 1, -1]
+
+
 def test_free_list_order():
     assert splitmix.free_list_order(10, 0) == list(range(10))
     perm = splitmix.free_list_order(1000, 77)
     assert sorted(perm) == list(range(1000)) and perm != list(range(1000))
     assert splitmix.free_list_order(1000, 77) == perm
+    _pin_fisher_yates_scripted(splitmix.fisher_yates)
+    _pin_free_list_golden(splitmix.fisher_yates)
+    assert splitmix.free_list_order(4, GOLDEN_GAMMA) == [2, 3, 1, 0]
+
+
+def test_codec_draws_pins():
+    _pin_box_muller_closed_forms(splitmix.box_muller)
+    _pin_codec_draws_scripted(splitmix.codec_draws_stream)
+    _pin_codec_signs_golden(splitmix.codec_draws_stream)
+    signs, s = splitmix.codec_draws(4, 0)
+    assert signs.tolist() == [-1, 1, 1, -1]
+    # the first pair of S comes from the 5th and 6th outputs, row-major
+    g = splitmix.SplitMix64(0)
+    outs = [g.next() for _ in range(6)]
+    a, b = splitmix.box_muller(outs[4], outs[5])
+    assert s[0, 0] == np.float32(a) and s[0, 1] == np.float32(b)
+
+
+def _fy_mutant(kind):
+    def fy(n, draw):
+        order = list(range(n))
+        steps = range(1, n) if kind == "upward" else range(n - 1, 0, -1)
+        for i in steps:
+            j = draw() % (i if kind == "mod_i" else i + 1)
+            order[i], order[j] = order[j], order[i]
+        return order
+
+    return fy
+
+
+def _bm_mutant(kind):
+    def bm(x1, x2):
+        u1 = ((x1 >> 11) + (0 if kind == "no_plus_one" else 1)) * 2.0 ** -53
+        u2 = (x2 >> 11) * 2.0 ** -53
+        rho = math.sqrt(-2.0 * math.log(u1)) if u1 > 0 else math.inf
+        c, sn = math.cos(2.0 * math.pi * u2), math.sin(2.0 * math.pi * u2)
+        return (rho * sn, rho * c) if kind == "cos_sin_swapped" else (rho * c, rho * sn)
+
+    return bm
+
+
+def _cd_mutant(kind):
+    bm = _bm_mutant(kind)
+
+    def cd(d, draw):
+        signs = np.empty(d, dtype=np.int8)
+        for i in range(d):
+            x = draw()
+            signs[i] = -1 if ((x & 1) if kind == "low_bit_sign" else (x >> 63)) else 1
+        flat = np.empty(d * d, dtype=np.float32)
+        for t in range(0, d * d, 2):
+            x1, x2 = draw(), draw()
+            with np.errstate(all="ignore"):
+                a, b = bm(x1, x2)
+                flat[t], flat[t + 1] = np.float32(a), np.float32(b)
+        s = flat.reshape(d, d)
+        return signs, (s.T.copy() if kind == "column_major" else s)
+
+    return cd
+
+
+@pytest.mark.parametrize("kind", ["mod_i", "upward"])
+def test_free_list_pins_catch_planted_mistake(kind):
+    bad = _fy_mutant(kind)
+    caught = []
+    for pin in (_pin_fisher_yates_scripted, _pin_free_list_golden):
+        try:
+            pin(bad)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the '{kind}' mistake"
+
+
+@pytest.mark.parametrize("kind", ["low_bit_sign", "cos_sin_swapped", "no_plus_one", "column_major"])
+def test_codec_draw_pins_catch_planted_mistake(kind):
+    caught = []
+    for pin, fn in ((_pin_box_muller_closed_forms, _bm_mutant(kind)), (_pin_codec_draws_scripted, _cd_mutant(kind)),
+                    (_pin_codec_signs_golden, _cd_mutant(kind))):
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the '{kind}' mistake"
 
 
 def test_codec_draw_statistics():
