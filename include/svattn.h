@@ -27,7 +27,12 @@
  * Conventions for every entry point:
  *  - Every function returns an int status: KV_OK (0) or a negative KV_E*
  *    code.  Arguments are validated on the host before anything is enqueued;
- *    a call that fails changes no state (host or device) and enqueues no work.
+ *    a call that fails validation changes no state (host or device) and
+ *    enqueues no work.  A call whose kernel launch fails (KV_EDEVICE) after
+ *    some of its work was enqueued leaves the host state (lengths, tables,
+ *    free list) unchanged too; the work already enqueued writes only
+ *    positions past the committed lengths, table entries past the committed
+ *    blocks, and the call's outputs, so a retry reads nothing it wrote.
  *    kv_last_error() gives a message for the last failure on a handle.
  *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).  All
  *    device work of a call is enqueued on it; no call waits for the device
@@ -239,6 +244,18 @@ int kv_encode(const kv_cache* c, int64_t n_vecs, const float* src, int32_t is_ke
 int kv_record_bytes(int32_t head_dim, int32_t is_key, int32_t* out);
 
 /*
+ * Device status bits of a handle (KV_TQ3 encoders set them; see kv_encode
+ * and kv_append): KV_STATUS_NORM_SATURATED when some vector's norm (or key
+ * residual norm) exceeded 65504 and was stored as 65504, the largest finite
+ * fp16 value.  Reads the word after the work enqueued on `stream` so far
+ * (waits for that stream), stores it in *out, and clears it first if clear
+ * is non-zero (with a fill kernel, no memset).  Errors: KV_EINVAL,
+ * KV_EDEVICE.
+ */
+#define KV_STATUS_NORM_SATURATED 1u
+int kv_read_status(kv_cache* c, uint32_t* out, int32_t clear, void* stream);
+
+/*
  * Workspace bytes spec_verify_attn needs for this call shape (same arguments
  * as spec_verify_attn).  Errors as spec_verify_attn's validation.
  */
@@ -265,6 +282,11 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  *    must be ordered on one stream.
  * KV_TQ3: queries are rotated in the kernel path (q' = Pi q, q'' = S q'),
  * scores use the stored codes and norms, and the output is rotated back.
+ * Precision: products accumulate in fp32.  KV_FP32 multiplies in fp32;
+ * KV_BF16 multiplies the stored bf16 K/V by the query and by the softmax
+ * weights, each carried as two bf16 parts (hi + lo, about 2^-17 relative);
+ * KV_TQ3 multiplies the exact fp16 code levels and signs by fp16 parts of
+ * q', q'' and the weights.
  * Errors: KV_ENOSEQ, KV_EINVAL, KV_ERANGE (n_rows > seq_len), KV_ENOMEM
  * (workspace too small), KV_EDEVICE.
  */
@@ -359,6 +381,20 @@ const char* spec_accept_last_error(void);
  * without the merge.  Passing NULL for both stops the recording.
  */
 int kv_trace_events(kv_cache* c, void* before, void* after);
+
+/*
+ * Streaming-read probe (measurement aid, not part of the attention path):
+ * reads the `bytes` bytes at src once, every wave loading 1 KiB of
+ * consecutive memory per step with 16-byte loads from every compute unit,
+ * and folds them into one word per workgroup in sink so that no load is
+ * elided.  Its duration measures the read bandwidth that a perfect
+ * single-pass reader of a cache of that size reaches on this GPU.
+ *  src: device, 16-byte aligned; bytes: a multiple of 16.
+ *  sink: device, at least kv_stream_probe_sink_bytes() bytes.
+ * Errors: KV_EINVAL, KV_EDEVICE.
+ */
+int kv_stream_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+size_t kv_stream_probe_sink_bytes(void);
 
 /* ---- introspection (host only; touches the device only to apply pending
  * device rollbacks first) ---- */

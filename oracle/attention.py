@@ -69,6 +69,51 @@ def verify_attention(q, k, v, scale, softcap=0.0, window=0, return_weights=False
     return out
 
 
+def verify_attention_grouped(q, k, v, scale, softcap=0.0, window=0, return_weights=False):
+    """The same attention as ``verify_attention``, arranged per kv head: the
+    scores of all n rows and g query heads of kv head h against every key
+    some row can see form one matrix (a single matrix product), each row's
+    invisible keys are masked out explicitly, and each column goes through
+    its own max-subtracted softmax.  Nothing is blocked, fused or reordered
+    beyond that grouping, so each entry is the definition's value; it is
+    here because long sequences are too slow row by row.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n, hq, d = q.shape
+    L, hkv, _ = k.shape
+    assert L >= n and hq % hkv == 0
+    g = hq // hkv
+    first = L - n
+    lo = 0 if window == 0 else max(0, first - window + 1)
+    keys = np.arange(lo, L)
+    pos = first + np.arange(n)
+    vis = keys[None, :] <= pos[:, None]
+    if window > 0:
+        vis &= (pos[:, None] - keys[None, :]) < window
+    vis = np.repeat(vis, g, axis=0)  # row i * g + j: row i, query head h * g + j
+    out = np.zeros((n, hq, d), dtype=np.float64)
+    weights = {}
+    for h in range(hkv):
+        qh = q[:, h * g:(h + 1) * g, :].reshape(n * g, d)
+        # fp64 copies of one kv head at a time (the caller's arrays may be fp32)
+        kh = np.asarray(k[lo:, h, :], dtype=np.float64)
+        vh = np.asarray(v[lo:, h, :], dtype=np.float64)
+        s = scale * (qh @ kh.T)
+        if softcap > 0.0:
+            s = softcap * np.tanh(s / softcap)
+        s = np.where(vis, s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        w = e / e.sum(axis=1, keepdims=True)
+        out[:, h * g:(h + 1) * g, :] = (w @ vh).reshape(n, g, d)
+        if return_weights:
+            for r in range(n * g):
+                i, j = divmod(r, g)
+                weights[(i, h * g + j)] = (keys[vis[r]], w[r, vis[r]])
+    if return_weights:
+        return out, weights
+    return out
+
+
 def verify_attention_batch(qs, ks, vs, scale, softcap=0.0, window=0):
     """One call over several sequences: lists of per-sequence arrays."""
     return [verify_attention(q, k, v, scale, softcap, window) for q, k, v in zip(qs, ks, vs)]

@@ -11,9 +11,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# SVATTN_LIB may name another build of the same library (e.g. a variant
-# being measured); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("SVATTN_LIB") or os.path.join(PKG, "libsvattn.so")
+# the in-tree build, always (no environment override)
+LIB_PATH = os.path.join(PKG, "libsvattn.so")
 CORE_LIB_PATH = os.path.join(PKG, "libsvattn_core.so")
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_ERANGE, KV_ENOSEQ, KV_EDEVICE = 0, -1, -2, -3, -4, -5
@@ -105,6 +104,8 @@ _SIGS = {
     "spec_accept": [_i32, _i32p, _i32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_size_t, _p],
     "spec_accept_workspace_bytes": [_i32, _i32p, _i32, _i32, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)],
     "spec_accept_last_error": [],
+    "kv_read_status": [_p, ctypes.POINTER(ctypes.c_uint32), _i32, _p],
+    "kv_stream_probe": [_p, ctypes.c_size_t, _p, ctypes.c_size_t, _p],
 }
 
 _NGRAM_SIGS = {
@@ -141,6 +142,9 @@ def _bind(lib, sigs):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name.endswith("last_error") else ctypes.c_int
+    if hasattr(lib, "kv_stream_probe_sink_bytes"):
+        lib.kv_stream_probe_sink_bytes.argtypes = []
+        lib.kv_stream_probe_sink_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -309,6 +313,23 @@ def kv_codec(h, head_dim):
     _check(lib().kv_codec(h, signs.ctypes.data, s.ctypes.data, lev.ctypes.data, lev16.ctypes.data,
                           thr.ctypes.data), h)
     return signs, s, lev, lev16, thr
+
+
+def kv_read_status(h, clear=False, stream=None):
+    out = ctypes.c_uint32()
+    _check(lib().kv_read_status(h, ctypes.byref(out), 1 if clear else 0, _stream_ptr(stream)), h)
+    return out.value
+
+
+def kv_stream_probe_sink_bytes():
+    return lib().kv_stream_probe_sink_bytes()
+
+
+def kv_stream_probe(src, sink, stream=None):
+    """One streaming read of the device tensor src (its bytes) into sink."""
+    _check(lib().kv_stream_probe(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                 ctypes.c_void_p(sink.data_ptr()), sink.numel() * sink.element_size(),
+                                 _stream_ptr(stream)))
 
 
 def kv_last_error(h):
@@ -519,6 +540,10 @@ class KVCache:
 
     def codec(self):
         return kv_codec(self.handle, self.head_dim)
+
+    def read_status(self, clear=False, stream=None):
+        """The device status word (bit 0: a norm saturated at 65504)."""
+        return kv_read_status(self.handle, clear, stream)
 
 
 class NgramDrafter:

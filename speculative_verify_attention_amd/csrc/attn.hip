@@ -90,24 +90,33 @@ struct QOperand;
 template <int D>
 struct QOperand<1, D> {
   // bf16: the fragments live in LDS, shared by the workgroup's token lanes:
-  // k-step kk of lane (c, hh) = dims 16kk + 8hh .. +8 at lds[kk * 64 + lane].
+  // k-step kk of lane (c, hh) = dims 16kk + 8hh .. +8 at lds[kk * 64 + lane]
+  // (high part) and lds[(D/16 + kk) * 64 + lane] (low part).  The fp32 query
+  // is carried as two bf16 parts, q = hi + lo to ~2^-17 relative: the
+  // residual of a float after rounding to bf16 is exact in fp32, and two
+  // products per k-step keep the scores as close to fp32 queries as the
+  // probabilities' hi + lo split keeps the value sums.
+  static constexpr int LDS_ENTRIES = 2 * (D / 16) * 64;
   const u32x4_t* lds;
   // Written by one wave per column group.
   __device__ __forceinline__ static void store(u32x4_t* dst, const float* q, bool ok, int lane) {
     const int hh = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      bf16x8_t v{};
+      bf16x8_t vh{}, vl{};
       if (ok) {
         const f32x4_t a = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh);
         const f32x4_t b = *reinterpret_cast<const f32x4_t*>(q + 16 * kk + 8 * hh + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (__bf16)a[e];
-          v[4 + e] = (__bf16)b[e];
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? a[e] : b[e - 4];
+          const __bf16 h = (__bf16)x;
+          vh[e] = h;
+          vl[e] = (__bf16)(x - (float)h);
         }
       }
-      dst[kk * 64 + lane] = __builtin_bit_cast(u32x4_t, v);
+      dst[kk * 64 + lane] = __builtin_bit_cast(u32x4_t, vh);
+      dst[(D / 16 + kk) * 64 + lane] = __builtin_bit_cast(u32x4_t, vl);
     }
   }
 };
@@ -136,9 +145,12 @@ __device__ __forceinline__ f32x16_t qk_sub(const QOperand<1, D>& q, const TileRe
   const int lane = threadIdx.x & 63;
   f32x16_t s = {};
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b.k[st][kk]),
-                                                __builtin_bit_cast(bf16x8_t, q.lds[kk * 64 + lane]), s, 0, 0, 0);
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, b.k[st][kk]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, q.lds[kk * 64 + lane]), s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, q.lds[(D / 16 + kk) * 64 + lane]),
+                                                s, 0, 0, 0);
+  }
   return s;
 }
 template <int D>
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   constexpr int TILE_REGS = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4;
   constexpr int NBUF = TILE_REGS <= 64 ? SVATTN_NBUF : 1;
   __shared__ float cbuf[CombineBuf<D, NCT>::FLOATS];
-  __shared__ u32x4_t qlds[FMT == 1 ? NCT * (D / 16) * 64 : 1];
+  __shared__ u32x4_t qlds[FMT == 1 ? NCT * QOperand<1, D>::LDS_ENTRIES : 1];
 
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane makes the compiler see it, so
@@ -365,9 +377,9 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   const float* qsrc = a.q + ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
   QOperand<FMT, D> qop;
   if constexpr (FMT == 1) {
-    if (tl == 0) QOperand<1, D>::store(qlds + ct * (D / 16) * 64, qsrc, col_ok, lane);
+    if (tl == 0) QOperand<1, D>::store(qlds + ct * QOperand<1, D>::LDS_ENTRIES, qsrc, col_ok, lane);
     __syncthreads();
-    qop.lds = qlds + ct * (D / 16) * 64;
+    qop.lds = qlds + ct * QOperand<1, D>::LDS_ENTRIES;
   } else {
     if (col_ok)
       qop.load(qsrc, hh);

@@ -258,6 +258,11 @@ struct AcceptArgs {
   int32_t d0[kMaxAcceptSeqs];  // first draft row (relative to rows_t)
 };
 
+// ---- streaming-read probe ------------------------------------------------------------
+// Workgroups of the probe (8 per compute unit); the sink holds one word each.
+constexpr int kProbeWorkgroups = 2048;
+hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
 static_assert(sizeof(AcceptArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
 static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");

@@ -320,20 +320,16 @@ int kv_destroy(kv_cache* c) {
   return KV_OK;
 }
 
-int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k,
-              const void* v, void* stream) {
-  if (!c) return KV_EINVAL;
-  int rc = check_device(c);
-  if (rc != KV_OK) return rc;
-  AppendPlan plan;
-  std::vector<int32_t> slack = pending_slack(c, n_seqs, seq_ids);
-  rc = c->core.plan_append(n_seqs, seq_ids, n_new, &plan, &c->err, slack.data());
-  if (rc != KV_OK) return rc;
-  if (plan.total_rows > 0 && (!k || !v)) return set_err(c, KV_EINVAL, "null k / v");
-  if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// Enqueue a planned append (table updates, then the slice-update or
+// quantize-on-append launches) without committing it to the host state.
+int enqueue_append(kv_cache* c, const AppendPlan& plan, const std::vector<int32_t>& slack, const void* k,
+                   const void* v, hipStream_t s) {
   // 1. new blocks become visible in the device table
-  rc = enqueue_table_updates(c, plan, s);
+  int rc = enqueue_table_updates(c, plan, s);
   if (rc != KV_OK) return rc;
   // 2. slice-update / quantize-on-append, in launches of <= kMaxAppendSegs segments
   const CoreParams& P = c->core.params();
@@ -400,6 +396,26 @@ int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t
     hipError_t e = launch_append(a, s);
     if (e != hipSuccess) return hip_fail(c, e, "append launch");
   }
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_append(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k,
+              const void* v, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  AppendPlan plan;
+  std::vector<int32_t> slack = pending_slack(c, n_seqs, seq_ids);
+  rc = c->core.plan_append(n_seqs, seq_ids, n_new, &plan, &c->err, slack.data());
+  if (rc != KV_OK) return rc;
+  if (plan.total_rows > 0 && (!k || !v)) return set_err(c, KV_EINVAL, "null k / v");
+  if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
+  rc = enqueue_append(c, plan, slack, k, v, static_cast<hipStream_t>(stream));
+  if (rc != KV_OK) return rc;
   c->core.commit_append(plan);
   return KV_OK;
 }
@@ -473,6 +489,31 @@ int kv_encode(const kv_cache* cc, int64_t n_vecs, const float* src, int32_t is_k
   hipError_t e = launch_encode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(c, e, "encode launch");
   return KV_OK;
+}
+
+int kv_read_status(kv_cache* c, uint32_t* out, int32_t clear, void* stream) {
+  if (!c || !out) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, c->dstatus, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && clear) e = launch_fill_zero(reinterpret_cast<int32_t*>(c->dstatus), 1, s);
+  if (e != hipSuccess) return hip_fail(c, e, "reading the status word");
+  *out = word;
+  return KV_OK;
+}
+
+size_t kv_stream_probe_sink_bytes(void) { return (size_t)kProbeWorkgroups * 4; }
+
+int kv_stream_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (!src || !sink || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16 ||
+      sink_bytes < kv_stream_probe_sink_bytes() || bytes > ((size_t)1 << 40))
+    return KV_EINVAL;
+  hipError_t e = launch_stream_probe(src, (int64_t)bytes, static_cast<uint32_t*>(sink),
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV_OK : KV_EDEVICE;
 }
 
 }  // extern "C"
@@ -706,10 +747,16 @@ int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   const bool fused = P.format != KV_TQ3 && reinterpret_cast<uintptr_t>(k) % 16 == 0 &&
                      reinterpret_cast<uintptr_t>(v) % 16 == 0;  // the kernel reads rows in 16-byte pieces
   if (!fused) {
-    rc = kv_append(c, n_seqs, seq_ids, n_rows, k, v, stream);
+    // the append's launches, then the verify planned with the appended
+    // lengths; the host state moves only once both are enqueued
+    if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
+    rc = enqueue_append(c, plan, slack, k, v, s);
     if (rc != KV_OK) return rc;
-    return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out,
-                          workspace, s, nullptr, nullptr);
+    rc = enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, n_rows, q, num_q_heads, scale, softcap, window, out,
+                        workspace, s, nullptr, nullptr);
+    if (rc != KV_OK) return rc;
+    c->core.commit_append(plan);
+    return KV_OK;
   }
   rc = enqueue_table_updates(c, plan, s);
   if (rc != KV_OK) return rc;

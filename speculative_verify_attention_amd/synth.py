@@ -11,8 +11,8 @@ chunk, so any slice of a long sequence can be regenerated on its own:
 * the queries of step t: seeded by (seed, "query", t).
 
 Distributions follow each workload's recipe (N(0,1), optional per-kv-head
-scales), and values are rounded to the cache's storage type (bf16 caches get
-bf16 K/V; their queries are bf16-representable floats).
+scales), and K/V are rounded to the cache's storage type (bf16 caches get
+bf16 K/V); queries are plain fp32 draws for every format.
 
 The pages measure end to end on real models (AX Engine page, "Performance
 Evidence & Results"; SwiftLM page, long-context benchmark and test-suite
@@ -202,15 +202,12 @@ def step_kv(wl, step, n_total, device):
 
 
 def queries(wl, step, n_total, device, scale=1.0):
-    """Queries of step `step`: [n_total, hq, d] fp32 (bf16-representable for
-    bf16 caches)."""
+    """Queries of step `step`: [n_total, hq, d] fp32 N(0, scale^2), whatever
+    the cache format (the boundary takes fp32 queries)."""
     import torch
 
     g = _gen(device, wl.seed, _TAG["query"], step)
-    q = torch.randn((n_total, wl.hq, wl.d), generator=g, device=device, dtype=torch.float32) * scale
-    if wl.fmt == KV_BF16:
-        q = q.to(torch.bfloat16).to(torch.float32)
-    return q
+    return torch.randn((n_total, wl.hq, wl.d), generator=g, device=device, dtype=torch.float32) * scale
 
 
 # ---- inputs of the acceptance step -------------------------------------------------------

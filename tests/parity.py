@@ -29,7 +29,7 @@ def oracle_seq(runner, s, rows, q_host, layer):
     window, cap = runner.layers[layer]
     off = qoffsets(rows)
     k, v = runner.logical_kv(s)
-    return A.verify_attention(q_host[off[s]: off[s + 1]], k, v, wl.scale, cap, window)
+    return A.verify_attention_grouped(q_host[off[s]: off[s + 1]], k, v, wl.scale, cap, window)
 
 
 def max_err(runner, rows, q, out, layer, seqs):
@@ -226,7 +226,7 @@ def tq3_oracle_seq(runner, s, rows, q_host, layer):
     kd = tq3.decode_keys(ke["code"], ke["bits"], ke["n16"], ke["g16"], pi, s_mat, c16).reshape(L, wl.hkv, wl.d)
     vd = tq3.decode_values(ve["code"], ve["n16"], pi, c16).reshape(L, wl.hkv, wl.d)
     off = qoffsets(rows)
-    return A.verify_attention(q_host[off[s]: off[s + 1]], kd, vd, wl.scale, cap, window)
+    return A.verify_attention_grouped(q_host[off[s]: off[s + 1]], kd, vd, wl.scale, cap, window)
 
 
 def max_err_tq3(runner, rows, q, out, layer, seqs):

@@ -6,6 +6,7 @@ bytes are compared bit for bit.
 """
 
 import math
+import os
 import zlib
 
 import numpy as np
@@ -18,6 +19,8 @@ from speculative_verify_attention_amd import (KV_BF16, KV_EINVAL, KV_ENOMEM, KV_
 from speculative_verify_attention_amd.runner import Runner
 
 pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 TOL = {KV_FP32: 1e-5, KV_BF16: 2e-3}
 
@@ -33,12 +36,12 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def run_and_check(wl, seqs=None, layers=None, scale_q=1.0, steps=(0,), check_steps=None):
-    r = Runner(wl, layers=layers, track=True)
+def run_and_check(wl, seqs=None, layers=None, scale_q=1.0, steps=(0,), check_steps=None, fused=False, ring=False):
+    r = Runner(wl, layers=layers, track=True, ring=ring)
     r.fill()
     worst = 0.0
     for t in steps:
-        rows, q, outs = r.step(t, scale_q)
+        rows, q, outs = r.step(t, scale_q, fused=fused)
         torch.cuda.synchronize()
         if check_steps is None or t in check_steps:
             for li, out in enumerate(outs):
@@ -105,38 +108,115 @@ def test_qwen3_4b_reduced():
     assert err <= TOL[KV_BF16], err
 
 
-def test_qwen3_4b_full():
-    banner("qwen3-4b dense 16x4096 (bench launch shape)")
+def test_qwen3_4b_full_separate_calls():
+    banner("qwen3-4b dense 16x4096, kv_append + spec_verify_attn, every sequence")
     wl = synth.qwen3_4b_dense()
     _, err = run_and_check(wl)
     print(f"max abs err {err:.3e}", flush=True)
     assert err <= TOL[KV_BF16], err
 
 
-def test_gemma_interleaved_full():
-    banner("gemma 8x32768 window 512 + full, cap 50")
+def test_qwen3_4b_full_fused():
+    banner("qwen3-4b dense 16x4096, kv_append_verify (the bench's launch), every sequence")
+    wl = synth.qwen3_4b_dense()
+    _, err = run_and_check(wl, fused=True)
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+def test_gemma_interleaved_full_separate_calls():
+    banner("gemma 8x32768 window 512 + full, cap 50, separate calls")
     wl = synth.gemma_interleaved()
     _, err = run_and_check(wl, layers=[(512, 50.0), (0, 50.0)])
     print(f"max abs err {err:.3e}", flush=True)
     assert err <= TOL[KV_BF16], err
 
 
-def test_mixed_batch_steps():
-    banner("mixed batch 64 seqs, 20 steps with rollbacks, sampled sequences")
+def test_gemma_interleaved_full_fused_ring():
+    banner("gemma 8x32768, window layer on a ring cache + full layer, kv_append_verify (the bench's launch)")
+    wl = synth.gemma_interleaved()
+    _, err = run_and_check(wl, layers=[(512, 50.0), (0, 50.0)], fused=True, ring=True)
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL[KV_BF16], err
+
+
+class HostKV:
+    """Host copy of a bf16 cache's logical contents, kept step by step
+    (rollback = truncate, append = concatenate): the runner's own rebuild
+    regenerates every prefill, which is too slow to repeat at every step of
+    a 64-sequence batch."""
+
+    def __init__(self, wl):
+        self.k, self.v = [], []
+        for s, L in enumerate(wl.prefill):
+            k, v = synth.prefill_kv(wl, s, 0, L, "cuda")
+            self.k.append(k.cpu())
+            self.v.append(v.cpu())
+
+    def step(self, rb, rows, k, v):
+        k, v = k.cpu(), v.cpu()
+        off = 0
+        for s, (r, n) in enumerate(zip(rb, rows)):
+            L = self.k[s].shape[0] - r
+            self.k[s] = torch.cat([self.k[s][:L], k[off: off + n]])
+            self.v[s] = torch.cat([self.v[s][:L], v[off: off + n]])
+            off += n
+
+
+@pytest.mark.timeout(1500)
+def test_mixed_batch_every_sequence_every_step_fused():
+    banner("mixed batch 64 seqs, 20 steps with rollbacks, kv_append_verify, every sequence at every step")
+    from oracle import attention as A
+
     wl = synth.mixed_batch()
-    order = np.argsort(wl.prefill)
-    sample = sorted(set(order[:3].tolist() + order[-1:].tolist() + [7, 31]))
-    _, err = run_and_check(wl, seqs=sample, steps=range(20), check_steps={0, 19})
-    print(f"max abs err {err:.3e}", flush=True)
-    assert err <= TOL[KV_BF16], err
+    wl.steps = 20
+    r = Runner(wl)
+    r.fill()
+    host = HostKV(wl)
+    seqs = list(range(wl.n_seqs))
+    worst = 0.0
+    for t in range(20):
+        rb, rows = synth.step_plan(wl, t)
+        r.rollback(rb)
+        k, v = synth.step_kv(wl, t, sum(rows), "cuda")
+        q = synth.queries(wl, t, sum(rows), "cuda")
+        out = r.caches[0].append_verify(seqs, rows, k, v, q, wl.hq, wl.scale)
+        torch.cuda.synchronize()
+        host.step(rb, rows, k, v)
+        qh = q.double().cpu().numpy()
+        oh = out.double().cpu().numpy()
+        off = qoffsets(rows)
+        step_worst = 0.0
+        for s in seqs:
+            assert r.caches[0].seq_len(s) == host.k[s].shape[0]
+            ref = A.verify_attention_grouped(qh[off[s]: off[s + 1]], host.k[s].float().numpy(),
+                                             host.v[s].float().numpy(), wl.scale)
+            got = oh[off[s]: off[s + 1]]
+            assert np.all(np.isfinite(got)), (t, s)
+            step_worst = max(step_worst, float(np.max(np.abs(got - ref))))
+        worst = max(worst, step_worst)
+        print(f"step {t}: rows {sum(rows)}, max abs err {step_worst:.3e}", flush=True)
+    assert worst <= TOL[KV_BF16], worst
 
 
-def test_bf16_long_context_sampled():
-    banner("bf16 4x100000, sampled sequence 1")
+@pytest.mark.timeout(900)
+def test_bf16_long_context_every_sequence_fused():
+    banner("bf16 4x100000, kv_append_verify (the bench's launch), every sequence")
     wl = synth.tq3_long(100000, fmt=KV_BF16)
-    _, err = run_and_check(wl, seqs=[1])
+    _, err = run_and_check(wl, fused=True)
     print(f"max abs err {err:.3e}", flush=True)
     assert err <= TOL[KV_BF16], err
+
+
+def test_library_loaded_from_tree():
+    banner("the library mapped into this process is the in-tree build")
+    from speculative_verify_attention_amd import _binding
+
+    wl = synth.tiny()
+    Runner(wl).fill()
+    maps = open("/proc/self/maps").read()
+    assert _binding.LIB_PATH in maps
+    assert os.path.dirname(_binding.LIB_PATH) == os.path.join(ROOT, "speculative_verify_attention_amd")
 
 
 # ---- edge cases -----------------------------------------------------------------------
@@ -161,6 +241,11 @@ EDGE = [
     # one (sequence, kv head) pair split into more than 64 chunks: the merge
     # folds chunks past the wave's 64 lanes
     ("single_pair_long", 8, 1, 128, KV_BF16, [60000], [5], 0, 0.0, 1.0),
+    # sharp scores from fp32 queries that bf16 cannot represent (the kernel
+    # carries the query as two bf16 parts)
+    ("sharp_fp32_queries", 32, 8, 128, KV_BF16, [3000, 500], [5, 5], 0, 0.0, 4.0),
+    ("sharp_fp32_queries_d256", 8, 1, 256, KV_BF16, [2000], [5], 0, 0.0, 3.0),
+    ("sharp_fp32_queries_d64", 16, 4, 64, KV_BF16, [1500], [4], 0, 0.0, 5.0),
 ]
 
 

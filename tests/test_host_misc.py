@@ -17,15 +17,25 @@ def run_py(code, env=None):
 
 
 def test_missing_library_raises():
+    # the binding's library path pointed at a missing file, as on a tree
+    # where the library was never built
     r = run_py("import speculative_verify_attention_amd as s\n"
+               "from speculative_verify_attention_amd import _binding\n"
+               f"_binding.LIB_PATH = {os.path.join(ROOT, '_no_such_dir', 'libsvattn.so')!r}\n"
                "try:\n"
                "    s.KVCache(1, 64, 4, 1, 2, s.KV_FP32)\n"
                "except RuntimeError as e:\n"
                "    print('raised:', e)\n"
                "else:\n"
-               "    print('no error')\n",
-               env={"SVATTN_LIB": os.path.join(ROOT, "_no_such_dir", "libsvattn.so")})
+               "    print('no error')\n")
     assert "raised:" in r.stdout and "not built" in r.stdout, r.stdout
+
+
+def test_library_path_is_in_tree():
+    sys.path.insert(0, ROOT)
+    from speculative_verify_attention_amd import _binding
+
+    assert _binding.LIB_PATH == os.path.join(ROOT, "speculative_verify_attention_amd", "libsvattn.so")
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -235,3 +235,32 @@ def test_pins_catch_planted_mistake(kind):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the '{kind}' mistake"
+
+
+# ---- the grouped arrangement (one matrix product per kv head) --------------------------
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_grouped_meets_every_pin(pin):
+    pin(A.verify_attention_grouped)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_grouped_equals_row_by_row(seed):
+    rng = np.random.default_rng(500 + seed)
+    hkv = int(rng.integers(1, 4))
+    g = int(rng.integers(1, 6))
+    n = int(rng.integers(1, 9))
+    L = n + int(rng.integers(0, 300))
+    d = int(rng.choice([8, 16, 64]))
+    window = int(rng.choice([0, 1, 3, 17, 400]))
+    cap = float(rng.choice([0.0, 0.7, 30.0]))
+    q, k, v = rand_case(L, n, hkv * g, hkv, d, rng)
+    scale = float(rng.uniform(0.05, 2.0))
+    a, wa = A.verify_attention(q, k, v, scale, cap, window, return_weights=True)
+    b, wb = A.verify_attention_grouped(q, k, v, scale, cap, window, return_weights=True)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    assert wa.keys() == wb.keys()
+    for key in wa:
+        assert np.array_equal(wa[key][0], wb[key][0])
+        assert np.allclose(wa[key][1], wb[key][1], rtol=0, atol=1e-13)
