@@ -479,7 +479,7 @@ def stream_probe(nbytes=2 << 30, runs=10):
     torch.cuda.empty_cache()
     return {"gbs_median": round(nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9, 1),
             "gbs_best": round(nbytes / (ms[0] * 1e-3) / 1e9, 1), "bytes": nbytes, "runs": runs,
-            "kernel": "kv_stream_probe (16-byte loads, 1 KiB per wave per step, 8 steps in flight)"}
+            "kernel": "kv_stream_probe (a contiguous chunk per workgroup, 16-byte loads, 16 steps in flight)"}
 
 
 def with_probe(res, probe):

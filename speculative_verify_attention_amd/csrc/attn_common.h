@@ -65,19 +65,18 @@ struct ColState {
 
 // Online-softmax update of one tile's scores p (log2 units, -inf = masked):
 // row maxima over the two half-waves, lazy move of the reference max (only
-// when the tile max exceeds it by more than 2^8, so probabilities stay below
-// 256 and rescales are rare), then p <- 2^(p - m) and the running sum.
+// when the tile max exceeds it by more than tau, 8 by default, so
+// probabilities stay below 2^tau and rescales are rare), then
+// p <- 2^(p - m) and the running sum.
 template <int D, int NSUB>
-__device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB][16]) {
+__device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB][16], float tau = 8.0f) {
   float mt = NEG_INF;
 #pragma unroll
   for (int st = 0; st < NSUB; ++st)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
   mt = fmaxf(mt, xor32(mt));
-  // move the reference only when the tile max exceeds it by more than 2^8,
-  // so probabilities stay below 256 and rescales are rare
-  const bool up = mt > cs.m + 8.0f;
+  const bool up = mt > cs.m + tau;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
     // lanes that move: alpha = 2^(m_old - m_new), 0 when nothing was seen yet;
     // lanes that stay keep alpha = 1 (their m may still be -inf)

@@ -11,35 +11,34 @@
 // in the rotated frame with their norm folded into the probability, and the
 // merge rotates the result back (o = Pi^T o').
 //
+// Precision.  The code levels c16 and the signs are exact in fp16; q', q''
+// and the probabilities are carried as two fp16 parts each (hi + lo, about
+// 2^-22 relative), so every product runs as two v_mfma_f32_32x32x16_f16 with
+// fp32 accumulation (48 matrix-core instructions per 32-key sub-tile).  One
+// part is not enough: its 2^-11 rounding of the query moves a peaked softmax
+// by about 1e-3.
+//
 // Layout and work split follow the plain kernel: one chunk of 32-key
-// sub-tiles of one (sequence, kv head) per workgroup, 4 token-lane waves,
-// keys as the MFMA M dimension.  Every wave-wide load reads contiguous
-// memory: 1 KiB per 4 key k-steps, 768 B per two value d-tiles, and the
-// 192-byte scales.  Codes become fp16 operands through two small LDS tables:
-// one byte of key nibbles -> (2 levels, 2 signs), 6 bits of value codes ->
-// 2 levels.  Products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation;
-// in precise mode q', q'' and the probabilities are each split into two fp16
-// parts (hi + lo, ~2^-22 relative) while the code levels and signs are exact
-// in fp16.
+// sub-tiles of one (sequence, kv head) per workgroup, eight waves (two per
+// SIMD, so that one wave's table reads and matrix-core latency hide behind
+// the other's work), keys as the MFMA M dimension.  Every wave-wide load
+// reads contiguous memory: 1 KiB per 4 key k-steps, 768 B per two value
+// d-tiles, and the 192-byte scales.  Codes become fp16 operands through two
+// small LDS tables: one byte of key nibbles -> (2 levels, 2 signs), 6 bits of
+// value codes -> 2 levels.
 #include <hip/hip_runtime.h>
 
 #include "attn_common.h"
 #include "kernels.h"
 
-// Query-fragment parts held in registers and depth of the sub-tile ring,
-// for one-part (fast) and two-part (precise) products; the rest of the
-// fragments are read from LDS (register budget of two waves per SIMD).
-#ifndef SVATTN_TQ3_QREGS_FAST
-#define SVATTN_TQ3_QREGS_FAST 2
+// Query-fragment parts held in registers (the others are read from LDS at
+// every use: the register budget of two waves per SIMD) and the depth of the
+// sub-tile ring.
+#ifndef SVATTN_TQ3_QREGS
+#define SVATTN_TQ3_QREGS 1
 #endif
-#ifndef SVATTN_TQ3_NBUF_FAST
-#define SVATTN_TQ3_NBUF_FAST 2
-#endif
-#ifndef SVATTN_TQ3_QREGS_PRECISE
-#define SVATTN_TQ3_QREGS_PRECISE 1
-#endif
-#ifndef SVATTN_TQ3_NBUF_PRECISE
-#define SVATTN_TQ3_NBUF_PRECISE 3
+#ifndef SVATTN_TQ3_NBUF
+#define SVATTN_TQ3_NBUF 2
 #endif
 // Waves per workgroup (one workgroup per CU: the tables fill the LDS).
 #ifndef SVATTN_TQ3_WAVES
@@ -171,11 +170,11 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
 //    (a single copy puts entries e and e + 32 on one bank), and per-wave
 //    scale slices.
 // The combine buffer reuses the key table and fragments after the loop.
-template <int D, int NCT, int P2>
+template <int D, int NCT>
 struct TQ3Smem {
   static constexpr int NW = SVATTN_TQ3_WAVES;
   static constexpr int TL = NW / NCT;
-  static constexpr int NPART = 2 * P2;  // q' hi, q'' hi (, q' lo, q'' lo)
+  static constexpr int NPART = 4;  // q' hi, q'' hi, q' lo, q'' lo
   // below 64 KiB: value table, scale slices, query fragments; the key table
   // fills the next 64 KiB, so that a key-table address is one byte permute
   // of (slot, code byte, 1) and every other address fits an instruction's
@@ -204,9 +203,9 @@ __device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, in
 
 // Query fragments of one lane: the leading NREG parts in registers, the
 // others read from LDS at every use.
-template <int D, int P2>
+template <int D>
 struct QFrags {
-  static constexpr int NREG = P2 == 1 ? SVATTN_TQ3_QREGS_FAST : SVATTN_TQ3_QREGS_PRECISE;
+  static constexpr int NREG = SVATTN_TQ3_QREGS;
   static constexpr int NR = NREG > 0 ? NREG : 1;
   f16x8_t f[NR][D / 16];
   const uint8_t* qf;
@@ -227,8 +226,8 @@ struct QFrags {
   }
 };
 
-template <int D, int P2, bool CAP>
-__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const QFrags<D, P2>& qr,
+template <int D, bool CAP>
+__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const QFrags<D>& qr,
                                             const uint8_t* __restrict__ lds, const uint32_t* __restrict__ vlut,
                                             uint32_t* scl, const AttnArgs& a, int key0, int L, int n, int ppos,
                                             int lane, uint32_t kslot) {
@@ -273,10 +272,8 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     const f16x8_t km = __builtin_bit_cast(f16x8_t, mse[kk & 1]), kq = __builtin_bit_cast(f16x8_t, qjl[kk & 1]);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(0, kk), s1, 0, 0, 0);
     s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(1, kk), s2, 0, 0, 0);
-    if constexpr (P2 == 2) {
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(2, kk), s1, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(3, kk), s2, 0, 0, 0);
-    }
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(2, kk), s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(3, kk), s2, 0, 0, 0);
   }
   // scores in log2 units (q'' already carries the QJL coefficient relative
   // to the first term)
@@ -287,8 +284,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     scale_words(1, gw);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f));
-      if constexpr (P2 == 2) x *= a.q1_mul;  // one-part fragments carry it already
+      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f)) * a.q1_mul;
       if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
       p[0][r] = x;
     }
@@ -307,7 +303,17 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
       if (kp >= L) vw[r >> 1] &= (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
     }
   }
-  softmax_update<D, 1>(cs, p);
+  // The probabilities carry the value norms into fp16 products: they may
+  // reach the lazy reference's 2^8 only while every value norm of the
+  // sub-tile is at most 240, else the reference moves to the sub-tile's
+  // maximum (probabilities <= 1), so that p * n16v stays finite.
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t nv2 = __builtin_bit_cast(f16x2_t, vw[0]);
+#pragma unroll
+  for (int q = 1; q < 8; ++q) nv2 = __builtin_elementwise_max(nv2, __builtin_bit_cast(f16x2_t, vw[q]));
+  float nvmax = fmaxf((float)nv2[0], (float)nv2[1]);
+  nvmax = fmaxf(nvmax, xor32(nvmax));
+  softmax_update<D, 1>(cs, p, nvmax <= 240.0f ? 8.0f : 0.0f);
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -315,19 +321,11 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int r = 8 * v + e;
-      if constexpr (P2 == 2) {
-        const u32x2_t sp = split_f16_pair(p[0][r] * half_at(vw, r), p[0][r + 1] * half_at(vw, r + 1));
-        phw[e / 2] = sp[0];
-        plw[e / 2] = sp[1];
-      } else {
-        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-        phw[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)fmaf(p[0][r], half_at(vw, r), 0.0f),
-                                                          (_Float16)fmaf(p[0][r + 1], half_at(vw, r + 1), 0.0f)});
-      }
+      const u32x2_t sp = split_f16_pair(p[0][r] * half_at(vw, r), p[0][r + 1] * half_at(vw, r + 1));
+      phw[e / 2] = sp[0];
+      plw[e / 2] = sp[1];
     }
-    const f16x8_t phi = __builtin_bit_cast(f16x8_t, phw);
-    f16x8_t plo{};
-    if constexpr (P2 == 2) plo = __builtin_bit_cast(f16x8_t, plw);
+    const f16x8_t phi = __builtin_bit_cast(f16x8_t, phw), plo = __builtin_bit_cast(f16x8_t, plw);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const uint32_t* w3 = t.vc[dt >> 1];
@@ -342,19 +340,19 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
       for (int q = 0; q < 4; ++q) vv[q] = vlut[((g >> (6 * q)) & 63) << 5];
       const f16x8_t vop = __builtin_bit_cast(f16x8_t, vv);
       cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, phi, cs.acc[dt], 0, 0, 0);
-      if constexpr (P2 == 2) cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
+      cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
     }
   }
 }
 
-template <int D, int NCT, int P2, bool CAP>
+template <int D, int NCT, bool CAP>
 __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArgs a) {
-  using SM = TQ3Smem<D, NCT, P2>;
+  using SM = TQ3Smem<D, NCT>;
   constexpr int NW = SM::NW;
   constexpr int TL = SM::TL;
   constexpr int NDT = D / 32;
   constexpr int SB = tq3_sub_bytes(D);
-  constexpr int NBUF = P2 == 1 ? SVATTN_TQ3_NBUF_FAST : SVATTN_TQ3_NBUF_PRECISE;
+  constexpr int NBUF = SVATTN_TQ3_NBUF;
   __shared__ __align__(16) uint8_t smem[SM::BYTES];
   uint8_t* klut = smem + SM::KLUT_OFF;
   float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF);
@@ -428,41 +426,31 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
         const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
         const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
         const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
-        // one-part fragments also carry the score multiplier (fp16 rounds
-        // relative to the value, so this costs no precision); two-part ones
-        // do not, which keeps their low-order parts out of the fp16
+        // the score multiplier is applied to the scores, not to the
+        // fragments: that keeps the low-order parts out of the fp16
         // subnormal range
-        const float m1 = P2 == 1 ? a.q1_mul : 1.0f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float xa = (e < 4 ? x0[e] : x1[e - 4]) * m1, xb = (e < 4 ? x0[e + 1] : x1[e - 3]) * m1;
-          const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul * m1;
-          const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul * m1;
-          if constexpr (P2 == 2) {
-            const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
-            h1[e / 2] = sx[0];
-            l1[e / 2] = sx[1];
-            h2[e / 2] = sy[0];
-            l2[e / 2] = sy[1];
-          } else {
-            typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-            h1[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)xa, (_Float16)xb});
-            h2[e / 2] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)ya, (_Float16)yb});
-          }
+          const float xa = e < 4 ? x0[e] : x1[e - 4], xb = e < 4 ? x0[e + 1] : x1[e - 3];
+          const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
+          const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul;
+          const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
+          h1[e / 2] = sx[0];
+          l1[e / 2] = sx[1];
+          h2[e / 2] = sy[0];
+          l2[e / 2] = sy[1];
         }
       }
       *reinterpret_cast<u32x4_t*>(qf + (0 * (D / 16) + kk) * 1024 + lane * 16) = h1;
       *reinterpret_cast<u32x4_t*>(qf + (1 * (D / 16) + kk) * 1024 + lane * 16) = h2;
-      if constexpr (P2 == 2) {
-        *reinterpret_cast<u32x4_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
-        *reinterpret_cast<u32x4_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
-      }
+      *reinterpret_cast<u32x4_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
+      *reinterpret_cast<u32x4_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
     }
   }
   const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
   __syncthreads();
 
-  QFrags<D, P2> qr;
+  QFrags<D> qr;
   qr.init(qf, lane);
   ColState<D> cs;
   cs.m = NEG_INF;
@@ -481,7 +469,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   auto stage = [&](int k, const TQ3Regs<D>& b) { scl[(k & 1) * 48 + sl] = b.sc; };
   auto step = [&](int k, const TQ3Regs<D>& cur, const TQ3Regs<D>& next) {
     __builtin_amdgcn_wave_barrier();
-    process_tq3<D, P2, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
+    process_tq3<D, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
                             (tlo + t_first + k * TL) * 32, L, n, ppos, lane, kslot);
     stage(k + 1, next);
     __builtin_amdgcn_wave_barrier();
@@ -511,28 +499,20 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
 }
 
 template <int D, int NCT>
-static hipError_t launch_tq3_dn(const AttnArgs& a, bool precise, hipStream_t s) {
-  const bool cap = a.softcap > 0.0f;
+static hipError_t launch_tq3_dn(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_wg), block(SVATTN_TQ3_WAVES * 64);
-  if (precise) {
-    if (cap)
-      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 2, false>), grid, block, 0, s, a);
-  } else {
-    if (cap)
-      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 1, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, 1, false>), grid, block, 0, s, a);
-  }
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_tq3(const AttnArgs& a, int nct, bool precise, hipStream_t s) {
+hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s) {
   if (a.n_wg <= 0) return hipSuccess;
   const int d = a.lay.d;
-  if (d == 64) return nct == 1 ? launch_tq3_dn<64, 1>(a, precise, s) : launch_tq3_dn<64, 2>(a, precise, s);
-  if (d == 128) return nct == 1 ? launch_tq3_dn<128, 1>(a, precise, s) : launch_tq3_dn<128, 2>(a, precise, s);
+  if (d == 64) return nct == 1 ? launch_tq3_dn<64, 1>(a, s) : launch_tq3_dn<64, 2>(a, s);
+  if (d == 128) return nct == 1 ? launch_tq3_dn<128, 1>(a, s) : launch_tq3_dn<128, 2>(a, s);
   return hipErrorInvalidValue;
 }
 

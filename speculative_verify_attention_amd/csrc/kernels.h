@@ -259,8 +259,8 @@ struct AcceptArgs {
 };
 
 // ---- streaming-read probe ------------------------------------------------------------
-// Workgroups of the probe (8 per compute unit); the sink holds one word each.
-constexpr int kProbeWorkgroups = 2048;
+// Workgroups of the probe (4 per compute unit); the sink holds one word each.
+constexpr int kProbeWorkgroups = 1024;
 hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
@@ -270,10 +270,10 @@ static_assert(sizeof(TableUpdateArgs) <= 4096, "kernel arguments must fit the 4 
 
 hipError_t launch_attn(const AttnArgs& a, int nct, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s);
-// TQ3: the query rotation, and the partial kernel with two-part (hi + lo)
-// fp16 operands when precise, one fp16 part otherwise.
+// TQ3: the query rotation, and the partial kernel (two-part (hi + lo) fp16
+// operands).
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
-hipError_t launch_attn_tq3(const AttnArgs& a, int nct, bool precise, hipStream_t s);
+hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s);
 // Acceptance: row statistics over every row (once per call), then decide and
 // draw for one group of up to kMaxAcceptSeqs sequences.
 hipError_t launch_accept_stats(const AcceptArgs& a, hipStream_t s);

@@ -1,8 +1,7 @@
 // probe.hip - streaming-read probe: the read bandwidth a single pass over a
 // buffer reaches on this GPU, as a ceiling to compare the attention kernels'
-// effective bandwidth with.  Each wave reads 1 KiB of consecutive memory per
-// step (16 bytes per lane), UNROLL steps in flight, grid-strided over the
-// buffer; the words are xor-folded so that no load is dead.
+// effective bandwidth with.  The words read are xor-folded so that no load
+// is dead.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -13,20 +12,26 @@ namespace svattn {
 
 typedef uint32_t pu32x4_t __attribute__((ext_vector_type(4)));
 
+// Workgroup w reads the w-th of kProbeWorkgroups contiguous chunks of the
+// buffer; its 256 threads read consecutive 16-byte pieces, UNROLL steps of
+// 4 KiB in flight, so each wave streams 1 KiB per step through its own
+// DRAM pages.  The ragged end of a chunk is read with one bounded step.
 template <int UNROLL>
 __global__ __launch_bounds__(256) void stream_probe_kernel(const pu32x4_t* __restrict__ src, int64_t n16,
                                                            uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
   pu32x4_t acc = {0u, 0u, 0u, 0u};
-  for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+  int64_t i = lo + threadIdx.x;
+  for (; i + (UNROLL - 1) * 256 < hi; i += UNROLL * 256) {
     pu32x4_t x[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) x[u] = src[i + u * stride];
+    for (int u = 0; u < UNROLL; ++u) x[u] = src[i + u * 256];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= x[u];
   }
-  for (; i < n16; i += stride) acc ^= src[i];
+  for (; i < hi; i += 256) acc ^= src[i];
   uint32_t w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) w ^= __shfl_xor(w, o);
@@ -39,7 +44,7 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const pu32x4_t* __res
 hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s) {
   const int64_t n16 = bytes / 16;
   if (n16 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(stream_probe_kernel<8>, dim3(kProbeWorkgroups), dim3(256), 0, s,
+  hipLaunchKernelGGL(stream_probe_kernel<16>, dim3(kProbeWorkgroups), dim3(256), 0, s,
                      static_cast<const pu32x4_t*>(src), n16, sink);
   return hipGetLastError();
 }

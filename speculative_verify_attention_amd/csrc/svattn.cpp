@@ -53,11 +53,6 @@ constexpr size_t kAlign = 256;
 #ifndef SVATTN_WG_PER_CALL_D256
 #define SVATTN_WG_PER_CALL_D256 256
 #endif
-// TQ3 calls whose every row sees at least this many keys use one-part fp16
-// operands (two-part below it).
-#ifndef SVATTN_TQ3_FAST_KEYS
-#define SVATTN_TQ3_FAST_KEYS 65536
-#endif
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MetaLayout {
@@ -589,20 +584,9 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
   // TQ3: the rotated queries q' = Pi q and q'' = S q' live after the partials
   float* q1 = nullptr;
   float* q2 = nullptr;
-  bool precise = true;
   if (tq3) {
     q1 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes);
     q2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes + vp.q_bytes);
-    // two-part fp16 operands unless every row sees many keys (errors of the
-    // one-part products average out over the keys)
-    int min_keys = INT32_MAX;
-    for (int i = 0; i < n_seqs; ++i) {
-      int32_t up, low;
-      verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
-      const int lo = window > 0 ? std::max(0, low - n_rows[i] - window + 1) : 0;
-      min_keys = std::min(min_keys, low - n_rows[i] + 1 - lo);
-    }
-    precise = min_keys < SVATTN_TQ3_FAST_KEYS;
     QPrepArgs qa;
     qa.q = q;
     qa.q1 = q1;
@@ -671,7 +655,7 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
   hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, s);
   for (size_t li = 0; li < args.size() && e == hipSuccess; ++li)
-    e = tq3 ? launch_attn_tq3(args[li], vp.nct, precise, s) : launch_attn(args[li], vp.nct, s);
+    e = tq3 ? launch_attn_tq3(args[li], vp.nct, s) : launch_attn(args[li], vp.nct, s);
   if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, s);
   if (e != hipSuccess) return hip_fail(c, e, "attention launch");
   for (size_t li = 0; li < args.size(); ++li) {
