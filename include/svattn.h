@@ -295,6 +295,24 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
                      int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * spec_verify_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the partial results and rotated
+ * queries go to a fixed scratch array of 32 MiB per device that the library
+ * owns for the life of the process.  The call allocates nothing.  The
+ * scratch of a device is shared by every call on it: calls that may overlap
+ * on one GPU (different streams, different handles) race, so order them
+ * (one stream) or use spec_verify_attn with workspaces of their own.  The
+ * scratch needs no clearing: every call writes each slot it reads.
+ * Arguments and results as spec_verify_attn's.  Errors: as
+ * spec_verify_attn's; KV_ENOMEM when the call needs more than 32 MiB of
+ * scratch (kv_workspace_bytes gives the need).
+ */
+int spec_verify_attn_static(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                            const float* q, int32_t num_q_heads, float scale, float softcap,
+                            int32_t window, float* out, void* stream);
+
+/*
  * Append the verified rows' K/V and verify them, in one call: kv_append of
  * n_rows[i] positions to each sequence followed by spec_verify_attn over
  * those same positions (AX Engine page, "Core Technical Architecture &

@@ -104,6 +104,7 @@ _SIGS = {
     "spec_accept": [_i32, _i32p, _i32, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_size_t, _p],
     "spec_accept_workspace_bytes": [_i32, _i32p, _i32, _i32, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)],
     "spec_accept_last_error": [],
+    "spec_verify_attn_static": [_p, _i32, _i32p, _i32p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p],
     "kv_read_status": [_p, ctypes.POINTER(ctypes.c_uint32), _i32, _p],
     "kv_stream_probe": [_p, ctypes.c_size_t, _p, ctypes.c_size_t, _p],
 }
@@ -315,6 +316,12 @@ def kv_codec(h, head_dim):
     return signs, s, lev, lev16, thr
 
 
+def spec_verify_attn_static(h, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out, stream=None):
+    return lib().spec_verify_attn_static(h, len(seq_ids), _arr(seq_ids), _arr(n_rows), ctypes.c_void_p(q.data_ptr()),
+                                         num_q_heads, scale, softcap, window, ctypes.c_void_p(out.data_ptr()),
+                                         _stream_ptr(stream))
+
+
 def kv_read_status(h, clear=False, stream=None):
     out = ctypes.c_uint32()
     _check(lib().kv_read_status(h, ctypes.byref(out), 1 if clear else 0, _stream_ptr(stream)), h)
@@ -487,6 +494,20 @@ class KVCache:
             workspace = self.workspace(seq_ids, n_rows, num_q_heads, window)
         _check(spec_verify_attn(self.handle, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out,
                                 workspace, stream), self.handle)
+        return out
+
+    def verify_static(self, seq_ids, n_rows, q, num_q_heads, scale, softcap=0.0, window=0, out=None, stream=None):
+        """verify() on the library's fixed per-device scratch: no workspace, no
+        allocation by the call (out=None allocates the output here, in Python)."""
+        import torch
+
+        rows = int(sum(n_rows))
+        self._check_rows("q", q, rows, num_q_heads, torch.float32)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_rows("out", out, rows, num_q_heads, torch.float32)
+        _check(spec_verify_attn_static(self.handle, seq_ids, n_rows, q, num_q_heads, float(scale), float(softcap),
+                                       window, out, stream), self.handle)
         return out
 
     def append_verify(self, seq_ids, n_rows, k, v, q, num_q_heads, scale, softcap=0.0, window=0, out=None,

@@ -39,8 +39,8 @@ HIP_FLAGS = [
     "-I", CSRC,
 ]
 
-HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "accept.hip", "probe.hip", "svattn.cpp", "kvcore.cpp",
-               "ngram.cpp"]
+HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "accept.hip", "probe.hip", "scratch.hip", "svattn.cpp",
+               "kvcore.cpp", "ngram.cpp"]
 CORE_SOURCES = ["kvcore.cpp", "svcore_capi.cpp", "ngram.cpp"]
 
 

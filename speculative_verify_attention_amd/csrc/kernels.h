@@ -258,6 +258,13 @@ struct AcceptArgs {
   int32_t d0[kMaxAcceptSeqs];  // first draft row (relative to rows_t)
 };
 
+// ---- fixed device scratch (spec_verify_attn_static) ------------------------------------
+// 32 MiB per device, held until the process ends; the device address of the
+// calling thread's current device (resolved on first use with that device
+// current).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** out);
+
 // ---- streaming-read probe ------------------------------------------------------------
 // Workgroups of the probe (4 per compute unit); the sink holds one word each.
 constexpr int kProbeWorkgroups = 1024;

@@ -707,6 +707,28 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
                         workspace, static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
+int spec_verify_attn_static(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                            const float* q, int32_t num_q_heads, float scale, float softcap, int32_t window,
+                            float* out, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  VerifyPlan vp;
+  rc = plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, nullptr, &vp, &c->err);
+  if (rc != KV_OK) return rc;
+  if (vp.total > kStaticScratchBytes)
+    return set_err(c, KV_ENOMEM,
+                   "call needs " + std::to_string(vp.total) + " bytes of scratch; the fixed scratch holds " +
+                       std::to_string(kStaticScratchBytes) + " (use spec_verify_attn with a workspace)");
+  void* ws = nullptr;
+  hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(c, e, "resolving the fixed scratch");
+  rc = check_verify_args(c, vp, q, scale, softcap, out, ws, kStaticScratchBytes);
+  if (rc != KV_OK) return rc;
+  return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out, ws,
+                        static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
 int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const void* k,
                      const void* v, const float* q, int32_t num_q_heads, float scale, float softcap, int32_t window,
                      float* out, void* workspace, size_t ws_bytes, void* stream) {
