@@ -52,6 +52,26 @@ int svcore_codec(const svcore* c, int8_t* signs, float* s_matrix, double* levels
                  double* thresholds);
 /* Round a double to IEEE half bits (nearest-even, saturating at 65504). */
 int svcore_half_bits(double x, uint16_t* out, int32_t* saturated);
+/*
+ * Plan a verify call on the host-only core: the planning spec_verify_attn
+ * and kv_append_verify do before they enqueue anything (AX Engine page,
+ * "Core Technical Architecture & Methods": 1 + k rows per sequence checked
+ * against its cache; SwiftLM page, long-context passage: a long pair is
+ * split over many workgroups and their partials merged).  The plan is then
+ * checked against the invariants its kernels rely on: launches of at most
+ * 128 sequences, each (sequence, kv head) pair cut into non-empty chunks of
+ * tiles, one partial slot per workgroup, row offsets, workspace bytes.
+ * pending: max_seqs device rollbacks not yet read back (null: none); fused:
+ * nonzero plans kv_append_verify (the rows are appended first).
+ * summary[6] receives: column groups, launches, partial slots, workspace
+ * bytes, partial bytes, rotated-query bytes.  ksplit (n_seqs entries, call
+ * order, or null) receives the chunks per kv head of each entry.
+ * Returns 0, the status codes of spec_verify_attn's argument checks, or -5
+ * when the plan breaks an invariant (svcore_last_error says which).
+ */
+int svcore_plan_verify(svcore* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                       int32_t num_q_heads, int32_t window, const int32_t* pending, int32_t fused,
+                       int64_t* summary, int32_t* ksplit);
 const char* svcore_last_error(const svcore* c);
 
 #ifdef __cplusplus

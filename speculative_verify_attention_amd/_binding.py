@@ -133,6 +133,7 @@ _CORE_SIGS = {
     "svcore_free_blocks": [_p, _i32p],
     "svcore_codec": [_p, _p, _p, _p, _p, _p],
     "svcore_half_bits": [ctypes.c_double, ctypes.POINTER(ctypes.c_uint16), _i32p],
+    "svcore_plan_verify": [_p, _i32, _i32p, _i32p, _i32, _i32, _p, _i32, _p, _p],
     "svcore_last_error": [_p],
     **_NGRAM_SIGS,
 }

@@ -4,6 +4,8 @@
   kernels for gfx950, built with hipcc.
 * ``libsvattn_core.so``  - the HIP-free host core alone (include/svcore.h),
   built with g++, for host-logic tests on machines without a GPU.
+* ``libsvattn_core_san.so`` - the same under ASan + UBSan with the verify
+  planner's invariant checks compiled in (SVATTN_CHECKED).
 
 Usage: ``python -m speculative_verify_attention_amd.build`` (or ``build()``).
 Every call compiles from source; objects go to ``_build/`` beside the
@@ -22,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsvattn.so")
 CORE_LIB = os.path.join(PKG, "libsvattn_core.so")
+CORE_SAN_LIB = os.path.join(PKG, "libsvattn_core_san.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,8 +43,12 @@ HIP_FLAGS = [
 ]
 
 HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "accept.hip", "probe.hip", "scratch.hip", "svattn.cpp",
-               "kvcore.cpp", "ngram.cpp"]
-CORE_SOURCES = ["kvcore.cpp", "svcore_capi.cpp", "ngram.cpp"]
+               "kvcore.cpp", "plan.cpp", "ngram.cpp"]
+CORE_SOURCES = ["kvcore.cpp", "plan.cpp", "svcore_capi.cpp", "ngram.cpp"]
+# the host core again, under AddressSanitizer and UndefinedBehaviorSanitizer,
+# with the planner's invariant checks compiled in (plain g++, no GPU code)
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined", "-DSVATTN_CHECKED"]
 
 
 def _run(cmd):
@@ -58,13 +65,17 @@ def _compile_hip(src, defines=(), tag=""):
     return obj
 
 
-def build_core():
+def build_core(sanitized=False):
+    """libsvattn_core.so, or with sanitized=True libsvattn_core_san.so (load
+    it with the sanitizer runtimes preloaded)."""
     os.makedirs(BUILD, exist_ok=True)
-    tmp = CORE_LIB + ".tmp"
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-I", INCLUDE, "-I", CSRC,
+    out = CORE_SAN_LIB if sanitized else CORE_LIB
+    flags = SAN_FLAGS if sanitized else ["-O2"]
+    tmp = out + ".tmp"
+    _run(["g++", *flags, "-std=c++17", "-fPIC", "-shared", "-Wall", "-I", INCLUDE, "-I", CSRC,
           *[os.path.join(CSRC, s) for s in CORE_SOURCES], "-o", tmp])
-    os.replace(tmp, CORE_LIB)
-    return CORE_LIB
+    os.replace(tmp, out)
+    return out
 
 
 def build_hip(jobs=None, out=LIB, defines=()):
@@ -83,6 +94,7 @@ def build_hip(jobs=None, out=LIB, defines=()):
 
 def build():
     core = build_core()
+    build_core(sanitized=True)
     lib = build_hip()
     return lib, core
 

@@ -8,6 +8,8 @@
 
 #include <cstdint>
 
+#include "plan.h"
+
 namespace svattn {
 
 // ---- pool layout -------------------------------------------------------------
@@ -56,9 +58,6 @@ __host__ __device__ inline int64_t plain_v_index(int fmt, int D, int j, int d) {
   return sb * 32 * D + (((uq * (D / 32) + dt) * 2 + h) * 32 + dr) * 4 + e;
 }
 
-// Keys per attention tile (one wavefront iteration): 16 KiB of bf16 K and V
-// at d <= 128, one 32-key sub-tile otherwise.
-constexpr int tile_keys(int fmt, int d) { return fmt == 1 ? 32 * (128 / d > 1 ? 128 / d : 1) : 32; }
 
 // Bytes of one 32-token TQ3 sub-tile of one head.
 __host__ __device__ constexpr int tq3_sub_bytes(int d) { return 28 * d + 192; }
@@ -153,10 +152,6 @@ struct EncodeArgs {
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
 // ---- verify attention ------------------------------------------------------------
-#ifndef SVATTN_MAX_ATTN_SEQS
-#define SVATTN_MAX_ATTN_SEQS 128
-#endif
-constexpr int kMaxAttnSeqs = SVATTN_MAX_ATTN_SEQS;
 
 // A call's work is cut into chunks of consecutive tiles of one (sequence, kv
 // head) pair; workgroup w takes one chunk.  Sequence i's pairs are split into

@@ -14,6 +14,7 @@
 
 #include "kernels.h"
 #include "kvcore.h"
+#include "plan.h"
 
 using namespace svattn;
 
@@ -42,18 +43,6 @@ struct kv_cache {
 };
 
 namespace {
-
-constexpr size_t kAlign = 256;
-
-// Workgroups a verify call is split into (one round on 256 compute units at
-// one workgroup per CU); build-time constants so variants can be measured.
-#ifndef SVATTN_WG_PER_CALL
-#define SVATTN_WG_PER_CALL 256
-#endif
-#ifndef SVATTN_WG_PER_CALL_D256
-#define SVATTN_WG_PER_CALL_D256 256
-#endif
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct MetaLayout {
   size_t blocks_bytes, table_off, status_off, roll_off, signs_off, st_off, total;
@@ -117,118 +106,13 @@ CoreParams core_params(const kv_params& p) {
 
 // ---- verify-call planning (shared by kv_workspace_bytes and spec_verify_attn) ----
 
-struct VerifyLaunch {
-  int first, count;  // sequences [first, first+count) of the call
-  int n_wg;
-  int64_t slot0;     // first partial slot of this launch
-  std::vector<int32_t> ksplit, wg_base;
-};
-
-struct VerifyPlan {
-  int nct = 1, rpad = 32;
-  std::vector<int> order;      // call index of the i-th sequence handed to the kernels
-  std::vector<int32_t> qrow0;  // first query/output row of each call index
-  int64_t slot_stride = 0, slots = 0, rows = 0;
-  size_t part_bytes = 0, q_bytes = 0, total = 0;
-  std::vector<VerifyLaunch> launches;
-};
-
-// Lengths a verify call plans with: the host's length (plus rows a fused
-// append adds first) is an upper bound of what the kernels will see; minus
-// the pending device rollbacks it is a lower bound.  Tiles are planned from
-// the lower bound's window start to the upper bound's end; the kernels cut
-// their chunks to the lengths they read on the device.
 void verify_lengths(const kv_cache* c, int32_t seq, int32_t added, int32_t* up, int32_t* low) {
-  int32_t len;
-  c->core.seq_len(seq, &len);
-  *up = len + added;
-  *low = *up - c->pend[seq];
+  svattn::verify_lengths(c->core, c->pend.data(), seq, added, up, low);
 }
 
 int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                 int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp, std::string* err) {
-  const CoreParams& P = c->core.params();
-  auto fail = [&](int code, const std::string& m) {
-    if (err) *err = m;
-    return code;
-  };
-  if (n_seqs < 1) return fail(KV_EINVAL, "n_seqs must be >= 1");
-  if (!seq_ids || !n_rows) return fail(KV_EINVAL, "null seq_ids / n_rows");
-  if (num_q_heads < 1 || num_q_heads % P.num_kv_heads) return fail(KV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
-  if (window < 0) return fail(KV_EINVAL, "window < 0");
-  if (P.ring_window > 0 && (window < 1 || window > P.ring_window))
-    return fail(KV_EINVAL, "a ring cache serves windows of 1 .. " + std::to_string(P.ring_window) + " positions");
-  const int g = num_q_heads / P.num_kv_heads;
-  int max_rows = 0;
-  for (int i = 0; i < n_seqs; ++i) {
-    if (!c->core.valid_seq(seq_ids[i])) return fail(KV_ENOSEQ, "sequence id " + std::to_string(seq_ids[i]) + " out of range");
-    int32_t up, low;
-    verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
-    if (n_rows[i] < 1 || n_rows[i] > KV_MAX_ROWS) return fail(KV_EINVAL, "n_rows must be in [1, 8]");
-    if (n_rows[i] > low)
-      return fail(KV_ERANGE, "n_rows exceeds seq_len of sequence " + std::to_string(seq_ids[i]) +
-                                 (up > low ? " (device rollbacks pending: the lower bound counts)" : ""));
-    if (P.ring_window > 0 && std::max(0, low - n_rows[i] - window + 1) < c->core.first_block(seq_ids[i]) * kBlock)
-      return fail(KV_ERANGE, "the rows' windows reach positions the ring cache released");
-    max_rows = std::max(max_rows, (int)n_rows[i]);
-    vp->rows += n_rows[i];
-  }
-  const int R = max_rows * g;
-  if (R > 64) return fail(KV_EINVAL, "n_rows * (num_q_heads / num_kv_heads) must be <= 64");
-  vp->nct = R > 32 ? 2 : 1;
-  vp->rpad = 32 * vp->nct;
-  vp->slot_stride = (int64_t)vp->rpad * (2 + P.head_dim);
-  const int TL = 4 / vp->nct;
-  const int target_wg = P.head_dim > 128 ? SVATTN_WG_PER_CALL_D256 : SVATTN_WG_PER_CALL;
-  // tiles of each (sequence, kv head) pair over the whole call
-  const int tk = tile_keys(P.format, P.head_dim);
-  std::vector<int> nt(n_seqs);
-  int64_t total_tiles = 0;
-  for (int i = 0; i < n_seqs; ++i) {
-    int32_t up, low;
-    verify_lengths(c, seq_ids[i], added ? added[i] : 0, &up, &low);
-    const int klo = window > 0 ? std::max(0, low - n_rows[i] - window + 1) : 0;
-    nt[i] = (up + tk - 1) / tk - klo / tk;
-    total_tiles += (int64_t)nt[i] * P.num_kv_heads;
-  }
-  // Uniform batches: one round of workgroups (one per CU).  Ragged batches
-  // (lengths far apart): four times as many, smaller chunks, so the dispatcher
-  // can even out the mix of long and short pairs.
-  const int nt_max = *std::max_element(nt.begin(), nt.end());
-  const int nt_min = *std::min_element(nt.begin(), nt.end());
-  const int64_t target = 4 * (int64_t)nt_min >= 3 * (int64_t)nt_max ? target_wg : 4 * (int64_t)target_wg;
-  // chunks of at most ~total / target tiles, never fewer than one per token lane
-  const int64_t per_wg = std::max<int64_t>(TL, (total_tiles + target - 1) / target);
-  // Sequences go to the kernel longest first (workgroups are dispatched in
-  // index order, so the big chunks start first and the short ones fill in).
-  vp->order.resize(n_seqs);
-  for (int i = 0; i < n_seqs; ++i) vp->order[i] = i;
-  std::stable_sort(vp->order.begin(), vp->order.end(), [&](int x, int y) { return nt[x] > nt[y]; });
-  vp->qrow0.assign(n_seqs, 0);
-  for (int i = 1; i < n_seqs; ++i) vp->qrow0[i] = vp->qrow0[i - 1] + n_rows[i - 1];
-  for (int first = 0; first < n_seqs; first += kMaxAttnSeqs) {
-    VerifyLaunch L;
-    L.first = first;
-    L.count = std::min(kMaxAttnSeqs, n_seqs - first);
-    L.ksplit.assign(L.count, 1);
-    L.wg_base.assign(L.count + 1, 0);
-    for (int i = 0; i < L.count; ++i) {
-      const int tiles = nt[vp->order[first + i]];
-      int k = (int)std::max<int64_t>(1, (tiles + per_wg - 1) / per_wg);
-      const int cs = (tiles + k - 1) / k;
-      k = (tiles + cs - 1) / cs;  // no empty chunk
-      L.ksplit[i] = k;
-      L.wg_base[i + 1] = L.wg_base[i] + k * P.num_kv_heads;
-    }
-    L.n_wg = L.wg_base[L.count];
-    L.slot0 = vp->slots;
-    vp->slots += L.n_wg;
-    vp->launches.push_back(std::move(L));
-  }
-  vp->part_bytes = align_up((size_t)vp->slots * vp->slot_stride * 4);
-  if (P.format == KV_TQ3) vp->q_bytes = align_up((size_t)vp->rows * num_q_heads * P.head_dim * 4);
-  vp->total = vp->part_bytes + 2 * vp->q_bytes;
-  return KV_OK;
+  return svattn::plan_verify(c->core, c->pend.data(), n_seqs, seq_ids, n_rows, num_q_heads, window, added, vp, err);
 }
 
 }  // namespace

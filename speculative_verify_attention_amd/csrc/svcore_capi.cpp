@@ -7,6 +7,7 @@
 #include <string>
 
 #include "kvcore.h"
+#include "plan.h"
 
 using namespace svattn;
 
@@ -105,6 +106,32 @@ int svcore_half_bits(double x, uint16_t* out, int32_t* saturated) {
   bool sat = false;
   *out = half_bits_rne(x, &sat);
   if (saturated) *saturated = sat ? 1 : 0;
+  return 0;
+}
+
+int svcore_plan_verify(svcore* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                       int32_t num_q_heads, int32_t window, const int32_t* pending, int32_t fused,
+                       int64_t* summary, int32_t* ksplit) {
+  if (!c || !summary) return -1;
+  VerifyPlan vp;
+  const int rc = plan_verify(c->core, pending, n_seqs, seq_ids, n_rows, num_q_heads, window, fused ? n_rows : nullptr,
+                             &vp, &c->err);
+  if (rc != 0) return rc;
+  const std::string bad =
+      check_plan(c->core, pending, n_seqs, seq_ids, n_rows, num_q_heads, window, fused ? n_rows : nullptr, vp);
+  if (!bad.empty()) {
+    c->err = "plan violates its invariants: " + bad;
+    return -5;
+  }
+  summary[0] = vp.nct;
+  summary[1] = (int64_t)vp.launches.size();
+  summary[2] = vp.slots;
+  summary[3] = (int64_t)vp.total;
+  summary[4] = (int64_t)vp.part_bytes;
+  summary[5] = (int64_t)vp.q_bytes;
+  if (ksplit)
+    for (const VerifyLaunch& L : vp.launches)
+      for (int i = 0; i < L.count; ++i) ksplit[vp.order[L.first + i]] = L.ksplit[i];
   return 0;
 }
 
