@@ -69,13 +69,16 @@ struct ColState {
 // probabilities stay below 2^tau and rescales are rare), then
 // p <- 2^(p - m) and the running sum.
 template <int D, int NSUB>
-__device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB][16], float tau = 8.0f) {
+__device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB][16], float tau = 8.0f,
+                                               float mul = 1.0f) {
+  // p holds scores in log2 units times 1 / mul (mul > 0): the multiply is
+  // folded into the max and into the exponent's argument
   float mt = NEG_INF;
 #pragma unroll
   for (int st = 0; st < NSUB; ++st)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, p[st][r]);
-  mt = fmaxf(mt, xor32(mt));
+  mt = fmaxf(mt, xor32(mt)) * mul;
   const bool up = mt > cs.m + tau;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
     // lanes that move: alpha = 2^(m_old - m_new), 0 when nothing was seen yet;
@@ -92,7 +95,7 @@ __device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB]
   for (int st = 0; st < NSUB; ++st)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(p[st][r] - m_use);
+      const float e = fast_exp2(fmaf(p[st][r], mul, -m_use));
       p[st][r] = e;
       lsum += e;
     }

@@ -64,6 +64,18 @@ __device__ __forceinline__ u32x2_t split_f16_pair(float a, float b) {
   return u32x2_t{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};  // (hi pair, lo pair)
 }
 
+// The same split of two products p * n (n an fp16 value widened): hi from the
+// rounded product, lo the exact product less hi rounded once (one fma), so
+// that hi + lo carries the product to ~2^-21.  Each product and residual is
+// one mixed-precision fma that reads n as fp16.
+__device__ __forceinline__ u32x2_t split_f16_prod(float p0, float n0, float p1, float n1) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(fmaf(p0, n0, 0.0f), fmaf(p1, n1, 0.0f));
+  const float ra = fmaf(p0, n0, -(float)h[0]), rb = fmaf(p1, n1, -(float)h[1]);
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t l = {(_Float16)ra, (_Float16)rb};
+  return u32x2_t{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
 // ---- query rotation --------------------------------------------------------------
 
 // One wave per query vector: q' = H (D q) / sqrt(d) with an in-register
@@ -265,6 +277,10 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
   };
   f32x16_t s1 = {}, s2 = {};
   u32x4_t mse[2], qjl[2];
+  // issue priority by phase: highest for the key products, lowest for the
+  // softmax, so that the other wave of the SIMD fills the matrix-core phases
+  // with its vector work
+  __builtin_amdgcn_s_setprio(2);
   fetch(0, mse[0], qjl[0]);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -275,18 +291,27 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(km, qr.get(2, kk), s1, 0, 0, 0);
     s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq, qr.get(3, kk), s2, 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
   // scores in log2 units (q'' already carries the QJL coefficient relative
-  // to the first term)
+  // to the first term), times 1 / smul: without a soft cap and with a
+  // positive multiplier, the multiplier is left to the softmax, which folds
+  // it into the exponent's argument
+  const bool fold = !CAP && a.q1_mul > 0.0f;
+  const float smul = fold ? a.q1_mul : 1.0f;
   float p[1][16];
   {
     uint32_t nw[8], gw[8];
     scale_words(0, nw);
     scale_words(1, gw);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f)) * a.q1_mul;
-      if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
-      p[0][r] = x;
+    for (int r = 0; r < 16; ++r) p[0][r] = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f));
+    if (!fold) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = p[0][r] * a.q1_mul;
+        if constexpr (CAP) x = a.cap_l2 * tanh_nb(x * a.inv_cap_l2);
+        p[0][r] = x;
+      }
     }
   }
   uint32_t vw[8];
@@ -313,7 +338,8 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
   for (int q = 1; q < 8; ++q) nv2 = __builtin_elementwise_max(nv2, __builtin_bit_cast(f16x2_t, vw[q]));
   float nvmax = fmaxf((float)nv2[0], (float)nv2[1]);
   nvmax = fmaxf(nvmax, xor32(nvmax));
-  softmax_update<D, 1>(cs, p, nvmax <= 240.0f ? 8.0f : 0.0f);
+  softmax_update<D, 1>(cs, p, nvmax <= 240.0f ? 8.0f : 0.0f, smul);
+  __builtin_amdgcn_s_setprio(1);
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -321,7 +347,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int r = 8 * v + e;
-      const u32x2_t sp = split_f16_pair(p[0][r] * half_at(vw, r), p[0][r + 1] * half_at(vw, r + 1));
+      const u32x2_t sp = split_f16_prod(p[0][r], half_at(vw, r), p[0][r + 1], half_at(vw, r + 1));
       phw[e / 2] = sp[0];
       plw[e / 2] = sp[1];
     }
@@ -343,6 +369,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
       cs.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, plo, cs.acc[dt], 0, 0, 0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int NCT, bool CAP>
@@ -475,6 +502,9 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
     __builtin_amdgcn_wave_barrier();
   };
   if (cnt > 0) stage(0, buf[0]);
+  // the two waves of a SIMD (waves w and w + 4) start half a phase apart, so
+  // that one is in its matrix-core phase while the other is in its softmax
+  if (wave >= 4) __builtin_amdgcn_s_sleep(24);
   // Whole rounds of NBUF sub-tiles, then the last ones (fewer than NBUF, all
   // in flight already).  Inside a round the prefetch is unconditional: past
   // the end it reloads the last sub-tile into the ring slot that no
