@@ -34,6 +34,20 @@
 #include "attn_common.h"
 #include "kernels.h"
 
+// Query fragments re-read from LDS at every tile from this head size up (0:
+// never), and the largest tile (registers per lane) kept in a ring of
+// SVATTN_NBUF tiles; bigger tiles are loaded one at a time.
+#ifndef SVATTN_Q_FROM_LDS
+#define SVATTN_Q_FROM_LDS 256
+#endif
+#ifndef SVATTN_RING_MAX_REGS
+#define SVATTN_RING_MAX_REGS 64
+#endif
+// Bigger tiles: one buffer refilled in halves (K, then V) instead of whole.
+#ifndef SVATTN_STAGGER
+#define SVATTN_STAGGER 1
+#endif
+
 namespace svattn {
 
 // ---- per-format traits ---------------------------------------------------------------
@@ -81,6 +95,27 @@ __device__ __forceinline__ void load_tile(TileRegs<FMT, D>& b, const uint8_t* __
     for (int j = 0; j < T::LV; ++j)
       b.v[st][j] = *reinterpret_cast<const u32x4_t*>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
   }
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void load_k(TileRegs<FMT, D>& b, const uint8_t* __restrict__ kbase, int lane) {
+  using T = Tr<FMT, D>;
+  constexpr int SUB_BYTES = 32 * D * (FMT == 1 ? 2 : 4);
+#pragma unroll
+  for (int st = 0; st < T::NSUB; ++st)
+#pragma unroll
+    for (int j = 0; j < T::LK; ++j)
+      b.k[st][j] = *reinterpret_cast<const u32x4_t*>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
+}
+template <int FMT, int D>
+__device__ __forceinline__ void load_v(TileRegs<FMT, D>& b, const uint8_t* __restrict__ vbase, int lane) {
+  using T = Tr<FMT, D>;
+  constexpr int SUB_BYTES = 32 * D * (FMT == 1 ? 2 : 4);
+#pragma unroll
+  for (int st = 0; st < T::NSUB; ++st)
+#pragma unroll
+    for (int j = 0; j < T::LV; ++j)
+      b.v[st][j] = *reinterpret_cast<const u32x4_t*>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
 }
 
 // Query operand of one lane (column c, half-wave hh).
@@ -143,13 +178,22 @@ struct QOperand<0, D> {  // k-step kk holds dim (D/2) hh + kk
 template <int D>
 __device__ __forceinline__ f32x16_t qk_sub(const QOperand<1, D>& q, const TileRegs<1, D>& b, int st) {
   const int lane = threadIdx.x & 63;
+  typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+  lds_u32x4_t* ql = (lds_u32x4_t*)q.lds;
+#if SVATTN_Q_FROM_LDS
+  // The fragments are read from LDS at every tile: hoisted out of the loop
+  // they would hold 2 x D/4 registers for the whole loop (parked in
+  // accumulation registers and copied back at every use), which leaves no
+  // room for a second tile in flight at d = 256.
+  if constexpr (D >= SVATTN_Q_FROM_LDS) asm volatile("" : "+v"(ql));
+#endif
   f32x16_t s = {};
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, b.k[st][kk]);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, q.lds[kk * 64 + lane]), s, 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, q.lds[(D / 16 + kk) * 64 + lane]),
-                                                s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, ql[kk * 64 + lane]), s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, __builtin_bit_cast(bf16x8_t, ql[(D / 16 + kk) * 64 + lane]), s,
+                                                0, 0, 0);
   }
   return s;
 }
@@ -240,9 +284,17 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const TileRegs<
 
 // ---- the partial kernel ----------------------------------------------------------
 
-template <int FMT, int D, bool CAP>
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// after_qk runs once the key products no longer need b.k, after_pv once the
+// value products no longer need b.v (a single-buffered loop refills them
+// there).
+template <int FMT, int D, bool CAP, typename AfterQK = NoHook, typename AfterPV = NoHook>
 __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& b, const QOperand<FMT, D>& q,
-                                             const AttnArgs& a, int key0, int L, int n, int ppos, int lane) {
+                                             const AttnArgs& a, int key0, int L, int n, int ppos, int lane,
+                                             AfterQK after_qk = AfterQK(), AfterPV after_pv = AfterPV()) {
   constexpr int NSUB = Tr<FMT, D>::NSUB;
   constexpr int TK = 32 * NSUB;
   const int hh = lane >> 5;
@@ -257,6 +309,7 @@ __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& 
       p[st][r] = x * 1.4426950408889634f;  // log2(e): the softmax runs on exp2
     }
   }
+  after_qk();
   // keys every row sees need no mask: all of the tile lies at or before the
   // first row's position and inside the last row's window
   const bool full = key0 + TK <= L - n + 1 && (a.window == 0 || L - key0 <= a.window);
@@ -273,6 +326,7 @@ __device__ __forceinline__ void process_tile(ColState<D>& cs, TileRegs<FMT, D>& 
   }
   softmax_update<D, NSUB>(cs, p);
   pv_tile<D>(cs.acc, b, p);
+  after_pv();
 }
 
 template <int FMT, int D, int NCT, bool CAP, bool APPEND>
@@ -283,7 +337,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   constexpr int E = FMT == 1 ? 2 : 4;
   // registers per tile buffer decide how many tiles are kept in flight
   constexpr int TILE_REGS = Tr<FMT, D>::NSUB * (Tr<FMT, D>::LK + Tr<FMT, D>::LV) * 4;
-  constexpr int NBUF = TILE_REGS <= 64 ? SVATTN_NBUF : 1;
+  constexpr int NBUF = TILE_REGS <= SVATTN_RING_MAX_REGS ? SVATTN_NBUF : 1;
   __shared__ float cbuf[CombineBuf<D, NCT>::FLOATS];
   __shared__ u32x4_t qlds[FMT == 1 ? NCT * QOperand<1, D>::LDS_ENTRIES : 1];
 
@@ -400,20 +454,39 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
   // numbers of loads in flight, and the compiler's wait counts then assume
   // the worse one: the wait for tile k would also wait for the tile just
   // requested.
-  int i = 0;
-  for (; i + NBUF <= cnt; i += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int k = i + u;
+  if constexpr (NBUF == 1 && FMT == 1 && SVATTN_STAGGER) {
+    // One tile buffer, refilled in halves: the next tile's K is requested as
+    // soon as this tile's key products are issued, its V once the value
+    // products are, so each half has the other half's compute to arrive
+    // (past the end the last tile is reloaded, unused).
+    if (cnt > 0) {
       const uint8_t *kb, *vb;
-      bases(t_first + min(k + NBUF - 1, cnt - 1) * TL, kb, vb);
-      load_tile<FMT, D>(buf[(u + NBUF - 1) % NBUF], kb, vb, lane);
-      process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane);
+      bases(t_first, kb, vb);
+      load_tile<FMT, D>(buf[0], kb, vb, lane);
     }
-  }
+    for (int k = 0; k < cnt; ++k) {
+      const uint8_t *kb, *vb;
+      bases(t_first + min(k + 1, cnt - 1) * TL, kb, vb);
+      process_tile<FMT, D, CAP>(cs, buf[0], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane,
+                                [&] { load_k<FMT, D>(buf[0], kb, lane); }, [&] { load_v<FMT, D>(buf[0], vb, lane); });
+    }
+  } else {
+    int i = 0;
+    for (; i + NBUF <= cnt; i += NBUF) {
 #pragma unroll
-  for (int u = 0; u + 1 < NBUF; ++u)
-    if (i + u < cnt) process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + (i + u) * TL) * TK, L, n, ppos, lane);
+      for (int u = 0; u < NBUF; ++u) {
+        const int k = i + u;
+        const uint8_t *kb, *vb;
+        bases(t_first + min(k + NBUF - 1, cnt - 1) * TL, kb, vb);
+        load_tile<FMT, D>(buf[(u + NBUF - 1) % NBUF], kb, vb, lane);
+        process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + k * TL) * TK, L, n, ppos, lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u + 1 < NBUF; ++u)
+      if (i + u < cnt)
+        process_tile<FMT, D, CAP>(cs, buf[u], qop, a, (tlo + t_first + (i + u) * TL) * TK, L, n, ppos, lane);
+  }
 
   combine_and_store<D, NCT>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
