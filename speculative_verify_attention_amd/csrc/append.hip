@@ -208,19 +208,25 @@ __device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    double proj[E];
+    // four partial sums per output (rows j = u mod 4), so that four chains
+    // of dependent fp64 fmas run side by side instead of one of length D;
+    // unrolled so that many rows of S^T are in flight at once
+    double proj[4][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) proj[e] = 0.0;
-    // unrolled so that many rows of S^T are in flight at once (the loop is
-    // a chain of dependent L2 round trips otherwise)
-#pragma unroll 16
-    for (int j = 0; j < D; ++j) {
-      const double rj = rbuf[j];
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < E; ++e) proj[e] += (double)s_t[j * D + lane * E + e] * rj;
+      for (int e = 0; e < E; ++e) proj[u][e] = 0.0;
+#pragma unroll 4
+    for (int j = 0; j < D; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double rj = rbuf[j + u];
+#pragma unroll
+        for (int e = 0; e < E; ++e) proj[u][e] = fma((double)s_t[(j + u) * D + lane * E + e], rj, proj[u][e]);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) o.bit[e] = proj[e] >= 0.0 ? 1 : 0;
+    for (int e = 0; e < E; ++e) o.bit[e] = ((proj[0][e] + proj[1][e]) + (proj[2][e] + proj[3][e])) >= 0.0 ? 1 : 0;
     // keep rbuf stable until every lane has read it before a later reuse
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -284,19 +290,22 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
 
 // ---- quantize-on-append ----------------------------------------------------------
 
-// One workgroup (4 waves) per (segment, 32-token sub-tile, kv head).  Each
-// wave encodes whole tokens; key codes and scales go straight to their
-// bytes (a byte never holds two tokens).  Value codes share 48-bit fields
+// One workgroup (8 waves) per (segment, 32-token sub-tile, kv head).  Each
+// wave encodes whole tokens (a decode step's <= 8 new rows: one each); key
+// codes and scales go straight to their bytes (a byte never holds two
+// tokens).  Value codes share 48-bit fields
 // across 16 tokens, so they are staged in LDS and then merged into their
 // fields by one thread each (one writer per field: no two workgroups race).
+constexpr int kAppendWaves = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_kernel(AppendArgs a) {
   constexpr int E = D / 64;
   constexpr int SB = tq3_sub_bytes(D);
   // S^T staged in LDS once per workgroup for d <= 128 (64 KiB), so the
   // projections of the key residuals read LDS instead of L2
   constexpr bool kStage = D <= 128;
-  __shared__ double rbuf[4][D];
+  __shared__ double rbuf[kAppendWaves][D];
   __shared__ uint8_t vcode[32][D];
   __shared__ __align__(16) float st_lds[kStage ? D * D : 4];
   __shared__ uint32_t sat_any;
@@ -315,14 +324,14 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
     const float4* src = reinterpret_cast<const float4*>(a.s_t);
     float4* dst = reinterpret_cast<float4*>(st_lds);
 #pragma unroll 4
-    for (int i = threadIdx.x; i < D * D / 4; i += 256) dst[i] = src[i];
+    for (int i = threadIdx.x; i < D * D / 4; i += kAppendWaves * 64) dst[i] = src[i];
   }
   const float* s_t = kStage ? st_lds : a.s_t;
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
   uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
   uint32_t sat = 0;
   __syncthreads();
-  for (int t = t0 + wave; t < t1; t += 4) {
+  for (int t = t0 + wave; t < t1; t += kAppendWaves) {
     const int m = t & 31;
     const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
     const float* kx = reinterpret_cast<const float*>(a.k) + (src_row * a.lay.hkv + h) * D;
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(256) void append_tq3_kernel(AppendArgs a) {
   // Merge the staged value codes into their 48-bit fields: one thread per
   // (dimension, half): the field of dimension i for tokens with bit 2 = h.
   const int m0 = t0 & 31, m1 = m0 + (t1 - t0);
-  for (int f = threadIdx.x; f < 2 * D; f += 256) {
+  for (int f = threadIdx.x; f < 2 * D; f += kAppendWaves * 64) {
     const int i = f >> 1, hsel = f & 1;
     int bit0;
     const int off = tq3_v_field(D, 4 * hsel, i, &bit0);  // any token of this half names the field
@@ -390,13 +399,13 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   } else {
     switch (a.lay.d) {
       case 64:
-        hipLaunchKernelGGL(append_tq3_kernel<64>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(append_tq3_kernel<64>, grid, dim3(kAppendWaves * 64), 0, s, a);
         break;
       case 128:
-        hipLaunchKernelGGL(append_tq3_kernel<128>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(append_tq3_kernel<128>, grid, dim3(kAppendWaves * 64), 0, s, a);
         break;
       case 256:
-        hipLaunchKernelGGL(append_tq3_kernel<256>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(append_tq3_kernel<256>, grid, dim3(kAppendWaves * 64), 0, s, a);
         break;
       default:
         return hipErrorInvalidValue;

@@ -122,16 +122,24 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float acc[E];
+  // four partial sums per output (rows j = u mod 4): four independent fma
+  // chains, and the loop unrolled so that many rows of S^T are in flight
+  float acc[4][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int j = 0; j < D; ++j) {
-    const float qj = buf[wave][j];
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(a.s_t[j * D + lane * E + e], qj, acc[e]);
+    for (int e = 0; e < E; ++e) acc[u][e] = 0.0f;
+#pragma unroll 4
+  for (int j = 0; j < D; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float qj = buf[wave][j + u];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[u][e] = fmaf(a.s_t[(j + u) * D + lane * E + e], qj, acc[u][e]);
+    }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) a.q2[vec * D + lane * E + e] = acc[e];
+  for (int e = 0; e < E; ++e) a.q2[vec * D + lane * E + e] = (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
