@@ -479,7 +479,7 @@ def stream_probe(nbytes=2 << 30, runs=10):
     torch.cuda.empty_cache()
     return {"gbs_median": round(nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9, 1),
             "gbs_best": round(nbytes / (ms[0] * 1e-3) / 1e9, 1), "bytes": nbytes, "runs": runs,
-            "kernel": "kv_stream_probe (a contiguous chunk per workgroup, 16-byte loads, 16 steps in flight)"}
+            "kernel": "kv_stream_probe (one workgroup per CU, grid-stride 16-byte loads, 16 steps in flight)"}
 
 
 def with_probe(res, probe):
@@ -608,7 +608,9 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
 SQ_PASSES = ("SQ_WAVES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS "
              "SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_LDS",
              "SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_SALU SQ_INSTS_VMEM_RD "
-             "SQ_LDS_ADDR_CONFLICT SQ_ACTIVE_INST_ANY")
+             "SQ_LDS_ADDR_CONFLICT SQ_ACTIVE_INST_ANY",
+             "SQ_INST_LEVEL_LDS SQ_INSTS_LDS SQ_INST_LEVEL_VMEM SQ_INSTS_VMEM_RD SQ_WAIT_ANY SQ_WAVE_CYCLES "
+             "SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_SCA")
 
 
 def summarize_sq(dirs, workload, cmds, out_path=None):

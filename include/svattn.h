@@ -402,10 +402,10 @@ int kv_trace_events(kv_cache* c, void* before, void* after);
 
 /*
  * Streaming-read probe (measurement aid, not part of the attention path):
- * reads the `bytes` bytes at src once, each workgroup one contiguous chunk
- * with 16-byte loads, every wave 1 KiB of consecutive memory per step, and
- * folds them into one word per workgroup in sink so that no load is
- * elided.  Its duration measures the read bandwidth that a perfect
+ * reads the `bytes` bytes at src once, one workgroup per compute unit
+ * walking the buffer grid-stride with 16-byte loads (every wave 1 KiB of
+ * consecutive memory per load, 16 loads in flight), and folds them into one
+ * word per workgroup in sink so that no load is elided.  Its duration measures the read bandwidth that a perfect
  * single-pass reader of a cache of that size reaches on this GPU.
  *  src: device, 16-byte aligned; bytes: a multiple of 16.
  *  sink: device, at least kv_stream_probe_sink_bytes() bytes.

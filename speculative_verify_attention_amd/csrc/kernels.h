@@ -261,8 +261,8 @@ constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 hipError_t static_scratch(void** out);
 
 // ---- streaming-read probe ------------------------------------------------------------
-// Workgroups of the probe (4 per compute unit); the sink holds one word each.
-constexpr int kProbeWorkgroups = 1024;
+// Workgroups of the probe (one per compute unit); the sink holds one word each.
+constexpr int kProbeWorkgroups = 256;
 hipError_t launch_stream_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments must fit the 4 KiB argument segment");
