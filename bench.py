@@ -663,12 +663,6 @@ def summarize_sq(dirs, workload, cmds, out_path=None):
                       "SQ_ACTIVE_INST_SCA", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
                 if c in g:
                     out.append(f"  {c.lower()[3:] + '_over_wave_cycles':28s} {g[c] / wc:18.4f}")
-        # average latency of an LDS / vector-memory instruction: in-flight
-        # level summed over cycles, over instructions issued
-        for lvl, n, name in (("SQ_INST_LEVEL_LDS", "SQ_INSTS_LDS", "lds"), ("SQ_INST_LEVEL_VMEM", "SQ_INSTS_VMEM_RD",
-                                                                          "vmem_rd")):
-            if g.get(lvl) and g.get(n):
-                out.append(f"  {name + '_latency_cycles':28s} {g[lvl] / g[n]:18.1f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in g:
             out.append(f"  {'mfma_busy_cycles_per_simd':28s} {g['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:18.1f}")
     for name, cs in sorted(other.items()):

@@ -272,7 +272,10 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  *    seq_len - n_rows[i] + r, so the rows' K/V must already be appended.
  *  q: device float32 [sum(n_rows)][num_q_heads][head_dim], rows in the order
  *    of seq_ids.  num_q_heads must be a multiple of num_kv_heads; query head
- *    h reads kv head h / (num_q_heads / num_kv_heads).
+ *    h reads kv head h / (num_q_heads / num_kv_heads).  One call serves at
+ *    most 64 query columns per kv head: max(n_rows) * (num_q_heads /
+ *    num_kv_heads) <= 64 (KV_EINVAL otherwise; e.g. 5 rows at a group of 16
+ *    need two calls).
  *  scale: multiplies <q, k>.  softcap: 0 = off, else s <- softcap *
  *    tanh(s / softcap) after scaling.  window: 0 = full, else position p sees
  *    keys j with 0 <= p - j < window.  Row p never sees keys beyond itself.
@@ -286,9 +289,10 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  * KV_BF16 multiplies the stored bf16 K/V by the query and by the softmax
  * weights, each carried as two bf16 parts (hi + lo, about 2^-17 relative);
  * KV_TQ3 multiplies the exact fp16 code levels and signs by fp16 parts of
- * q', q'' and the weights.
- * Errors: KV_ENOSEQ, KV_EINVAL, KV_ERANGE (n_rows > seq_len), KV_ENOMEM
- * (workspace too small), KV_EDEVICE.
+ * q', q'' and the weights (two parts each, about 2^-21 relative).
+ * Errors: KV_ENOSEQ, KV_EINVAL (bad arguments, more than 64 query columns
+ * per kv head, KV_TQ3 with head_dim 256), KV_ERANGE (n_rows > seq_len),
+ * KV_ENOMEM (workspace too small), KV_EDEVICE.
  */
 int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                      const float* q, int32_t num_q_heads, float scale, float softcap,
