@@ -219,6 +219,41 @@ def test_library_loaded_from_tree():
     assert os.path.dirname(_binding.LIB_PATH) == os.path.join(ROOT, "speculative_verify_attention_amd")
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 * 256 * 16 + 48, 4 << 20])
+def test_stream_probe_reads_every_word(nbytes):
+    # the probe folds every 32-bit word of the buffer into the sink exactly
+    # once (xor), so the xor of the sink words is the xor of the buffer
+    banner(f"kv_stream_probe over {nbytes} bytes")
+    import numpy as np
+
+    from speculative_verify_attention_amd import _binding
+
+    g = torch.Generator(device="cpu")
+    g.manual_seed(nbytes)
+    host = torch.randint(-(1 << 31), (1 << 31) - 1, (nbytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    src = host.cuda()
+    sink = torch.full((_binding.kv_stream_probe_sink_bytes() // 4,), -1, dtype=torch.int32, device="cuda")
+    _binding.kv_stream_probe(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert int(got) == int(want)
+
+
+def test_stream_probe_rejects_bad_arguments():
+    banner("kv_stream_probe argument checks")
+    from speculative_verify_attention_amd import _binding
+
+    src = torch.zeros(64, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(_binding.kv_stream_probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(SvattnError) as ei:
+        _binding.kv_stream_probe(src[:3], sink)  # 12 bytes: not a multiple of 16
+    assert ei.value.code == KV_EINVAL
+    with pytest.raises(SvattnError) as ei:
+        _binding.kv_stream_probe(src, sink[:4])  # sink too small
+    assert ei.value.code == KV_EINVAL
+
+
 # ---- edge cases -----------------------------------------------------------------------
 
 
