@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "qprep.h"
 
 namespace svattn {
 
@@ -298,19 +299,27 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
 // fields by one thread each (one writer per field: no two workgroups race).
 constexpr int kAppendWaves = 8;
 
+// Shared memory of one TQ3 append workgroup.  S^T is staged in LDS once per
+// workgroup for d <= 128 (64 KiB), so the projections of the key residuals
+// read LDS instead of L2.
 template <int D>
-__global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_kernel(AppendArgs a) {
+struct AppendTq3Smem {
+  static constexpr bool kStage = D <= 128;
+  double rbuf[kAppendWaves][D];
+  uint8_t vcode[32][D];
+  float st_lds[kStage ? D * D : 4];
+  uint32_t sat_any;
+};
+
+template <int D>
+__device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, int h, AppendTq3Smem<D>& sm) {
   constexpr int E = D / 64;
   constexpr int SB = tq3_sub_bytes(D);
-  // S^T staged in LDS once per workgroup for d <= 128 (64 KiB), so the
-  // projections of the key residuals read LDS instead of L2
-  constexpr bool kStage = D <= 128;
-  __shared__ double rbuf[kAppendWaves][D];
-  __shared__ uint8_t vcode[32][D];
-  __shared__ __align__(16) float st_lds[kStage ? D * D : 4];
-  __shared__ uint32_t sat_any;
-  const int unit = blockIdx.x;
-  const int h = blockIdx.y;
+  constexpr bool kStage = AppendTq3Smem<D>::kStage;
+  auto& rbuf = sm.rbuf;
+  auto& vcode = sm.vcode;
+  float* st_lds = sm.st_lds;
+  uint32_t& sat_any = sm.sat_any;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sat_any = 0;
@@ -387,6 +396,50 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_kernel(AppendArg
     for (int b = 0; b < 6; ++b) p[b] = (uint8_t)(field >> (8 * b));
   }
   if (threadIdx.x == 0 && sat_any) atomicOr(a.status, 1u);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_kernel(AppendArgs a) {
+  __shared__ __align__(16) AppendTq3Smem<D> sm;
+  append_tq3_block<D>(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// A decode step's two small launches of the compressed path in one: the
+// first n_app workgroups encode the appended rows (workgroup b: unit b / hkv,
+// kv head b % hkv), the rest rotate the queries, eight vectors per
+// workgroup.  The two jobs touch disjoint memory and run side by side.
+template <int D>
+__global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_qprep_kernel(AppendArgs a, QPrepArgs q,
+                                                                            int32_t n_app) {
+  __shared__ __align__(16) AppendTq3Smem<D> sm;
+  const int b = blockIdx.x;
+  if (b < n_app) {
+    append_tq3_block<D>(a, b / a.lay.hkv, b % a.lay.hkv, sm);
+    return;
+  }
+  const int wave = threadIdx.x >> 6;
+  const int64_t vec = (int64_t)(b - n_app) * kAppendWaves + wave;
+  if (vec < q.n_vec) qprep_vector<D>(q, vec, reinterpret_cast<float*>(sm.rbuf[wave]));
+}
+
+hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStream_t s) {
+  if (a.lay.fmt != 2 || q.d != a.lay.d) return hipErrorInvalidValue;
+  const int64_t n_app = (int64_t)a.total_units * a.lay.hkv;
+  const int64_t n_q = (q.n_vec + kAppendWaves - 1) / kAppendWaves;
+  if (n_app + n_q <= 0) return hipSuccess;
+  if (n_app + n_q > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(n_app + n_q)), block(kAppendWaves * 64);
+  switch (a.lay.d) {
+    case 64:
+      hipLaunchKernelGGL(append_tq3_qprep_kernel<64>, grid, block, 0, s, a, q, (int32_t)n_app);
+      break;
+    case 128:
+      hipLaunchKernelGGL(append_tq3_qprep_kernel<128>, grid, block, 0, s, a, q, (int32_t)n_app);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {

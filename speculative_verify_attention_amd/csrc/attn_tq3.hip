@@ -30,6 +30,7 @@
 
 #include "attn_common.h"
 #include "kernels.h"
+#include "qprep.h"
 
 // Query-fragment parts held in registers (the others are read from LDS at
 // every use: the register budget of two waves per SIMD) and the depth of the
@@ -76,70 +77,16 @@ __device__ __forceinline__ u32x2_t split_f16_prod(float p0, float n0, float p1, 
   return u32x2_t{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
 }
 
-// ---- query rotation --------------------------------------------------------------
+// ---- query rotation ---------------------------------------------------------------
 
-// One wave per query vector: q' = H (D q) / sqrt(d) with an in-register
-// Walsh-Hadamard transform, then q'' = S q' (S read transposed, coalesced).
+// One wave per query vector (qprep_vector in qprep.h), four per workgroup.
 template <int D>
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
-  constexpr int E = D / 64;
   __shared__ float buf[4][D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int64_t vec = (int64_t)blockIdx.x * 4 + wave;
   if (vec >= a.n_vec) return;
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = lane * E + e;
-    const float x = a.q[vec * D + i];
-    v[e] = a.signs[i] < 0 ? -x : x;
-  }
-#pragma unroll
-  for (int h = 1; h < E; h <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (!(e & h)) {
-        const float x = v[e], y = v[e + h];
-        v[e] = x + y;
-        v[e + h] = x - y;
-      }
-#pragma unroll
-  for (int hl = 1; hl < 64; hl <<= 1) {
-    const bool upper = (lane & hl) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float p = __shfl_xor(v[e], hl);
-      v[e] = upper ? (p - v[e]) : (v[e] + p);
-    }
-  }
-  const float inv = 1.0f / sqrtf((float)D);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    v[e] *= inv;
-    a.q1[vec * D + lane * E + e] = v[e];
-    buf[wave][lane * E + e] = v[e];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // four partial sums per output (rows j = u mod 4): four independent fma
-  // chains, and the loop unrolled so that many rows of S^T are in flight
-  float acc[4][E];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[u][e] = 0.0f;
-#pragma unroll 4
-  for (int j = 0; j < D; j += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float qj = buf[wave][j + u];
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[u][e] = fmaf(a.s_t[(j + u) * D + lane * E + e], qj, acc[u][e]);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) a.q2[vec * D + lane * E + e] = (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
+  qprep_vector<D>(a, vec, buf[wave]);
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {

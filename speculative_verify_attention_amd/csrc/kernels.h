@@ -275,6 +275,8 @@ hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s);
 // TQ3: the query rotation, and the partial kernel (two-part (hi + lo) fp16
 // operands).
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
+// One launch that encodes a TQ3 append (a) and rotates the queries (q).
+hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStream_t s);
 hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s);
 // Acceptance: row statistics over every row (once per call), then decide and
 // draw for one group of up to kMaxAcceptSeqs sequences.

@@ -205,8 +205,11 @@ namespace {
 
 // Enqueue a planned append (table updates, then the slice-update or
 // quantize-on-append launches) without committing it to the host state.
+// qp (TQ3, optional): the queries' rotation, launched together with the last
+// append launch; *qp_done tells whether it was (not when nothing is stored).
 int enqueue_append(kv_cache* c, const AppendPlan& plan, const std::vector<int32_t>& slack, const void* k,
-                   const void* v, hipStream_t s) {
+                   const void* v, hipStream_t s, const QPrepArgs* qp = nullptr, bool* qp_done = nullptr) {
+  if (qp_done) *qp_done = false;
   // 1. new blocks become visible in the device table
   int rc = enqueue_table_updates(c, plan, s);
   if (rc != KV_OK) return rc;
@@ -272,8 +275,10 @@ int enqueue_append(kv_cache* c, const AppendPlan& plan, const std::vector<int32_
       for (int j = 0; j < 8; ++j) a.lev16[j] = cd.levels16[j];
       a.status = c->dstatus;
     }
-    hipError_t e = launch_append(a, s);
+    const bool with_q = tq3 && qp && i == segs.size();
+    hipError_t e = with_q ? launch_append_qprep(a, *qp, s) : launch_append(a, s);
     if (e != hipSuccess) return hip_fail(c, e, "append launch");
+    if (with_q && qp_done) *qp_done = true;
   }
   return KV_OK;
 }
@@ -457,30 +462,39 @@ int enqueue_table_updates(kv_cache* c, const AppendPlan& plan, hipStream_t s) {
   return KV_OK;
 }
 
+// TQ3: the rotation of a verify call's queries; q' = Pi q and q'' = S q'
+// live in the workspace after the partials.
+QPrepArgs make_qprep(const kv_cache* c, const VerifyPlan& vp, const float* q, int32_t num_q_heads, void* workspace) {
+  QPrepArgs qa;
+  qa.q = q;
+  qa.q1 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes);
+  qa.q2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes + vp.q_bytes);
+  qa.signs = c->dsigns;
+  qa.s_t = c->ds_t;
+  qa.n_vec = (int32_t)(vp.rows * num_q_heads);
+  qa.d = c->core.params().head_dim;
+  return qa;
+}
+
 // Enqueue a planned verify call.  added / new_k / new_v: a fused append of
 // the verified rows (plain formats; the table already holds their blocks),
-// else null.
+// else null.  rotated: TQ3 queries already rotated into the workspace.
 int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                    const int32_t* added, const float* q, int32_t num_q_heads, float scale, float softcap,
-                   int32_t window, float* out, void* workspace, hipStream_t s, const void* new_k, const void* new_v) {
+                   int32_t window, float* out, void* workspace, hipStream_t s, const void* new_k, const void* new_v,
+                   bool rotated = false) {
   const CoreParams& P = c->core.params();
   const bool tq3 = P.format == KV_TQ3;
-  // TQ3: the rotated queries q' = Pi q and q'' = S q' live after the partials
   float* q1 = nullptr;
   float* q2 = nullptr;
   if (tq3) {
-    q1 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes);
-    q2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + vp.part_bytes + vp.q_bytes);
-    QPrepArgs qa;
-    qa.q = q;
-    qa.q1 = q1;
-    qa.q2 = q2;
-    qa.signs = c->dsigns;
-    qa.s_t = c->ds_t;
-    qa.n_vec = (int32_t)(vp.rows * num_q_heads);
-    qa.d = P.head_dim;
-    hipError_t e = launch_qprep(qa, s);
-    if (e != hipSuccess) return hip_fail(c, e, "query rotation launch");
+    const QPrepArgs qa = make_qprep(c, vp, q, num_q_heads, workspace);
+    q1 = qa.q1;
+    q2 = qa.q2;
+    if (!rotated) {
+      hipError_t e = launch_qprep(qa, s);
+      if (e != hipSuccess) return hip_fail(c, e, "query rotation launch");
+    }
   }
   const int g = num_q_heads / P.num_kv_heads;
   std::vector<AttnArgs> args(vp.launches.size());
@@ -640,10 +654,14 @@ int kv_append_verify(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
     // the append's launches, then the verify planned with the appended
     // lengths; the host state moves only once both are enqueued
     if (plan.total_rows > (int64_t)INT32_MAX / 8) return set_err(c, KV_EINVAL, "append too large");
-    rc = enqueue_append(c, plan, slack, k, v, s);
+    // TQ3: the queries are rotated in the append's (last) launch, beside the
+    // encode
+    const QPrepArgs qa = make_qprep(c, vp, q, num_q_heads, workspace);
+    bool rotated = false;
+    rc = enqueue_append(c, plan, slack, k, v, s, P.format == KV_TQ3 ? &qa : nullptr, &rotated);
     if (rc != KV_OK) return rc;
     rc = enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, n_rows, q, num_q_heads, scale, softcap, window, out,
-                        workspace, s, nullptr, nullptr);
+                        workspace, s, nullptr, nullptr, rotated);
     if (rc != KV_OK) return rc;
     c->core.commit_append(plan);
     return KV_OK;
