@@ -286,14 +286,21 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
   // The probabilities carry the value norms into fp16 products: they may
   // reach the lazy reference's 2^8 only while every value norm of the
   // sub-tile is at most 240, else the reference moves to the sub-tile's
-  // maximum (probabilities <= 1), so that p * n16v stays finite.
-  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-  f16x2_t nv2 = __builtin_bit_cast(f16x2_t, vw[0]);
+  // maximum (probabilities <= 1), so that p * n16v stays finite.  The norms
+  // are non-negative fp16 (saturated at 65504), which order as 16-bit
+  // integers: 240 is 0x5B80.  Every lane holds the norms of half the
+  // sub-tile's keys, so one ballot over the wave covers all of them.
+  typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+  u16x2_t nv[8];
 #pragma unroll
-  for (int q = 1; q < 8; ++q) nv2 = __builtin_elementwise_max(nv2, __builtin_bit_cast(f16x2_t, vw[q]));
-  float nvmax = fmaxf((float)nv2[0], (float)nv2[1]);
-  nvmax = fmaxf(nvmax, xor32(nvmax));
-  softmax_update<D, 1>(cs, p, nvmax <= 240.0f ? 8.0f : 0.0f, smul);
+  for (int q = 0; q < 8; ++q) nv[q] = __builtin_bit_cast(u16x2_t, vw[q]);
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)  // tree: no chain of dependent packed operations
+#pragma unroll
+    for (int q = 0; q < w; ++q) nv[q] = __builtin_elementwise_max(nv[q], nv[q + w]);
+  const u16x2_t nv2 = nv[0];
+  const bool big = __builtin_amdgcn_ballot_w64(nv2[0] > 0x5B80u || nv2[1] > 0x5B80u) != 0;
+  softmax_update<D, 1>(cs, p, big ? 0.0f : 8.0f, smul);
   __builtin_amdgcn_s_setprio(1);
   // O'^T += C16[vcode]^T (P * n16v)^T; the merge applies 1/sqrt(d)
 #pragma unroll
@@ -359,14 +366,24 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   const int head_j = col_ok ? c - row_i * a.g : 0;
   const int ppos = L - n + row_i;
 
-  // the table is read through the constant address space, so that its reads
-  // are scalar loads; a vector load here would be followed by a wait for
-  // every load in flight, the prefetched sub-tiles included
-  typedef __attribute__((address_space(4))) const int32_t cint32_t;
-  cint32_t* trow = (cint32_t*)(a.table + (int64_t)ch.seq * a.max_bps);
+  // Block-table entries of 64 consecutive blocks from tb, one per lane: a
+  // sub-tile's block is then a lane read, with no memory round trip in the
+  // loop (a scalar load there waits on the counter it shares with the LDS
+  // reads, draining them).  Each wave visits its blocks in ascending order
+  // and reloads the 64 entries when it moves past them.
+  const int32_t* trow = a.table + (int64_t)ch.seq * a.max_bps;
+  auto tab_load = [&](int b0) { return trow[min(b0 + lane, a.max_bps - 1)]; };
+  int tb = (tlo + ch.t_begin) >> 3;
+  int tab = tab_load(tb);
   auto sub_of = [&](int t) {
     const int key0 = (tlo + t) * 32;
-    return a.pool + (int64_t)trow[key0 >> 8] * a.lay.block_bytes + ((int64_t)h * 8 + ((key0 & 255) >> 5)) * SB;
+    const int blk = key0 >> 8;
+    if (blk - tb >= 64) {
+      tb = blk;
+      tab = tab_load(tb);
+    }
+    const int e = __builtin_amdgcn_readlane(tab, blk - tb);
+    return a.pool + (int64_t)e * a.lay.block_bytes + ((int64_t)h * 8 + ((key0 & 255) >> 5)) * SB;
   };
   const int t_first = ch.t_begin + tl;
   const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
