@@ -369,8 +369,8 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   // Block-table entries of 64 consecutive blocks from tb, one per lane: a
   // sub-tile's block is then a lane read, with no memory round trip in the
   // loop (a scalar load there waits on the counter it shares with the LDS
-  // reads, draining them).  Each wave visits its blocks in ascending order
-  // and reloads the 64 entries when it moves past them.
+  // reads, draining them).  The entries are reloaded whenever a block falls
+  // outside [tb, tb + 64); each wave visits its blocks in ascending order.
   const int32_t* trow = a.table + (int64_t)ch.seq * a.max_bps;
   auto tab_load = [&](int b0) { return trow[min(b0 + lane, a.max_bps - 1)]; };
   int tb = (tlo + ch.t_begin) >> 3;
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   auto sub_of = [&](int t) {
     const int key0 = (tlo + t) * 32;
     const int blk = key0 >> 8;
-    if (blk - tb >= 64) {
+    if ((unsigned)(blk - tb) >= 64u) {
       tb = blk;
       tab = tab_load(tb);
     }
