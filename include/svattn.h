@@ -272,10 +272,12 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  *    seq_len - n_rows[i] + r, so the rows' K/V must already be appended.
  *  q: device float32 [sum(n_rows)][num_q_heads][head_dim], rows in the order
  *    of seq_ids.  num_q_heads must be a multiple of num_kv_heads; query head
- *    h reads kv head h / (num_q_heads / num_kv_heads).  One call serves at
- *    most 64 query columns per kv head: max(n_rows) * (num_q_heads /
- *    num_kv_heads) <= 64 (KV_EINVAL otherwise; e.g. 5 rows at a group of 16
- *    need two calls).
+ *    h reads kv head h / (num_q_heads / num_kv_heads).  The kernels hold
+ *    at most 64 query columns (rows x group heads) of a kv head at once;
+ *    beyond that (e.g. 5 rows at a group of 16) the call splits each group
+ *    into the fewest equal slices of heads that fit and runs one pass of
+ *    launches per slice, so the cache is read once per slice and the
+ *    workspace holds one set of partials per slice.
  *  scale: multiplies <q, k>.  softcap: 0 = off, else s <- softcap *
  *    tanh(s / softcap) after scaling.  window: 0 = full, else position p sees
  *    keys j with 0 <= p - j < window.  Row p never sees keys beyond itself.
@@ -290,8 +292,8 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  * weights, each carried as two bf16 parts (hi + lo, about 2^-17 relative);
  * KV_TQ3 multiplies the exact fp16 code levels and signs by fp16 parts of
  * q', q'' and the weights (two parts each, about 2^-21 relative).
- * Errors: KV_ENOSEQ, KV_EINVAL (bad arguments, more than 64 query columns
- * per kv head, KV_TQ3 with head_dim 256), KV_ERANGE (n_rows > seq_len),
+ * Errors: KV_ENOSEQ, KV_EINVAL (bad arguments, KV_TQ3 with head_dim 256),
+ * KV_ERANGE (n_rows > seq_len),
  * KV_ENOMEM (workspace too small), KV_EDEVICE.
  */
 int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,

@@ -63,8 +63,11 @@ int svcore_half_bits(double x, uint16_t* out, int32_t* saturated);
  * tiles, one partial slot per workgroup, row offsets, workspace bytes.
  * pending: max_seqs device rollbacks not yet read back (null: none); fused:
  * nonzero plans kv_append_verify (the rows are appended first).
- * summary[6] receives: column groups, launches, partial slots, workspace
- * bytes, partial bytes, rotated-query bytes.  ksplit (n_seqs entries, call
+ * summary[7] receives: column groups, launches (per head slice), partial
+ * slots (per head slice), workspace bytes, partial bytes, rotated-query
+ * bytes, head slices (the query heads of a kv head are split into this many
+ * slices, each verified by its own launches, when rows x group heads
+ * exceeds 64).  ksplit (n_seqs entries, call
  * order, or null) receives the chunks per kv head of each entry.
  * Returns 0, the status codes of spec_verify_attn's argument checks, or -5
  * when the plan breaks an invariant (svcore_last_error says which).

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256, (FMT == 1 && D <= 128) ? SVATTN_BF16_WAVES : 1
     }
   }
 
-  const float* qsrc = a.q + ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
+  const float* qsrc = a.q + ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D;
   QOperand<FMT, D> qop;
   if constexpr (FMT == 1) {
     if (tl == 0) QOperand<1, D>::store(qlds + ct * QOperand<1, D>::LDS_ENTRIES, qsrc, col_ok, lane);
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
     for (int e = 0; e < EL; ++e) acc[e] *= (a.signs[lane * EL + e] < 0 ? -inv_d : inv_d);
   }
   const int row_i = c / a.g, head_j = c - row_i * a.g;
-  float* o = a.out + ((int64_t)(q0 + row_i) * a.hq + h * a.g + head_j) * D + lane * EL;
+  float* o = a.out + ((int64_t)(q0 + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D + lane * EL;
 #pragma unroll
   for (int e = 0; e < EL; ++e) o[e] = acc[e];
 }

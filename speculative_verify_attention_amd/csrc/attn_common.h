@@ -234,7 +234,7 @@ __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, 
   if (tl == 0 && col_ok) {
     if (k == 1 && !a.force_partial) {
       const float inv = 1.0f / cs.l;
-      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.g + head_j) * D;
+      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

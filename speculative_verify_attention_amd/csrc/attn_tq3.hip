@@ -415,7 +415,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
       vlut[idx] = lv[e & 7] | (lv[e >> 3] << 16);
     }
     // query fragments of this wave's column group: k-steps tl, tl + TL, ...
-    const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.g + head_j) * D;
+    const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D;
     for (int kk = tl; kk < D / 16; kk += TL) {
       u32x4_t h1{}, l1{}, h2{}, l2{};  // fp16 pairs
       if (col_ok) {

@@ -167,7 +167,9 @@ struct AttnArgs {
   float* out;        // [rows][hq][d]
   float* part;       // partial slots
   PoolLayout lay;
-  int32_t hq, g, max_bps, window;
+  // g: query heads of a kv head this launch serves (one head slice);
+  // query head of column head j of kv head h = h * gq + head0 + j
+  int32_t hq, g, gq, head0, max_bps, window;
   float scale;       // multiplies <q, k>
   float softcap;     // 0 = off
   float inv_softcap;

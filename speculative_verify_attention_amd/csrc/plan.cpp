@@ -47,8 +47,12 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
     max_rows = std::max(max_rows, (int)n_rows[i]);
     vp->rows += n_rows[i];
   }
-  const int R = max_rows * g;
-  if (R > 64) return fail(KV_EINVAL, "n_rows * (num_q_heads / num_kv_heads) must be <= 64");
+  // head slices: the fewest that bring a slice's columns to 64 or fewer
+  // (hs = g always works: one head per slice, at most 8 rows)
+  vp->hs = 1;
+  while (g % vp->hs || max_rows * (g / vp->hs) > 64) ++vp->hs;
+  vp->gs = g / vp->hs;
+  const int R = max_rows * vp->gs;
   vp->nct = R > 32 ? 2 : 1;
   vp->rpad = 32 * vp->nct;
   vp->slot_stride = (int64_t)vp->rpad * (2 + P.head_dim);
@@ -99,7 +103,7 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
     vp->slots += L.n_wg;
     vp->launches.push_back(std::move(L));
   }
-  vp->part_bytes = align_up((size_t)vp->slots * vp->slot_stride * 4);
+  vp->part_bytes = align_up((size_t)vp->hs * vp->slots * vp->slot_stride * 4);
   if (P.format == KV_TQ3) vp->q_bytes = align_up((size_t)vp->rows * num_q_heads * P.head_dim * 4);
   vp->total = vp->part_bytes + 2 * vp->q_bytes;
 #ifdef SVATTN_CHECKED
@@ -128,10 +132,16 @@ std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, co
     rows += n_rows[i];
   }
   if (vp.rows != rows) return "rows " + str(vp.rows) + " != " + str(rows);
+  // head slices: hs x gs = g, a slice's columns fit two 32-column groups,
+  // and no smaller number of slices would do
+  if (vp.hs < 1 || vp.gs < 1 || vp.hs * vp.gs != g) return "head slices " + str(vp.hs) + " x " + str(vp.gs);
+  if (max_rows * vp.gs > 64) return "slice columns " + str(max_rows * vp.gs);
+  for (int h2 = 1; h2 < vp.hs; ++h2)
+    if (g % h2 == 0 && max_rows * (g / h2) <= 64) return "fewer head slices would do: " + str(h2);
   if (vp.nct != 1 && vp.nct != 2) return "column groups " + str(vp.nct);
   if (vp.rpad != 32 * vp.nct) return "padded columns " + str(vp.rpad);
-  if (max_rows * g > vp.rpad || (vp.nct == 2 && max_rows * g <= 32))
-    return "columns " + str(max_rows * g) + " vs " + str(vp.rpad);
+  if (max_rows * vp.gs > vp.rpad || (vp.nct == 2 && max_rows * vp.gs <= 32))
+    return "columns " + str(max_rows * vp.gs) + " vs " + str(vp.rpad);
   if (vp.slot_stride != (int64_t)vp.rpad * (2 + P.head_dim)) return "slot stride";
   // row offsets: prefix sums of the row counts, in call order
   if ((int)vp.qrow0.size() != n_seqs) return "qrow0 size";
@@ -153,10 +163,11 @@ std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, co
     if (ci < 0 || ci >= n_seqs || seen[ci]++) return "order is not a permutation at " + str(i);
     if (i > 0 && nt[vp.order[i - 1]] < nt[ci]) return "order not longest first at " + str(i);
   }
-  // launches: consecutive runs of at most kMaxAttnSeqs sequences; inside one,
-  // sequence i owns workgroups wg_base[i] .. wg_base[i+1]-1, ksplit[i] chunks
-  // per kv head, each chunk a non-empty run of tiles, one partial slot per
-  // workgroup
+  // launches (of one head slice; every slice repeats them with its own
+  // block of `slots` partial slots): consecutive runs of at most
+  // kMaxAttnSeqs sequences; inside one, sequence i owns workgroups
+  // wg_base[i] .. wg_base[i+1]-1, ksplit[i] chunks per kv head, each chunk a
+  // non-empty run of tiles, one partial slot per workgroup
   int first = 0;
   int64_t slot = 0;
   for (size_t li = 0; li < vp.launches.size(); ++li) {
@@ -182,7 +193,7 @@ std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, co
   if (vp.slots != slot) return "slots";
   // workspace: partial slots, then (compressed caches) two rotated copies of
   // the queries
-  if (vp.part_bytes != align_up((size_t)vp.slots * vp.slot_stride * 4)) return "partial bytes";
+  if (vp.part_bytes != align_up((size_t)vp.hs * vp.slots * vp.slot_stride * 4)) return "partial bytes";
   const size_t q = P.format == KV_TQ3 ? align_up((size_t)rows * num_q_heads * P.head_dim * 4) : 0;
   if (vp.q_bytes != q) return "query bytes";
   if (vp.total != vp.part_bytes + 2 * vp.q_bytes) return "total bytes";

@@ -51,8 +51,14 @@ struct VerifyLaunch {
   std::vector<int32_t> ksplit, wg_base;
 };
 
+// Query columns of a (sequence, kv head) pair are rows x group heads.  More
+// than 64 (two 32-column groups) are served by splitting the group's heads
+// into hs slices of gs heads each, gs the largest divisor of the group with
+// max rows x gs <= 64; each slice is its own set of launches over the same
+// keys, with its own partial slots.
 struct VerifyPlan {
   int nct = 1, rpad = 32;
+  int hs = 1, gs = 1;          // head slices and query heads per slice
   std::vector<int> order;      // call index of the i-th sequence handed to the kernels
   std::vector<int32_t> qrow0;  // first query/output row of each call index
   int64_t slot_stride = 0, slots = 0, rows = 0;

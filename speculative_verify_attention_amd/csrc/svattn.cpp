@@ -497,11 +497,16 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
     }
   }
   const int g = num_q_heads / P.num_kv_heads;
-  std::vector<AttnArgs> args(vp.launches.size());
-  std::vector<char> split(vp.launches.size(), 0);
-  for (size_t li = 0; li < vp.launches.size(); ++li) {
-    const VerifyLaunch& L = vp.launches[li];
-    AttnArgs& a = args[li];
+  // one set of launches per head slice, each over its own block of partial
+  // slots; the fused append rides on the first slice only (the later
+  // slices' launches follow it on the stream and read the rows it stored)
+  const size_t nl = vp.launches.size();
+  std::vector<AttnArgs> args(vp.hs * nl);
+  std::vector<char> split(args.size(), 0);
+  for (size_t ai = 0; ai < args.size(); ++ai) {
+    const int slice = (int)(ai / nl);
+    const VerifyLaunch& L = vp.launches[ai % nl];
+    AttnArgs& a = args[ai];
     std::memset(&a, 0, sizeof(a));
     a.pool = c->pool;
     a.table = c->dtable;
@@ -516,10 +521,12 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
     a.inv_cap_l2 = softcap > 0.0f ? (float)(1.0 / ((double)softcap * M_LOG2E)) : 0.0f;
     for (int j = 0; j < 8; ++j) a.lev16_bits[j] = tq3 ? c->core.codec().levels16_bits[j] : 0;
     a.out = out;
-    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace)) + L.slot0 * vp.slot_stride;
+    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace)) + (slice * vp.slots + L.slot0) * vp.slot_stride;
     a.lay = c->lay;
     a.hq = num_q_heads;
-    a.g = g;
+    a.g = vp.gs;
+    a.gq = g;
+    a.head0 = slice * vp.gs;
     a.max_bps = P.max_blocks_per_seq;
     a.window = window;
     a.scale = scale;
@@ -532,8 +539,8 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
     a.force_partial = tq3 ? 1 : 0;  // the merge rotates TQ3 outputs back
     a.tile_keys = tile_keys(P.format, P.head_dim);
     a.roll = c->any_pend ? c->droll : nullptr;
-    a.new_k = new_k;
-    a.new_v = new_v;
+    a.new_k = slice == 0 ? new_k : nullptr;
+    a.new_v = slice == 0 ? new_v : nullptr;
     bool any_split = tq3;
     for (int i = 0; i < L.count; ++i) {
       const int ci = vp.order[L.first + i];
@@ -548,7 +555,7 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
       if (L.ksplit[i] > 1) any_split = true;
     }
     for (int i = 0; i <= L.count; ++i) a.wg_base[i] = L.wg_base[i];
-    split[li] = any_split ? 1 : 0;
+    split[ai] = any_split ? 1 : 0;
   }
   hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, s);

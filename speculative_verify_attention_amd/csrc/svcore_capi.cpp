@@ -129,6 +129,7 @@ int svcore_plan_verify(svcore* c, int32_t n_seqs, const int32_t* seq_ids, const 
   summary[3] = (int64_t)vp.total;
   summary[4] = (int64_t)vp.part_bytes;
   summary[5] = (int64_t)vp.q_bytes;
+  summary[6] = vp.hs;
   if (ksplit)
     for (const VerifyLaunch& L : vp.launches)
       for (int i = 0; i < L.count; ++i) ksplit[vp.order[L.first + i]] = L.ksplit[i];

@@ -158,6 +158,9 @@ CASES = [
     ("bf16_d64_two_groups", KV_BF16, 24, 2, 64, [255, 90], [(0, 0.0)]),
     ("tq3_d128", KV_TQ3, 8, 2, 128, [250, 509, 33], [(0, 0.0)]),
     ("tq3_d64_window", KV_TQ3, 8, 1, 64, [700, 40], [(64, 0.0)]),
+    # a group of 16: steps with 5 rows split the heads into two slices
+    ("bf16_g16_head_slices", KV_BF16, 32, 2, 128, [250, 700, 31], [(0, 0.0)]),
+    ("tq3_g16_head_slices", KV_TQ3, 32, 2, 128, [300, 90], [(0, 0.0)]),
 ]
 
 

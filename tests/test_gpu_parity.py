@@ -281,6 +281,12 @@ EDGE = [
     ("sharp_fp32_queries", 32, 8, 128, KV_BF16, [3000, 500], [5, 5], 0, 0.0, 4.0),
     ("sharp_fp32_queries_d256", 8, 1, 256, KV_BF16, [2000], [5], 0, 0.0, 3.0),
     ("sharp_fp32_queries_d64", 16, 4, 64, KV_BF16, [1500], [4], 0, 0.0, 5.0),
+    # more than 64 query columns per kv head: the call splits the group's
+    # heads into slices (5 x 16 = 80 -> 2 x 8 heads; 8 x 12 = 96 -> 2 x 6;
+    # 8 x 64 = 512 -> 8 x 8, with a window, a cap and sharp scores)
+    ("head_slices_g16", 32, 2, 128, KV_BF16, [900, 300], [5, 4], 0, 0.0, 1.0),
+    ("head_slices_g12_fp32", 12, 1, 64, KV_FP32, [400, 9], [8, 8], 0, 0.0, 1.0),
+    ("head_slices_g64_window_cap", 64, 1, 128, KV_BF16, [700, 20], [8, 3], 100, 30.0, 2.0),
 ]
 
 

@@ -192,6 +192,9 @@ EDGE = [
     # fields) and more than one launch
     ("many_seqs", 8, 2, 64, [int(x) for x in np.linspace(1, 700, 140)], [2] * 140, 0, 0.0, 1.0),
     ("single_pair_long", 8, 1, 128, [30000], [5], 0, 0.0, 1.0),
+    # more than 64 query columns per kv head: head slices
+    ("head_slices_g16", 32, 2, 128, [1500, 90], [5, 3], 0, 0.0, 1.0),
+    ("head_slices_g64", 64, 1, 64, [600], [8], 0, 0.0, 2.0),
     # many query vectors (60 sequences x 1..5 rows x 32 heads, about 5,800)
     # for value-dependent rounding cases such as exact fp16 ties
     ("stress_short", 32, 8, 128, np.random.default_rng(60).integers(1, 1500, size=60).tolist(),

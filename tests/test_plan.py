@@ -50,7 +50,7 @@ class HostCore:
         n = len(seqs)
         a = (ctypes.c_int32 * n)(*seqs)
         r = (ctypes.c_int32 * n)(*rows)
-        summ = (ctypes.c_int64 * 6)()
+        summ = (ctypes.c_int64 * 7)()
         ks = (ctypes.c_int32 * n)()
         pend = None if pending is None else (ctypes.c_int32 * len(pending))(*pending)
         rc = self.lib.svcore_plan_verify(self.h, n, a, r, hq, window, pend, 1 if fused else 0, summ, ks)
@@ -67,7 +67,7 @@ def align(x):
 
 
 def expected_valid(lens, seqs, rows, g, window, pending, fused):
-    if max(rows) * g > 64 or min(rows) < 1 or max(rows) > 8:
+    if min(rows) < 1 or max(rows) > 8:
         return False
     for s, n in zip(seqs, rows):
         up = lens[s] + (n if fused else 0)
@@ -82,7 +82,7 @@ def batches(draw):
     hkv = draw(st.sampled_from([1, 2, 8]))
     d = draw(st.sampled_from([64, 128, 256]))
     fmt = draw(st.sampled_from([0, 1, 2]))
-    g = draw(st.sampled_from([1, 2, 4, 8, 16]))
+    g = draw(st.sampled_from([1, 2, 4, 8, 12, 13, 16, 64]))
     n = draw(st.integers(1, 300))
     long_ = draw(st.booleans())
     hi = 120000 if long_ else 3000
@@ -109,8 +109,11 @@ def test_plans_hold_their_invariants(b):
         if rc != KV_OK:
             assert rc in (KV_EINVAL, KV_ERANGE)
             return
-        nct, launches, slots, total, part, qb = summ
-        assert nct == (2 if max(rows) * g > 32 else 1)
+        nct, launches, slots, total, part, qb, hs = summ
+        # head slices: the fewest equal slices of the group whose columns fit 64
+        hs_want = min(h for h in range(1, g + 1) if g % h == 0 and max(rows) * (g // h) <= 64)
+        assert hs == hs_want
+        assert nct == (2 if max(rows) * (g // hs) > 32 else 1)
         assert launches == math.ceil(len(seqs) / 128)
         tk = tile_keys(fmt, d)
         n_tiles = []
@@ -122,7 +125,7 @@ def test_plans_hold_their_invariants(b):
         for t, k in zip(n_tiles, ks):
             assert 1 <= k <= t
         assert slots == sum(k * hkv for k in ks)
-        assert part == align(slots * 32 * nct * (2 + d) * 4)
+        assert part == align(hs * slots * 32 * nct * (2 + d) * 4)
         assert qb == (align(sum(rows) * hkv * g * d * 4) if fmt == 2 else 0)
         assert total == part + 2 * qb
     finally:
@@ -170,11 +173,25 @@ def test_launch_boundaries(n):
         c.close()
 
 
-def test_rows_times_group_limit():
-    c = HostCore(2, 128, 1, [100, 100])
+@pytest.mark.parametrize(
+    "hkv,hq,rows,hs,nct",
+    [
+        (2, 32, [4, 4], 1, 2),   # 4 x 16 = 64 columns: one pass
+        (2, 32, [5, 4], 2, 2),   # 5 x 16 = 80: two slices of 8 heads (40 columns)
+        (1, 12, [8], 2, 2),      # 8 x 12 = 96: two slices of 6 heads (48)
+        (1, 64, [8, 1], 8, 2),   # 8 x 64 = 512: eight slices of 8 heads (64)
+        (1, 64, [3], 4, 2),      # 3 x 64 = 192: four slices of 16 heads (48)
+        (1, 7, [8], 1, 2),       # 8 x 7 = 56: fits
+        (1, 14, [8], 2, 2),      # 8 x 14 = 112: two slices of 7 (56)
+        (1, 13, [5], 13, 1),     # a prime group of 13 x 5 rows = 65: one head per slice
+    ],
+)
+def test_head_slices(hkv, hq, rows, hs, nct):
+    c = HostCore(hkv, 128, 1, [100] * len(rows))
     try:
-        assert c.plan([0, 1], [4, 4], 32)[0] == KV_OK  # 4 x 16 = 64 columns
-        rc, _, _, err = c.plan([0, 1], [5, 4], 32)  # 5 x 16 = 80
-        assert rc == KV_EINVAL and "64" in err
+        rc, summ, _, err = c.plan(list(range(len(rows))), rows, hq)
+        assert rc == KV_OK, err
+        assert summ[6] == hs and summ[0] == nct
+        assert summ[4] == align(hs * summ[2] * 32 * nct * (2 + 128) * 4)
     finally:
         c.close()
