@@ -317,10 +317,12 @@ def cpu_baseline(wl, layers, budget_s=10.0):
 def run(args, name):
     import torch
 
-    from speculative_verify_attention_amd import synth
+    from speculative_verify_attention_amd import kv_workspace_bytes_valu, synth
     from speculative_verify_attention_amd.runner import Runner, alg_bytes_per_call
 
     wl, layers = workloads()[name]()
+    if args.valu:
+        args.separate = True  # the vector-unit verify has no fused-append form
     layers = layers or [(wl.window, wl.softcap)]
     total_steps = args.warmup + args.steps
     wl.steps = total_steps  # room in the tables for every step's growth
@@ -348,7 +350,9 @@ def run(args, name):
     # the workgroup target plus the (sequence, kv head) pairs, whatever the lengths
     ws_need = max(max(runners[0].caches[li].workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq, layers[li][0]),
                       runners[0].caches[li].append_verify_workspace_bytes(seqs, [8] * wl.n_seqs, wl.hq,
-                                                                          layers[li][0]))
+                                                                          layers[li][0]),
+                      kv_workspace_bytes_valu(runners[0].caches[li].handle, seqs, [8] * wl.n_seqs, wl.hq,
+                                              layers[li][0]) if args.valu else 0)
                   for li in range(len(layers)))
     ws = [[torch.empty(2 * ws_need, dtype=torch.uint8, device=dev) for _ in layers] for _ in range(reps)]
     hip = Hip()
@@ -380,7 +384,9 @@ def run(args, name):
             if li == dom and timed_idx in ev:
                 c.trace_events(*ev[timed_idx])
             window, cap = layers[li][0], layers[li][1]
-            if args.separate:
+            if args.valu:
+                c.verify_valu(seqs, rows, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
+            elif args.separate:
                 c.verify(seqs, rows, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
             else:
                 c.append_verify(seqs, rows, k, v, q, wl.hq, wl.scale, cap, window, out=out, workspace=ws[rep][li])
@@ -415,7 +421,7 @@ def run(args, name):
     value = tok / el
     kv_gbs = byt / el / 1e9
     achieved = dom_bytes_avg / (kern_avg * 1e-3) / 1e9
-    traffic = load_traffic(name)
+    traffic = None if args.valu else load_traffic(name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -431,13 +437,15 @@ def run(args, name):
         "data": "synthetic",
         "config": {"workload": describe(name, wl, layers), "layer_replicas": reps,
                    "step": ("rollback previous drafts + append new rows + verify attention (partials + merge)"
-                            + (", append and verify as separate calls" if args.separate else
+                            + (", append and verify as separate calls, products on the vector ALUs "
+                               "(spec_verify_attn_valu)" if args.valu else
+                               ", append and verify as separate calls" if args.separate else
                                ", append and verify in one call (kv_append_verify)"))},
         "effective_kv_gbs": round(kv_gbs, 2),
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_tq3_kernel" if wl.fmt == 2 else "attn_kernel",
+            "kernel": "attn_valu_kernel" if args.valu else "attn_tq3_kernel" if wl.fmt == 2 else "attn_kernel",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -533,7 +541,7 @@ def _layer_pick(workload):
 
 
 def _is_attn(name):
-    return "attn_kernel" in name or "attn_tq3_kernel" in name
+    return "attn_kernel" in name or "attn_tq3_kernel" in name or "attn_valu_kernel" in name
 
 
 def summarize_trace(directory, workload, cmd, out_path=None):
@@ -681,6 +689,8 @@ def main():
     ap.add_argument("--workload", default=None, choices=sorted(workloads()) + sorted(ACCEPT_WORKLOADS),
                     help="one workload; default: tq3_100000 as the line's value, with bf16_100000 beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--valu", action="store_true",
+                    help="time spec_verify_attn_valu (products on the vector ALUs; bf16 workloads at d 64/128)")
     ap.add_argument("--separate", action="store_true",
                     help="append and verify as two calls (kv_append + spec_verify_attn) instead of kv_append_verify")
     ap.add_argument("--copy-probe", action="store_true", help="run a 1 GiB plain copy first (counter calibration)")

@@ -319,6 +319,23 @@ int spec_verify_attn_static(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids,
                             int32_t window, float* out, void* stream);
 
 /*
+ * spec_verify_attn with the products on the vector ALUs instead of the
+ * matrix cores: a measurement aid for choosing between the two units at the
+ * verify step's shapes (1 + k rows x a GQA group of query columns per kv
+ * head).  The same call, result and precision (the bf16 keys and values
+ * times two bf16 parts of the fp32 queries and probabilities, fp32
+ * accumulation, here by packed dot products), for KV_BF16 caches at
+ * head_dim 64 and 128; a kv head's columns are served 20 at a time (head
+ * slices beyond).  workspace: ws_bytes >= kv_workspace_bytes_valu(...).
+ * Errors: as spec_verify_attn's; KV_EINVAL for another format or head_dim.
+ */
+int kv_workspace_bytes_valu(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids,
+                            const int32_t* n_rows, int32_t num_q_heads, int32_t window, size_t* out);
+int spec_verify_attn_valu(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                          const float* q, int32_t num_q_heads, float scale, float softcap,
+                          int32_t window, float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Append the verified rows' K/V and verify them, in one call: kv_append of
  * n_rows[i] positions to each sequence followed by spec_verify_attn over
  * those same positions (AX Engine page, "Core Technical Architecture &

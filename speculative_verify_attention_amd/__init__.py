@@ -45,9 +45,11 @@ from ._binding import (  # noqa: F401
     kv_seq_free,
     kv_seq_len,
     kv_workspace_bytes,
+    kv_workspace_bytes_valu,
     lib,
     spec_accept,
     spec_accept_workspace_bytes,
     spec_verify_attn,
+    spec_verify_attn_valu,
     svcore_params,
 )

@@ -91,6 +91,9 @@ _SIGS = {
     "kv_workspace_bytes": [_p, _i32, _i32p, _i32p, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)],
     "spec_verify_attn": [_p, _i32, _i32p, _i32p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p,
                          ctypes.c_size_t, _p],
+    "kv_workspace_bytes_valu": [_p, _i32, _i32p, _i32p, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)],
+    "spec_verify_attn_valu": [_p, _i32, _i32p, _i32p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p,
+                              ctypes.c_size_t, _p],
     "kv_append_verify": [_p, _i32, _i32p, _i32p, _p, _p, _p, _i32, ctypes.c_float, ctypes.c_float, _i32, _p, _p,
                          ctypes.c_size_t, _p],
     "kv_append_verify_workspace_bytes": [_p, _i32, _i32p, _i32p, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)],
@@ -257,6 +260,23 @@ def spec_verify_attn(h, seq_ids, n_rows, q, num_q_heads, scale, softcap, window,
                                   num_q_heads, float(scale), float(softcap), window,
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws_ptr), ws_bytes,
                                   _stream_ptr(stream))
+
+
+def kv_workspace_bytes_valu(h, seq_ids, n_rows, num_q_heads, window):
+    out = ctypes.c_size_t()
+    rc = lib().kv_workspace_bytes_valu(h, len(seq_ids), _arr(seq_ids), _arr(n_rows), num_q_heads, window,
+                                       ctypes.byref(out))
+    _check(rc, h)
+    return out.value
+
+
+def spec_verify_attn_valu(h, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out, workspace, stream=None):
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return lib().spec_verify_attn_valu(h, len(seq_ids), _arr(seq_ids), _arr(n_rows), ctypes.c_void_p(q.data_ptr()),
+                                       num_q_heads, float(scale), float(softcap), window,
+                                       ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                       _stream_ptr(stream))
 
 
 def kv_append_verify_workspace_bytes(h, seq_ids, n_rows, num_q_heads, window):
@@ -495,6 +515,24 @@ class KVCache:
             workspace = self.workspace(seq_ids, n_rows, num_q_heads, window)
         _check(spec_verify_attn(self.handle, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out,
                                 workspace, stream), self.handle)
+        return out
+
+    def verify_valu(self, seq_ids, n_rows, q, num_q_heads, scale, softcap=0.0, window=0, out=None, workspace=None,
+                    stream=None):
+        """verify() with the products on the vector ALUs (spec_verify_attn_valu;
+        bf16 caches at head_dim 64 and 128): the measurement twin of verify()."""
+        import torch
+
+        rows = int(sum(n_rows))
+        self._check_rows("q", q, rows, num_q_heads, torch.float32)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_rows("out", out, rows, num_q_heads, torch.float32)
+        if workspace is None:
+            need = max(256, kv_workspace_bytes_valu(self.handle, seq_ids, n_rows, num_q_heads, window))
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.pool.device)
+        _check(spec_verify_attn_valu(self.handle, seq_ids, n_rows, q, num_q_heads, scale, softcap, window, out,
+                                     workspace, stream), self.handle)
         return out
 
     def verify_static(self, seq_ids, n_rows, q, num_q_heads, scale, softcap=0.0, window=0, out=None, stream=None):

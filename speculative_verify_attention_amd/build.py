@@ -42,7 +42,7 @@ HIP_FLAGS = [
     "-I", CSRC,
 ]
 
-HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "append.hip", "accept.hip", "probe.hip", "scratch.hip", "svattn.cpp",
+HIP_SOURCES = ["attn.hip", "attn_tq3.hip", "attn_valu.hip", "append.hip", "accept.hip", "probe.hip", "scratch.hip", "svattn.cpp",
                "kvcore.cpp", "plan.cpp", "ngram.cpp"]
 CORE_SOURCES = ["kvcore.cpp", "plan.cpp", "svcore_capi.cpp", "ngram.cpp"]
 # the host core again, under AddressSanitizer and UndefinedBehaviorSanitizer,

@@ -280,6 +280,10 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
 // One launch that encodes a TQ3 append (a) and rotates the queries (q).
 hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStream_t s);
 hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s);
+// The partial kernel with its products on the vector ALUs (bf16 caches,
+// d = 64 or 128, at most kValuMaxCols query columns: plans with that cap).
+constexpr int kValuMaxCols = 20;
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 // Acceptance: row statistics over every row (once per call), then decide and
 // draw for one group of up to kMaxAcceptSeqs sequences.
 hipError_t launch_accept_stats(const AcceptArgs& a, hipStream_t s);

@@ -19,7 +19,7 @@ void verify_lengths(const Core& core, const int32_t* pend, int32_t seq, int32_t 
 
 int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int32_t* seq_ids,
                 const int32_t* n_rows, int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp,
-                std::string* err) {
+                std::string* err, int max_cols) {
   *vp = VerifyPlan();
   const CoreParams& P = core.params();
   auto fail = [&](int code, const std::string& m) {
@@ -47,10 +47,11 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
     max_rows = std::max(max_rows, (int)n_rows[i]);
     vp->rows += n_rows[i];
   }
-  // head slices: the fewest that bring a slice's columns to 64 or fewer
-  // (hs = g always works: one head per slice, at most 8 rows)
+  // head slices: the fewest that bring a slice's columns to max_cols or
+  // fewer (hs = g always works: one head per slice, at most 8 rows)
+  if (max_cols < 8 || max_cols > 64) return fail(KV_EINVAL, "column cap");
   vp->hs = 1;
-  while (g % vp->hs || max_rows * (g / vp->hs) > 64) ++vp->hs;
+  while (g % vp->hs || max_rows * (g / vp->hs) > max_cols) ++vp->hs;
   vp->gs = g / vp->hs;
   const int R = max_rows * vp->gs;
   vp->nct = R > 32 ? 2 : 1;
@@ -107,7 +108,7 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
   if (P.format == KV_TQ3) vp->q_bytes = align_up((size_t)vp->rows * num_q_heads * P.head_dim * 4);
   vp->total = vp->part_bytes + 2 * vp->q_bytes;
 #ifdef SVATTN_CHECKED
-  const std::string bad = check_plan(core, pend, n_seqs, seq_ids, n_rows, num_q_heads, window, added, *vp);
+  const std::string bad = check_plan(core, pend, n_seqs, seq_ids, n_rows, num_q_heads, window, added, *vp, max_cols);
   if (!bad.empty()) {
     std::fprintf(stderr, "svattn: verify plan violates its invariants: %s\n", bad.c_str());
     std::abort();
@@ -118,7 +119,7 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
 
 std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, const int32_t* seq_ids,
                        const int32_t* n_rows, int32_t num_q_heads, int32_t window, const int32_t* added,
-                       const VerifyPlan& vp) {
+                       const VerifyPlan& vp, int max_cols) {
   const CoreParams& P = core.params();
   auto str = [](int64_t x) { return std::to_string(x); };
   if (n_seqs < 1) return "no sequences";
@@ -135,9 +136,9 @@ std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, co
   // head slices: hs x gs = g, a slice's columns fit two 32-column groups,
   // and no smaller number of slices would do
   if (vp.hs < 1 || vp.gs < 1 || vp.hs * vp.gs != g) return "head slices " + str(vp.hs) + " x " + str(vp.gs);
-  if (max_rows * vp.gs > 64) return "slice columns " + str(max_rows * vp.gs);
+  if (max_rows * vp.gs > max_cols) return "slice columns " + str(max_rows * vp.gs);
   for (int h2 = 1; h2 < vp.hs; ++h2)
-    if (g % h2 == 0 && max_rows * (g / h2) <= 64) return "fewer head slices would do: " + str(h2);
+    if (g % h2 == 0 && max_rows * (g / h2) <= max_cols) return "fewer head slices would do: " + str(h2);
   if (vp.nct != 1 && vp.nct != 2) return "column groups " + str(vp.nct);
   if (vp.rpad != 32 * vp.nct) return "padded columns " + str(vp.rpad);
   if (max_rows * vp.gs > vp.rpad || (vp.nct == 2 && max_rows * vp.gs <= 32))

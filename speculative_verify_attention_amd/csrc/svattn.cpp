@@ -111,8 +111,22 @@ void verify_lengths(const kv_cache* c, int32_t seq, int32_t added, int32_t* up, 
 }
 
 int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
-                int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp, std::string* err) {
-  return svattn::plan_verify(c->core, c->pend.data(), n_seqs, seq_ids, n_rows, num_q_heads, window, added, vp, err);
+                int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp, std::string* err,
+                int max_cols = 64) {
+  return svattn::plan_verify(c->core, c->pend.data(), n_seqs, seq_ids, n_rows, num_q_heads, window, added, vp, err,
+                             max_cols);
+}
+
+// The vector-unit verify's plan: at most kValuMaxCols columns per slice.
+int plan_verify_valu(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                     int32_t num_q_heads, int32_t window, VerifyPlan* vp) {
+  kv_cache* cc = const_cast<kv_cache*>(c);
+  const CoreParams& P = c->core.params();
+  if (P.format != KV_BF16 || (P.head_dim != 64 && P.head_dim != 128)) {
+    cc->err = "the vector-unit verify serves KV_BF16 caches at head_dim 64 and 128";
+    return KV_EINVAL;
+  }
+  return plan_verify(c, n_seqs, seq_ids, n_rows, num_q_heads, window, nullptr, vp, &cc->err, kValuMaxCols);
 }
 
 }  // namespace
@@ -482,7 +496,7 @@ QPrepArgs make_qprep(const kv_cache* c, const VerifyPlan& vp, const float* q, in
 int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                    const int32_t* added, const float* q, int32_t num_q_heads, float scale, float softcap,
                    int32_t window, float* out, void* workspace, hipStream_t s, const void* new_k, const void* new_v,
-                   bool rotated = false) {
+                   bool rotated = false, bool valu = false) {
   const CoreParams& P = c->core.params();
   const bool tq3 = P.format == KV_TQ3;
   float* q1 = nullptr;
@@ -560,7 +574,9 @@ int enqueue_verify(kv_cache* c, const VerifyPlan& vp, int32_t n_seqs, const int3
   hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, s);
   for (size_t li = 0; li < args.size() && e == hipSuccess; ++li)
-    e = tq3 ? launch_attn_tq3(args[li], vp.nct, s) : launch_attn(args[li], vp.nct, s);
+    e = valu  ? launch_attn_valu(args[li], s)
+        : tq3 ? launch_attn_tq3(args[li], vp.nct, s)
+              : launch_attn(args[li], vp.nct, s);
   if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, s);
   if (e != hipSuccess) return hip_fail(c, e, "attention launch");
   for (size_t li = 0; li < args.size(); ++li) {
@@ -610,6 +626,31 @@ int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const 
   if (rc != KV_OK) return rc;
   return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out,
                         workspace, static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+int kv_workspace_bytes_valu(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
+                            int32_t num_q_heads, int32_t window, size_t* out) {
+  if (!c || !out) return KV_EINVAL;
+  VerifyPlan vp;
+  int rc = plan_verify_valu(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp);
+  if (rc != KV_OK) return rc;
+  *out = vp.total;
+  return KV_OK;
+}
+
+int spec_verify_attn_valu(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows, const float* q,
+                          int32_t num_q_heads, float scale, float softcap, int32_t window, float* out,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return KV_EINVAL;
+  int rc = check_device(c);
+  if (rc != KV_OK) return rc;
+  VerifyPlan vp;
+  rc = plan_verify_valu(c, n_seqs, seq_ids, n_rows, num_q_heads, window, &vp);
+  if (rc != KV_OK) return rc;
+  rc = check_verify_args(c, vp, q, scale, softcap, out, workspace, ws_bytes);
+  if (rc != KV_OK) return rc;
+  return enqueue_verify(c, vp, n_seqs, seq_ids, n_rows, nullptr, q, num_q_heads, scale, softcap, window, out,
+                        workspace, static_cast<hipStream_t>(stream), nullptr, nullptr, false, true);
 }
 
 int spec_verify_attn_static(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
