@@ -487,7 +487,7 @@ def stream_probe(nbytes=2 << 30, runs=10):
     torch.cuda.empty_cache()
     return {"gbs_median": round(nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9, 1),
             "gbs_best": round(nbytes / (ms[0] * 1e-3) / 1e9, 1), "bytes": nbytes, "runs": runs,
-            "kernel": "kv_stream_probe (one workgroup per CU, grid-stride 16-byte loads, 16 steps in flight)"}
+            "kernel": "kv_stream_probe (one workgroup per CU, grid-stride 16-byte non-temporal loads, 16 steps in flight)"}
 
 
 def with_probe(res, probe):

@@ -47,6 +47,12 @@
 #ifndef SVATTN_STAGGER
 #define SVATTN_STAGGER 1
 #endif
+// Non-temporal hint on the tile loads from this head size down (the
+// measured choice: faster at d <= 128, slower at d = 256, where one tile
+// buffer is refilled in halves).
+#ifndef SVATTN_NT_MAX_D
+#define SVATTN_NT_MAX_D 128
+#endif
 
 namespace svattn {
 
@@ -73,6 +79,14 @@ struct Tr<0, D> {  // fp32: v_mfma_f32_32x32x2f32
   static constexpr int LV = D / 8;  // 4 groups of 4 PV k-steps x D/32 output tiles
 };
 
+template <int D>
+__device__ __forceinline__ u32x4_t tile_ld(const uint8_t* p) {
+  if constexpr (D <= SVATTN_NT_MAX_D)
+    return ld_stream(p);
+  else
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
 // One tile of raw operand registers.
 template <int FMT, int D>
 struct TileRegs {
@@ -90,10 +104,10 @@ __device__ __forceinline__ void load_tile(TileRegs<FMT, D>& b, const uint8_t* __
   for (int st = 0; st < T::NSUB; ++st) {
 #pragma unroll
     for (int j = 0; j < T::LK; ++j)
-      b.k[st][j] = *reinterpret_cast<const u32x4_t*>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
+      b.k[st][j] = tile_ld<D>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
 #pragma unroll
     for (int j = 0; j < T::LV; ++j)
-      b.v[st][j] = *reinterpret_cast<const u32x4_t*>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
+      b.v[st][j] = tile_ld<D>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
   }
 }
 
@@ -105,7 +119,7 @@ __device__ __forceinline__ void load_k(TileRegs<FMT, D>& b, const uint8_t* __res
   for (int st = 0; st < T::NSUB; ++st)
 #pragma unroll
     for (int j = 0; j < T::LK; ++j)
-      b.k[st][j] = *reinterpret_cast<const u32x4_t*>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
+      b.k[st][j] = tile_ld<D>(kbase + st * SUB_BYTES + j * 1024 + lane * 16);
 }
 template <int FMT, int D>
 __device__ __forceinline__ void load_v(TileRegs<FMT, D>& b, const uint8_t* __restrict__ vbase, int lane) {
@@ -115,7 +129,7 @@ __device__ __forceinline__ void load_v(TileRegs<FMT, D>& b, const uint8_t* __res
   for (int st = 0; st < T::NSUB; ++st)
 #pragma unroll
     for (int j = 0; j < T::LV; ++j)
-      b.v[st][j] = *reinterpret_cast<const u32x4_t*>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
+      b.v[st][j] = tile_ld<D>(vbase + st * SUB_BYTES + j * 1024 + lane * 16);
 }
 
 // Query operand of one lane (column c, half-wave hh).

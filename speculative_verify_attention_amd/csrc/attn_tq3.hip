@@ -45,6 +45,10 @@
 #ifndef SVATTN_TQ3_WAVES
 #define SVATTN_TQ3_WAVES 8
 #endif
+// Non-temporal hint on the sub-tile loads.
+#ifndef SVATTN_TQ3_NT
+#define SVATTN_TQ3_NT 1
+#endif
 
 namespace svattn {
 
@@ -115,14 +119,25 @@ template <int D>
 __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restrict__ sub, int lane) {
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
-    t.kc[j] = *reinterpret_cast<const u32x4_t*>(sub + j * 1024 + lane * 16);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(sub + 16 * D + j * 768 + lane * 12);
-    t.vc[j][0] = vp[0];
-    t.vc[j][1] = vp[1];
-    t.vc[j][2] = vp[2];
+    const uint8_t* vp = sub + 16 * D + j * 768 + lane * 12;
+    if constexpr (SVATTN_TQ3_NT) {
+      t.kc[j] = ld_stream(sub + j * 1024 + lane * 16);
+      t.vc[j][0] = ld_stream_u32(vp);
+      t.vc[j][1] = ld_stream_u32(vp + 4);
+      t.vc[j][2] = ld_stream_u32(vp + 8);
+    } else {
+      t.kc[j] = *reinterpret_cast<const u32x4_t*>(sub + j * 1024 + lane * 16);
+      t.vc[j][0] = reinterpret_cast<const uint32_t*>(vp)[0];
+      t.vc[j][1] = reinterpret_cast<const uint32_t*>(vp)[1];
+      t.vc[j][2] = reinterpret_cast<const uint32_t*>(vp)[2];
+    }
   }
   // lanes 48..63 repeat lanes 32..47 (no branch around the load)
-  t.sc = *reinterpret_cast<const uint32_t*>(sub + 28 * D + (lane < 48 ? lane : lane - 16) * 4);
+  const uint8_t* sp = sub + 28 * D + (lane < 48 ? lane : lane - 16) * 4;
+  if constexpr (SVATTN_TQ3_NT)
+    t.sc = ld_stream_u32(sp);
+  else
+    t.sc = *reinterpret_cast<const uint32_t*>(sp);
 }
 
 // Shared memory of the partial kernel (NW waves; 8 = two per SIMD).

@@ -145,8 +145,8 @@ __global__ __launch_bounds__(256, 1) void attn_valu_kernel(AttnArgs a) {
     const uint8_t* pb = base(ub_of(k)) + a.lay.k_off;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      ka[j] = *reinterpret_cast<const u32x4_t*>(pa + j * 1024 + lane * 16);
-      kb[j] = *reinterpret_cast<const u32x4_t*>(pb + j * 1024 + lane * 16);
+      ka[j] = ld_stream(pa + j * 1024 + lane * 16);
+      kb[j] = ld_stream(pb + j * 1024 + lane * 16);
     }
   };
   auto load_v = [&](int k) {
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256, 1) void attn_valu_kernel(AttnArgs a) {
     const uint8_t* pb = base(ub_of(k)) + a.lay.v_off;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      va[j] = *reinterpret_cast<const u32x4_t*>(pa + j * 1024 + lane * 16);
-      vb[j] = *reinterpret_cast<const u32x4_t*>(pb + j * 1024 + lane * 16);
+      va[j] = ld_stream(pa + j * 1024 + lane * 16);
+      vb[j] = ld_stream(pb + j * 1024 + lane * 16);
     }
   };
 

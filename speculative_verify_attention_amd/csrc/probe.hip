@@ -15,8 +15,11 @@ typedef uint32_t pu32x4_t __attribute__((ext_vector_type(4)));
 // One workgroup per compute unit walks the buffer grid-stride: each step
 // reads UNROLL wave-wide 1 KiB pieces per wave, kProbeWorkgroups x 4 KiB
 // apart, so that all 256 compute units stream side by side through the
-// whole buffer.  (Measured against contiguous chunks per workgroup at 256 to
-// 8192 workgroups, this is the fastest single pass over 2 GiB on MI355X.)
+// whole buffer, with non-temporal loads (read once, as the attention
+// kernels read the cache).  Measured over 2 GiB on MI355X (best of ten):
+// this shape 6.5 TB/s with plain loads and 7.2 TB/s non-temporal; 512 to
+// 4096 workgroups of 256 to 1024 threads, or contiguous chunks per
+// workgroup, 5.3 to 6.4 TB/s.
 template <int UNROLL>
 __global__ __launch_bounds__(256) void stream_probe_kernel(const pu32x4_t* __restrict__ src, int64_t n16,
                                                            uint32_t* __restrict__ sink) {
@@ -26,7 +29,7 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const pu32x4_t* __res
   for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
     pu32x4_t x[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) x[u] = src[i + u * stride];
+    for (int u = 0; u < UNROLL; ++u) x[u] = __builtin_nontemporal_load(src + i + u * stride);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= x[u];
   }
