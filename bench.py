@@ -48,6 +48,7 @@ def workloads():
         "tiny": lambda: (synth.tiny(), None),
         "qwen3_4b_dense": lambda: (synth.qwen3_4b_dense(), None),
         "gemma_interleaved": lambda: (synth.gemma_interleaved(), [(512, 50.0), (0, 50.0)]),
+        "gemma_tq3": lambda: (synth.gemma_interleaved(fmt=synth.KV_TQ3), [(512, 50.0), (0, 50.0)]),
         "tq3_512": lambda: (synth.tq3_long(512), None),
         "tq3_40000": lambda: (synth.tq3_long(40000), None),
         "tq3_100000": lambda: (synth.tq3_long(100000), None),

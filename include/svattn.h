@@ -273,8 +273,9 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  *  q: device float32 [sum(n_rows)][num_q_heads][head_dim], rows in the order
  *    of seq_ids.  num_q_heads must be a multiple of num_kv_heads; query head
  *    h reads kv head h / (num_q_heads / num_kv_heads).  The kernels hold
- *    at most 64 query columns (rows x group heads) of a kv head at once;
- *    beyond that (e.g. 5 rows at a group of 16) the call splits each group
+ *    at most 64 query columns (rows x group heads) of a kv head at once (32
+ *    for KV_TQ3 at head_dim 256); beyond that (e.g. 5 rows at a group of
+ *    16) the call splits each group
  *    into the fewest equal slices of heads that fit and runs one pass of
  *    launches per slice, so the cache is read once per slice and the
  *    workspace holds one set of partials per slice.
@@ -292,8 +293,7 @@ int kv_workspace_bytes(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids
  * weights, each carried as two bf16 parts (hi + lo, about 2^-17 relative);
  * KV_TQ3 multiplies the exact fp16 code levels and signs by fp16 parts of
  * q', q'' and the weights (two parts each, about 2^-21 relative).
- * Errors: KV_ENOSEQ, KV_EINVAL (bad arguments, KV_TQ3 with head_dim 256),
- * KV_ERANGE (n_rows > seq_len),
+ * Errors: KV_ENOSEQ, KV_EINVAL (bad arguments), KV_ERANGE (n_rows > seq_len),
  * KV_ENOMEM (workspace too small), KV_EDEVICE.
  */
 int spec_verify_attn(kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,

@@ -436,6 +436,9 @@ hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStrea
     case 128:
       hipLaunchKernelGGL(append_tq3_qprep_kernel<128>, grid, block, 0, s, a, q, (int32_t)n_app);
       break;
+    case 256:
+      hipLaunchKernelGGL(append_tq3_qprep_kernel<256>, grid, block, 0, s, a, q, (int32_t)n_app);
+      break;
     default:
       return hipErrorInvalidValue;
   }

@@ -668,7 +668,9 @@ hipError_t launch_merge(const AttnArgs& a, int nct, hipStream_t s) {
     hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, s, a);
   else if (d == 128)
     hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, s, a);
-  else if (d == 256 && !rot)
+  else if (d == 256 && rot)
+    hipLaunchKernelGGL((merge_kernel<256, true>), grid, block, 0, s, a);
+  else if (d == 256)
     hipLaunchKernelGGL((merge_kernel<256, false>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;

@@ -52,6 +52,23 @@
 
 namespace svattn {
 
+// Per head size: waves per workgroup and query-fragment parts (q' hi, q''
+// hi, q' lo, q'' lo) held in registers.  d <= 128: two waves per SIMD, the
+// first part in registers as well as all four in LDS (the others are read
+// from LDS at every use).  d = 256: one wave per SIMD (the output
+// accumulators alone take 128 registers); q' hi lives in registers only and
+// the other three parts in LDS only, so that they and the key table fit a
+// CU's 160 KiB; one column group (at most 32 query columns: the planner
+// splits wider groups into head slices).
+template <int D>
+struct TQ3Cfg {
+  static constexpr bool WIDE = D > 128;
+  static constexpr int NW = WIDE ? 4 : SVATTN_TQ3_WAVES;
+  static constexpr int NREG = WIDE ? 1 : SVATTN_TQ3_QREGS;
+  static constexpr int LDS_PART0 = WIDE ? 1 : 0;  // the first part kept in LDS
+  static constexpr int NPART_LDS = 4 - LDS_PART0;
+};
+
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -100,6 +117,8 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(qprep_kernel<64>, grid, dim3(256), 0, s, a);
   else if (a.d == 128)
     hipLaunchKernelGGL(qprep_kernel<128>, grid, dim3(256), 0, s, a);
+  else if (a.d == 256)
+    hipLaunchKernelGGL(qprep_kernel<256>, grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -154,9 +173,9 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
 // The combine buffer reuses the key table and fragments after the loop.
 template <int D, int NCT>
 struct TQ3Smem {
-  static constexpr int NW = SVATTN_TQ3_WAVES;
+  static constexpr int NW = TQ3Cfg<D>::NW;
   static constexpr int TL = NW / NCT;
-  static constexpr int NPART = 4;  // q' hi, q'' hi, q' lo, q'' lo
+  static constexpr int NPART = TQ3Cfg<D>::NPART_LDS;  // parts in LDS (of q' hi, q'' hi, q' lo, q'' lo)
   // below 64 KiB: value table, scale slices, query fragments; the key table
   // fills the next 64 KiB, so that a key-table address is one byte permute
   // of (slot, code byte, 1) and every other address fits an instruction's
@@ -178,27 +197,36 @@ struct TQ3Smem {
   static_assert(CBUF_OFF + CombineBuf<D, NCT, NW>::FLOATS * 4 <= BYTES, "combine buffer");
 };
 
+// LDS address of part `part`, k-step kk, of a lane's query fragments.
+template <int D>
+__device__ __forceinline__ int qfrag_off(int part, int kk, int lane) {
+  return ((part - TQ3Cfg<D>::LDS_PART0) * (D / 16) + kk) * 1024 + lane * 16;
+}
 template <int D>
 __device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, int lane) {
-  return *reinterpret_cast<const f16x8_t*>(qf + (part * (D / 16) + kk) * 1024 + lane * 16);
+  return *reinterpret_cast<const f16x8_t*>(qf + qfrag_off<D>(part, kk, lane));
 }
 
 // Query fragments of one lane: the leading NREG parts in registers, the
 // others read from LDS at every use.
 template <int D>
 struct QFrags {
-  static constexpr int NREG = SVATTN_TQ3_QREGS;
+  static constexpr int NREG = TQ3Cfg<D>::NREG;
   static constexpr int NR = NREG > 0 ? NREG : 1;
   f16x8_t f[NR][D / 16];
   const uint8_t* qf;
   int lane;
+  // d <= 128: the register parts are copies of LDS parts; d = 256: the
+  // prologue fills them itself (they are not in LDS)
   __device__ __forceinline__ void init(const uint8_t* q, int l) {
     qf = q;
     lane = l;
+    if constexpr (!TQ3Cfg<D>::WIDE) {
 #pragma unroll
-    for (int pt = 0; pt < NREG; ++pt)
+      for (int pt = 0; pt < NREG; ++pt)
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
+        for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
+    }
   }
   __device__ __forceinline__ f16x8_t get(int pt, int kk) const {
     if (pt < NREG)
@@ -350,7 +378,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
 }
 
 template <int D, int NCT, bool CAP>
-__global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArgs a) {
+__global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a) {
   using SM = TQ3Smem<D, NCT>;
   constexpr int NW = SM::NW;
   constexpr int TL = SM::TL;
@@ -362,6 +390,10 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF);
   uint32_t* vlut = reinterpret_cast<uint32_t*>(smem + SM::VLUT_OFF);
 
+  // d = 256 needs more than the 256 vector registers a lane can address
+  // (the output accumulators alone take 128): naming an accumulation
+  // register lets the compiler hold the matrix-core accumulators there
+  if constexpr (TQ3Cfg<D>::WIDE) asm volatile("" ::: "a0");
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane makes the compiler see it, so
   // tile indices and block-table reads stay scalar (no wait on vector loads)
@@ -407,6 +439,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
   for (int j = 0; j < NBUF - 1; ++j)
     if (j < cnt) load_tq3<D>(buf[j], sub_of(t_first + j * TL), lane);
 
+  QFrags<D> qr;
   // the 8 levels pass through LDS (wave 0's scale slice, unused until the loop)
   if (threadIdx.x == 0) {
 #pragma unroll
@@ -429,42 +462,61 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
       const int e = idx >> 5;  // entry; idx & 31 is the lane slot
       vlut[idx] = lv[e & 7] | (lv[e >> 3] << 16);
     }
-    // query fragments of this wave's column group: k-steps tl, tl + TL, ...
     const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D;
-    for (int kk = tl; kk < D / 16; kk += TL) {
-      u32x4_t h1{}, l1{}, h2{}, l2{};  // fp16 pairs
-      if (col_ok) {
-        const float* q1p = a.q + qrow + 16 * kk + 8 * hh;
-        const float* q2p = a.q2 + qrow + 16 * kk + 8 * hh;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q1p);
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
-        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
-        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
-        // the score multiplier is applied to the scores, not to the
-        // fragments: that keeps the low-order parts out of the fp16
-        // subnormal range
+    // fp16 hi/lo pairs of q' (h1, l1) and of q'' (h2, l2) at k-step kk
+    auto frags = [&](int kk, u32x4_t& h1, u32x4_t& l1, u32x4_t& h2, u32x4_t& l2) {
+      h1 = l1 = h2 = l2 = u32x4_t{};
+      if (!col_ok) return;
+      const float* q1p = a.q + qrow + 16 * kk + 8 * hh;
+      const float* q2p = a.q2 + qrow + 16 * kk + 8 * hh;
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q1p);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
+      const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
+      const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
+      // the score multiplier is applied to the scores, not to the
+      // fragments: that keeps the low-order parts out of the fp16
+      // subnormal range
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float xa = e < 4 ? x0[e] : x1[e - 4], xb = e < 4 ? x0[e + 1] : x1[e - 3];
-          const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
-          const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul;
-          const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
-          h1[e / 2] = sx[0];
-          l1[e / 2] = sx[1];
-          h2[e / 2] = sy[0];
-          l2[e / 2] = sy[1];
+      for (int e = 0; e < 8; e += 2) {
+        const float xa = e < 4 ? x0[e] : x1[e - 4], xb = e < 4 ? x0[e + 1] : x1[e - 3];
+        const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
+        const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul;
+        const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
+        h1[e / 2] = sx[0];
+        l1[e / 2] = sx[1];
+        h2[e / 2] = sy[0];
+        l2[e / 2] = sy[1];
+      }
+    };
+    if constexpr (TQ3Cfg<D>::WIDE) {
+      // every wave builds q' hi of every k-step in its registers and stores
+      // the other parts of k-steps tl, tl + TL, ...
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        u32x4_t h1, l1, h2, l2;
+        frags(kk, h1, l1, h2, l2);
+        qr.f[0][kk] = __builtin_bit_cast(f16x8_t, h1);
+        if (kk % TL == tl) {
+          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(1, kk, lane)) = h2;
+          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(2, kk, lane)) = l1;
+          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(3, kk, lane)) = l2;
         }
       }
-      *reinterpret_cast<u32x4_t*>(qf + (0 * (D / 16) + kk) * 1024 + lane * 16) = h1;
-      *reinterpret_cast<u32x4_t*>(qf + (1 * (D / 16) + kk) * 1024 + lane * 16) = h2;
-      *reinterpret_cast<u32x4_t*>(qf + (2 * (D / 16) + kk) * 1024 + lane * 16) = l1;
-      *reinterpret_cast<u32x4_t*>(qf + (3 * (D / 16) + kk) * 1024 + lane * 16) = l2;
+    } else {
+      // query fragments of this wave's column group: k-steps tl, tl + TL, ...
+      for (int kk = tl; kk < D / 16; kk += TL) {
+        u32x4_t h1, l1, h2, l2;
+        frags(kk, h1, l1, h2, l2);
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(0, kk, lane)) = h1;
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(1, kk, lane)) = h2;
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(2, kk, lane)) = l1;
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(3, kk, lane)) = l2;
+      }
     }
   }
   const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
   __syncthreads();
 
-  QFrags<D> qr;
   qr.init(qf, lane);
   ColState<D> cs;
   cs.m = NEG_INF;
@@ -517,7 +569,7 @@ __global__ __launch_bounds__(SVATTN_TQ3_WAVES * 64) void attn_tq3_kernel(AttnArg
 
 template <int D, int NCT>
 static hipError_t launch_tq3_dn(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_wg), block(SVATTN_TQ3_WAVES * 64);
+  dim3 grid(a.n_wg), block(TQ3Cfg<D>::NW * 64);
   if (a.softcap > 0.0f)
     hipLaunchKernelGGL((attn_tq3_kernel<D, NCT, true>), grid, block, 0, s, a);
   else
@@ -530,6 +582,7 @@ hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s) {
   const int d = a.lay.d;
   if (d == 64) return nct == 1 ? launch_tq3_dn<64, 1>(a, s) : launch_tq3_dn<64, 2>(a, s);
   if (d == 128) return nct == 1 ? launch_tq3_dn<128, 1>(a, s) : launch_tq3_dn<128, 2>(a, s);
+  if (d == 256 && nct == 1) return launch_tq3_dn<256, 1>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -49,6 +49,7 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
   }
   // head slices: the fewest that bring a slice's columns to max_cols or
   // fewer (hs = g always works: one head per slice, at most 8 rows)
+  if (max_cols == 0) max_cols = mfma_max_cols(P.format, P.head_dim);
   if (max_cols < 8 || max_cols > 64) return fail(KV_EINVAL, "column cap");
   vp->hs = 1;
   while (g % vp->hs || max_rows * (g / vp->hs) > max_cols) ++vp->hs;
@@ -122,6 +123,7 @@ std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, co
                        const VerifyPlan& vp, int max_cols) {
   const CoreParams& P = core.params();
   auto str = [](int64_t x) { return std::to_string(x); };
+  if (max_cols == 0) max_cols = mfma_max_cols(P.format, P.head_dim);
   if (n_seqs < 1) return "no sequences";
   const int g = num_q_heads / P.num_kv_heads;
   // rows and column groups: every query column of a (sequence, kv head) pair

@@ -78,11 +78,17 @@ void verify_lengths(const Core& core, const int32_t* pend, int32_t seq, int32_t 
 // spec_verify_attn's) and fills vp.  added: rows a fused append adds to each
 // entry before the verify (null: none).  Built with SVATTN_CHECKED, every
 // plan is also run through check_plan and a violation aborts.
-// max_cols: the most query columns one slice may hold, 8 .. 64 (64 for the
-// matrix-core kernels, 20 for the vector-unit kernel).
+// max_cols: the most query columns one slice may hold, 8 .. 64, or 0 for
+// the matrix-core kernels' cap (mfma_max_cols); 20 for the vector-unit
+// kernel.
 int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int32_t* seq_ids,
                 const int32_t* n_rows, int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp,
-                std::string* err, int max_cols = 64);
+                std::string* err, int max_cols = 0);
+
+// Query columns one matrix-core workgroup holds: two 32-column groups, or
+// one for the compressed format at d = 256 (whose registers and LDS hold a
+// single group's query fragments).
+constexpr int mfma_max_cols(int fmt, int d) { return fmt == 2 && d > 128 ? 32 : 64; }
 
 // The invariants the kernels and the workspace layout rely on, checked from
 // scratch against the call's arguments: the launch and chunk tables, the
@@ -90,6 +96,6 @@ int plan_verify(const Core& core, const int32_t* pend, int32_t n_seqs, const int
 // hold, else a description of the first violation.
 std::string check_plan(const Core& core, const int32_t* pend, int32_t n_seqs, const int32_t* seq_ids,
                        const int32_t* n_rows, int32_t num_q_heads, int32_t window, const int32_t* added,
-                       const VerifyPlan& vp, int max_cols = 64);
+                       const VerifyPlan& vp, int max_cols = 0);
 
 }  // namespace svattn

@@ -112,7 +112,7 @@ void verify_lengths(const kv_cache* c, int32_t seq, int32_t added, int32_t* up, 
 
 int plan_verify(const kv_cache* c, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_rows,
                 int32_t num_q_heads, int32_t window, const int32_t* added, VerifyPlan* vp, std::string* err,
-                int max_cols = 64) {
+                int max_cols = 0) {
   return svattn::plan_verify(c->core, c->pend.data(), n_seqs, seq_ids, n_rows, num_q_heads, window, added, vp, err,
                              max_cols);
 }
@@ -455,8 +455,6 @@ int check_verify_args(kv_cache* c, const VerifyPlan& vp, const float* q, float s
   if (ws_bytes < vp.total) return set_err(c, KV_ENOMEM, "workspace too small");
   if (vp.total > 0 && (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign))
     return set_err(c, KV_EINVAL, "workspace must be non-null and 256-byte aligned");
-  const CoreParams& P = c->core.params();
-  if (P.format == KV_TQ3 && P.head_dim > 128) return set_err(c, KV_EINVAL, "KV_TQ3 attention supports head_dim 64 and 128");
   return KV_OK;
 }
 

@@ -100,11 +100,13 @@ def qwen3_4b_dense(batch=16, ctx=4096, seed=2):
                     head_scales=True)
 
 
-def gemma_interleaved(batch=8, ctx=32768, window=512, seed=3):
-    """Gemma-style layer: Hq=8, Hkv=1, d=256, bf16, soft cap 50; window=512
-    for the local layer, 0 for the global layer."""
-    return Workload("gemma_window" if window else "gemma_full", 8, 1, 256, KV_BF16, [ctx] * batch, [5] * batch,
-                    window=window, softcap=50.0, seed=seed)
+def gemma_interleaved(batch=8, ctx=32768, window=512, seed=3, fmt=KV_BF16):
+    """Gemma-style layer: Hq=8, Hkv=1, d=256, soft cap 50; window=512 for the
+    local layer, 0 for the global layer; bf16 cache (or the compressed one
+    from an fp32 N(0,1) source with fmt=KV_TQ3)."""
+    name = ("gemma_window" if window else "gemma_full") + ("_tq3" if fmt == KV_TQ3 else "")
+    return Workload(name, 8, 1, 256, fmt, [ctx] * batch, [5] * batch, window=window, softcap=50.0, seed=seed,
+                    codec_seed=0x5EED if fmt == KV_TQ3 else 0)
 
 
 def tq3_long(ctx, batch=4, seed=None, fmt=KV_TQ3):

@@ -161,6 +161,7 @@ CASES = [
     # a group of 16: steps with 5 rows split the heads into two slices
     ("bf16_g16_head_slices", KV_BF16, 32, 2, 128, [250, 700, 31], [(0, 0.0)]),
     ("tq3_g16_head_slices", KV_TQ3, 32, 2, 128, [300, 90], [(0, 0.0)]),
+    ("tq3_d256_window_cap", KV_TQ3, 8, 1, 256, [300, 700, 62], [(64, 50.0), (0, 0.0)]),
 ]
 
 

@@ -199,6 +199,14 @@ EDGE = [
     # for value-dependent rounding cases such as exact fp16 ties
     ("stress_short", 32, 8, 128, np.random.default_rng(60).integers(1, 1500, size=60).tolist(),
      np.random.default_rng(61).integers(1, 6, size=60).tolist(), 0, 0.0, 1.0),
+    # head_dim 256: one 32-column group per workgroup, wider groups in head
+    # slices (5 rows x 8 heads = 40 columns: two slices of 4 heads)
+    ("d256_slices", 8, 1, 256, [1500, 90], [5, 3], 0, 0.0, 1.0),
+    ("d256_one_group", 4, 1, 256, [3000], [8], 0, 0.0, 1.0),
+    ("d256_window_softcap", 8, 2, 256, [2500, 300], [4, 2], 512, 30.0, 2.0),
+    ("d256_short", 2, 1, 256, [0, 3], [5, 1], 0, 0.0, 1.0),
+    ("d256_ragged", 16, 2, 256, [int(x) for x in np.linspace(1, 2000, 24)], [3] * 24, 0, 0.0, 1.0),
+    ("d256_long_pair", 8, 1, 256, [20000], [4], 0, 0.0, 1.0),
 ]
 
 

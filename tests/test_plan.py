@@ -110,8 +110,11 @@ def test_plans_hold_their_invariants(b):
             assert rc in (KV_EINVAL, KV_ERANGE)
             return
         nct, launches, slots, total, part, qb, hs = summ
-        # head slices: the fewest equal slices of the group whose columns fit 64
-        hs_want = min(h for h in range(1, g + 1) if g % h == 0 and max(rows) * (g // h) <= 64)
+        # head slices: the fewest equal slices of the group whose columns fit
+        # the kernel's workgroup (64 columns; 32 for the compressed format at
+        # d = 256, whose workgroup holds one column group)
+        cap = 32 if fmt == 2 and d == 256 else 64
+        hs_want = min(h for h in range(1, g + 1) if g % h == 0 and max(rows) * (g // h) <= cap)
         assert hs == hs_want
         assert nct == (2 if max(rows) * (g // hs) > 32 else 1)
         assert launches == math.ceil(len(seqs) / 128)
@@ -193,5 +196,25 @@ def test_head_slices(hkv, hq, rows, hs, nct):
         assert rc == KV_OK, err
         assert summ[6] == hs and summ[0] == nct
         assert summ[4] == align(hs * summ[2] * 32 * nct * (2 + 128) * 4)
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize(
+    "hq,rows,hs",
+    [
+        (8, [4], 1),    # 4 x 8 = 32 columns: one group
+        (8, [5], 2),    # 5 x 8 = 40: two slices of 4 heads (20)
+        (16, [8], 4),   # 8 x 16 = 128: four slices of 4 heads (32)
+        (4, [8, 3], 1),  # 8 x 4 = 32: fits
+    ],
+)
+def test_head_slices_compressed_d256(hq, rows, hs):
+    # the compressed format at d = 256 runs one 32-column group per workgroup
+    c = HostCore(1, 256, 2, [100] * len(rows))
+    try:
+        rc, summ, _, err = c.plan(list(range(len(rows))), rows, hq)
+        assert rc == KV_OK, err
+        assert summ[6] == hs and summ[0] == 1
     finally:
         c.close()
