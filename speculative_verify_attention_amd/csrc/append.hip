@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "lanes.h"
 #include "qprep.h"
 
 namespace svattn {
@@ -98,11 +99,6 @@ __device__ inline int find_seg(const int32_t* unit0, int n_segs, int unit) {
   return lo;
 }
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // IEEE half (bits) of a non-negative double, nearest-even, saturating at 65504.
 __device__ inline uint16_t half_rne(double x, uint32_t* sat) {
@@ -140,10 +136,21 @@ struct EncOut {
   uint16_t n16, g16;
 };
 
-// Encode x (global, fp32, D values) with one full wavefront.  rbuf: this
-// wave's D doubles of LDS.
+// A lane's E = D / 64 values of a source vector (dimensions lane*E ..).
 template <int D>
-__device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool is_key, const int8_t* __restrict__ signs,
+struct SrcVec {
+  float x[D / 64];
+  __device__ __forceinline__ void load(const float* __restrict__ src) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) x[e] = src[lane * (D / 64) + e];
+  }
+};
+
+// Encode one vector (its values already loaded by every lane) with one full
+// wavefront.  rbuf: this wave's D doubles of LDS.
+template <int D>
+__device__ __forceinline__ void encode_vector(const SrcVec<D>& xs, bool is_key, const int8_t* __restrict__ signs,
                               const float* __restrict__ s_t, const double* thr, const double* lev16,
                               double* rbuf, EncOut<D>& o, uint32_t* sat) {
   constexpr int E = D / 64;
@@ -152,11 +159,11 @@ __device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool 
   double ss = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    double xi = (double)x[lane * E + e];
+    double xi = (double)xs.x[e];
     ss += xi * xi;
     v[e] = signs[lane * E + e] < 0 ? -xi : xi;  // D x
   }
-  ss = wave_sum(ss);
+  ss = lanes_sum(ss);
   const double n = sqrt(ss);
   // zx = H (D x): Walsh-Hadamard butterflies; in-lane stages first, then
   // cross-lane stages (partner lane = lane ^ (h / E)).
@@ -171,15 +178,7 @@ __device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool 
       }
     }
   }
-#pragma unroll
-  for (int hl = 1; hl < 64; hl <<= 1) {
-    const bool upper = (lane & hl) != 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      double p = __shfl_xor(v[e], hl);
-      v[e] = upper ? (p - v[e]) : (v[e] + p);
-    }
-  }
+  wht_lanes(v, lane);
   // z = sqrt(d) * Pi x / n = zx / n; code = #thresholds <= z.
   uint32_t s = 0;
   const uint16_t n16 = half_rne(n, &s);
@@ -201,7 +200,7 @@ __device__ __forceinline__ void encode_vector(const float* __restrict__ x, bool 
   o.n16 = n16;
   o.g16 = 0;
   if (is_key) {
-    rr = wave_sum(rr);
+    rr = lanes_sum(rr);
     o.g16 = half_rne(sqrt(rr), &s);
     // proj = S r: every lane needs all of r, so pass it through LDS.
 #pragma unroll
@@ -301,14 +300,41 @@ constexpr int kAppendWaves = 8;
 
 // Shared memory of one TQ3 append workgroup.  S^T is staged in LDS once per
 // workgroup for d <= 128 (64 KiB), so the projections of the key residuals
-// read LDS instead of L2.
+// and of the rotated queries read LDS instead of L2.
+// A workgroup either encodes (residual and value-code buffers) or rotates
+// queries (kQVec rotated vectors per wave), so the two share their LDS,
+// which keeps two encoding workgroups per CU at d <= 128.
 template <int D>
 struct AppendTq3Smem {
   static constexpr bool kStage = D <= 128;
-  double rbuf[kAppendWaves][D];
-  uint8_t vcode[32][D];
+  static constexpr int kQVec = 3;  // query vectors per wave in the rotation workgroups
+  struct Enc {
+    double rbuf[kAppendWaves][D];
+    uint8_t vcode[32][D];
+  };
+  union {
+    Enc enc;
+    float qbuf[kAppendWaves][kQVec * D];
+  };
   float st_lds[kStage ? D * D : 4];
   uint32_t sat_any;
+};
+static_assert(sizeof(AppendTq3Smem<128>) <= 80 * 1024, "two encoding workgroups per CU");
+
+// S^T into LDS in two halves, so that the loads can be issued before the
+// work that does not need them: every thread holds NST 16-byte pieces.
+template <int D>
+struct StStage {
+  static constexpr int NST = AppendTq3Smem<D>::kStage ? D * D / 4 / (kAppendWaves * 64) : 0;
+  float4 r[NST > 0 ? NST : 1];
+  __device__ __forceinline__ void load(const float* s_t) {
+#pragma unroll
+    for (int i = 0; i < NST; ++i) r[i] = reinterpret_cast<const float4*>(s_t)[threadIdx.x + i * kAppendWaves * 64];
+  }
+  __device__ __forceinline__ void store(float* st_lds) const {
+#pragma unroll
+    for (int i = 0; i < NST; ++i) reinterpret_cast<float4*>(st_lds)[threadIdx.x + i * kAppendWaves * 64] = r[i];
+  }
 };
 
 template <int D>
@@ -316,12 +342,16 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
   constexpr int E = D / 64;
   constexpr int SB = tq3_sub_bytes(D);
   constexpr bool kStage = AppendTq3Smem<D>::kStage;
-  auto& rbuf = sm.rbuf;
-  auto& vcode = sm.vcode;
+  static_assert(2 * D <= kAppendWaves * 64, "one value-code field pair per thread");
+  auto& rbuf = sm.enc.rbuf;
+  auto& vcode = sm.enc.vcode;
   float* st_lds = sm.st_lds;
   uint32_t& sat_any = sm.sat_any;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  // S^T first: its loads depend on nothing
+  StStage<D> st;
+  if constexpr (kStage) st.load(a.s_t);
   if (threadIdx.x == 0) sat_any = 0;
   const int seg = find_seg(a.unit0, a.n_segs, unit);
   const int pos0 = seg_pos0(a, seg);
@@ -329,24 +359,57 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
   const int t0 = max(max(pos0, grp * 32), a.keep[seg]);  // ring caches store nothing below keep
   const int t1 = min(pos0 + a.n[seg], grp * 32 + 32);
   if (t0 >= t1) return;  // a spare unit, or one a ring cache drops (whole workgroup)
-  if constexpr (kStage) {
-    const float4* src = reinterpret_cast<const float4*>(a.s_t);
-    float4* dst = reinterpret_cast<float4*>(st_lds);
-#pragma unroll 4
-    for (int i = threadIdx.x; i < D * D / 4; i += kAppendWaves * 64) dst[i] = src[i];
+  const int nr = t1 - t0;
+  // this wave's first source vector (see the assignment below), requested
+  // before the block-table read
+  SrcVec<D> first;
+  {
+    int t = -1;
+    const void* base = a.k;
+    if (nr < kAppendWaves) {
+      if (wave < nr) {
+        t = t0 + wave;
+      } else if (wave - nr < nr) {
+        t = t0 + wave - nr;
+        base = a.v;
+      }
+    } else if (wave < 2 * nr) {
+      const bool is_key = wave < nr;
+      t = t0 + (is_key ? wave : wave - nr);
+      base = is_key ? a.k : a.v;
+    }
+    if (t >= 0) {
+      const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
+      first.load(reinterpret_cast<const float*>(base) + (src_row * a.lay.hkv + h) * D);
+    }
   }
-  const float* s_t = kStage ? st_lds : a.s_t;
   const int block = a.table[(int64_t)a.seq[seg] * a.max_bps + (grp >> 3)];
   uint8_t* sub = a.pool + (int64_t)block * a.lay.block_bytes + ((int64_t)h * 8 + (grp & 7)) * SB;
+  // The stored value-code fields this workgroup merges into (one thread per
+  // (dimension, half): the 48-bit field of dimension i for the tokens with
+  // bit 2 = half), read now so that the reads overlap the encoding.  Only
+  // this workgroup writes this sub-tile's fields.
+  const int fi = threadIdx.x >> 1, fsel = threadIdx.x & 1;
+  uint8_t* fp = nullptr;
+  uint64_t field = 0;
+  if (threadIdx.x < 2 * D) {
+    int bit0;
+    fp = sub + tq3_v_field(D, 4 * fsel, fi, &bit0);  // any token of this half names the field
+#pragma unroll
+    for (int b = 0; b < 6; ++b) field |= (uint64_t)fp[b] << (8 * b);
+  }
+  if constexpr (kStage) st.store(st_lds);
+  const float* s_t = kStage ? st_lds : a.s_t;
   uint32_t sat = 0;
   __syncthreads();
-  for (int t = t0 + wave; t < t1; t += kAppendWaves) {
+  // one wave per encoded vector.  Up to kAppendWaves - 1 rows: the keys of
+  // rows t0 + w on waves w < nr, the values on the other waves, round robin
+  // (a key costs about two values: its residual projection); more rows:
+  // keys, then values, round robin over all waves.
+  auto enc_key = [&](int t, const SrcVec<D>& xs) {
     const int m = t & 31;
-    const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
-    const float* kx = reinterpret_cast<const float*>(a.k) + (src_row * a.lay.hkv + h) * D;
-    const float* vx = reinterpret_cast<const float*>(a.v) + (src_row * a.lay.hkv + h) * D;
-    EncOut<D> ko, vo;
-    encode_vector<D>(kx, true, a.signs, s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
+    EncOut<D> ko;
+    encode_vector<D>(xs, true, a.signs, s_t, a.thr, a.lev16, rbuf[wave], ko, &sat);
     // key nibbles: dims 2b, 2b+1 share a byte
     if constexpr (E == 1) {
       const uint32_t nib = (uint32_t)(ko.code[0] | (ko.bit[0] << 3));
@@ -364,36 +427,66 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
         sub[tq3_k_byte(D, m, lane * E + e, &nb)] = (uint8_t)(lo | (hi << 4));
       }
     }
-    encode_vector<D>(vx, false, a.signs, s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
-#pragma unroll
-    for (int e = 0; e < E; ++e) vcode[m][lane * E + e] = vo.code[e];
     if (lane == 0) {
       store_half(sub + tq3_scale_byte(D, m, 0), ko.n16);
       store_half(sub + tq3_scale_byte(D, m, 1), ko.g16);
-      store_half(sub + tq3_scale_byte(D, m, 2), vo.n16);
+    }
+  };
+  auto enc_value = [&](int t, const SrcVec<D>& xs) {
+    const int m = t & 31;
+    EncOut<D> vo;
+    encode_vector<D>(xs, false, a.signs, s_t, a.thr, a.lev16, rbuf[wave], vo, &sat);
+#pragma unroll
+    for (int e = 0; e < E; ++e) vcode[m][lane * E + e] = vo.code[e];
+    if (lane == 0) store_half(sub + tq3_scale_byte(D, m, 2), vo.n16);
+  };
+  auto src_of = [&](const void* base, int t) {
+    const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
+    return reinterpret_cast<const float*>(base) + (src_row * a.lay.hkv + h) * D;
+  };
+  if (nr < kAppendWaves) {
+    if (wave < nr) {
+      enc_key(t0 + wave, first);
+    } else {
+      bool have = true;
+      for (int j = wave - nr; j < nr; j += kAppendWaves - nr) {
+        SrcVec<D> xs;
+        if (have)
+          xs = first;
+        else
+          xs.load(src_of(a.v, t0 + j));
+        have = false;
+        enc_value(t0 + j, xs);
+      }
+    }
+  } else {
+    for (int it = wave; it < 2 * nr; it += kAppendWaves) {
+      const bool is_key = it < nr;
+      const int t = t0 + (is_key ? it : it - nr);
+      SrcVec<D> xs;
+      if (it == wave)
+        xs = first;
+      else
+        xs.load(src_of(is_key ? a.k : a.v, t));
+      if (is_key)
+        enc_key(t, xs);
+      else
+        enc_value(t, xs);
     }
   }
   if (sat) atomicOr(&sat_any, 1u);
   __syncthreads();
-  // Merge the staged value codes into their 48-bit fields: one thread per
-  // (dimension, half): the field of dimension i for tokens with bit 2 = h.
-  const int m0 = t0 & 31, m1 = m0 + (t1 - t0);
-  for (int f = threadIdx.x; f < 2 * D; f += kAppendWaves * 64) {
-    const int i = f >> 1, hsel = f & 1;
-    int bit0;
-    const int off = tq3_v_field(D, 4 * hsel, i, &bit0);  // any token of this half names the field
-    uint8_t* p = sub + off;
-    uint64_t field = 0;
-#pragma unroll
-    for (int b = 0; b < 6; ++b) field |= (uint64_t)p[b] << (8 * b);
+  // Merge the staged value codes into their fields.
+  const int m0 = t0 & 31, m1 = m0 + nr;
+  if (threadIdx.x < 2 * D) {
     for (int m = m0; m < m1; ++m) {
-      if (((m >> 2) & 1) != hsel) continue;
+      if (((m >> 2) & 1) != fsel) continue;
       int bit;
-      tq3_v_field(D, m, i, &bit);
-      field = (field & ~((uint64_t)7 << bit)) | ((uint64_t)vcode[m][i] << bit);
+      tq3_v_field(D, m, fi, &bit);
+      field = (field & ~((uint64_t)7 << bit)) | ((uint64_t)vcode[m][fi] << bit);
     }
 #pragma unroll
-    for (int b = 0; b < 6; ++b) p[b] = (uint8_t)(field >> (8 * b));
+    for (int b = 0; b < 6; ++b) fp[b] = (uint8_t)(field >> (8 * b));
   }
   if (threadIdx.x == 0 && sat_any) atomicOr(a.status, 1u);
 }
@@ -417,15 +510,30 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_qprep_kernel(App
     append_tq3_block<D>(a, b / a.lay.hkv, b % a.lay.hkv, sm);
     return;
   }
+  // query rotation: S^T staged once, kQVec vectors per wave (their loads
+  // issued alongside the staging)
+  constexpr bool kStage = AppendTq3Smem<D>::kStage;
+  constexpr int NV = AppendTq3Smem<D>::kQVec;
   const int wave = threadIdx.x >> 6;
-  const int64_t vec = (int64_t)(b - n_app) * kAppendWaves + wave;
-  if (vec < q.n_vec) qprep_vector<D>(q, vec, reinterpret_cast<float*>(sm.rbuf[wave]));
+  const int64_t vec0 = ((int64_t)(b - n_app) * kAppendWaves + wave) * NV;
+  QVecs<D, NV> qv;
+  if constexpr (kStage) {
+    StStage<D> st;
+    st.load(q.s_t);
+    qv.load(q, vec0);
+    st.store(sm.st_lds);
+    __syncthreads();
+  } else {
+    qv.load(q, vec0);
+  }
+  if (vec0 < q.n_vec) qprep_vectors<D, NV>(q, vec0, qv, kStage ? sm.st_lds : q.s_t, sm.qbuf[wave]);
 }
 
 hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStream_t s) {
   if (a.lay.fmt != 2 || q.d != a.lay.d) return hipErrorInvalidValue;
   const int64_t n_app = (int64_t)a.total_units * a.lay.hkv;
-  const int64_t n_q = (q.n_vec + kAppendWaves - 1) / kAppendWaves;
+  const int64_t per_wg = (int64_t)kAppendWaves * AppendTq3Smem<128>::kQVec;
+  const int64_t n_q = (q.n_vec + per_wg - 1) / per_wg;
   if (n_app + n_q <= 0) return hipSuccess;
   if (n_app + n_q > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)(n_app + n_q)), block(kAppendWaves * 64);
@@ -488,7 +596,9 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const int rec = a.is_key ? (D / 2 + 4) : (3 * D / 8 + 2);
     uint8_t* dst = a.dst + vec * rec;
     EncOut<D> o;
-    encode_vector<D>(a.src + vec * D, a.is_key != 0, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], o, &sat);
+    SrcVec<D> xs;
+    xs.load(a.src + vec * D);
+    encode_vector<D>(xs, a.is_key != 0, a.signs, a.s_t, a.thr, a.lev16, rbuf[wave], o, &sat);
     if (a.is_key) {
       store_key_nibbles<D>(dst, o);
       if (lane == 0) {

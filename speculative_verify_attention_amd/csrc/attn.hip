@@ -33,6 +33,7 @@
 
 #include "attn_common.h"
 #include "kernels.h"
+#include "lanes.h"
 
 // Query fragments re-read from LDS at every tile from this head size up (0:
 // never), and the largest tile (registers per lane) kept in a ring of
@@ -556,26 +557,28 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
     }
   }
   float M = mj;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  M = fmaxf(M, lane_xor<32>(M));
+  M = fmaxf(M, lane_xor<16>(M));
+  M = fmaxf(M, lane_xor<8>(M));
+  M = fmaxf(M, lane_xor<4>(M));
+  M = fmaxf(M, lane_xor<2>(M));
+  M = fmaxf(M, lane_xor<1>(M));
   const float mu = M == NEG_INF ? 0.0f : M;
-  float lsum = lj * fast_exp2(mj - mu);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+  const float lsum = lanes_sum(lj * fast_exp2(mj - mu));
   float acc[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
 #pragma unroll
   for (int j = 0; j < KB; ++j) {
     if (j < k) {
-      const float f = fast_exp2(__shfl(m_own, j) - mu);
+      const float f = fast_exp2(lane_value(m_own, j) - mu);
 #pragma unroll
       for (int e = 0; e < EL; ++e) acc[e] += accj[j][e] * f;
     }
   }
   for (int j = KB; j < k; ++j) {
     const float* slot = base + (int64_t)j * a.slot_stride;
-    const float f = fast_exp2((j < 64 ? __shfl(m_own, j) : slot[c]) - mu);
+    const float f = fast_exp2((j < 64 ? lane_value(m_own, j) : slot[c]) - mu);
     const float* src = slot + 2 * a.rpad + (int64_t)c * D + lane * EL;
 #pragma unroll
     for (int e = 0; e < EL; ++e) acc[e] += src[e] * f;
@@ -595,15 +598,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
           acc[e] = x + y;
           acc[e + hs] = x - y;
         }
-#pragma unroll
-    for (int hl = 1; hl < 64; hl <<= 1) {
-      const bool upper = (lane & hl) != 0;
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        const float pv = __shfl_xor(acc[e], hl);
-        acc[e] = upper ? (pv - acc[e]) : (acc[e] + pv);
-      }
-    }
+    wht_lanes(acc, lane);
     // 1/sqrt(d) of the rotation and 1/sqrt(d) of the value reconstruction
     // (the partial kernel accumulates n16 * c16[code] without it)
     constexpr float inv_d = 1.0f / D;
