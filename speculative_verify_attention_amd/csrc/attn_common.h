@@ -97,7 +97,18 @@ __device__ __forceinline__ void softmax_update(ColState<D>& cs, float (&p)[NSUB]
     const float alpha = up ? fast_exp2(cs.m - mt) : 1.0f;
     cs.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) cs.acc[dt] *= alpha;
+    for (int dt = 0; dt < D / 32; ++dt) {
+      // d = 256: the accumulators live in accumulation registers.  Taking
+      // them from there and handing the scaled values back inside this
+      // rarely taken branch (the empty asm statements pin both ends to it)
+      // keeps the compiler from holding a vector-register copy of every
+      // accumulator across the whole loop for the multiply.
+      f32x16_t t = cs.acc[dt];
+      if constexpr (D > 128) asm volatile("" : "+a"(t));
+      t *= alpha;
+      if constexpr (D > 128) asm volatile("" : "+a"(t));
+      cs.acc[dt] = t;
+    }
     cs.m = up ? mt : cs.m;
   }
   const float m_use = cs.m == NEG_INF ? 0.0f : cs.m;
