@@ -491,11 +491,52 @@ def stream_probe(nbytes=2 << 30, runs=10):
             "kernel": "kv_stream_probe (one workgroup per CU, grid-stride 16-byte non-temporal loads, 16 steps in flight)"}
 
 
+def probe_at_size(nbytes, runs=10, pool=3 << 30):
+    """The read probe over `nbytes` (one launch's algorithmic bytes), cycling
+    through disjoint slices of a `pool`-byte buffer so that a slice is no
+    longer in the 256 MB Infinity Cache when it is read again: how long a
+    perfect single-pass reader of that many bytes takes on this GPU, start
+    and finish included.  Median of `runs` launches, HIP events."""
+    import torch
+
+    from speculative_verify_attention_amd._binding import kv_stream_probe, kv_stream_probe_sink_bytes
+
+    nbytes = int(nbytes) // 16 * 16
+    if nbytes <= 0:
+        return None
+    pool = max(pool, nbytes) // 16 * 16
+    buf = torch.ones(pool // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(kv_stream_probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+    nslice = pool // nbytes
+    views = [buf[i * (nbytes // 4):(i + 1) * (nbytes // 4)] for i in range(nslice)]
+    stream = torch.cuda.current_stream()
+    for v in views[:2]:
+        kv_stream_probe(v, sink, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for j, (a, b) in enumerate(ev):
+        a.record(stream)
+        kv_stream_probe(views[j % nslice], sink, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    del views, buf, sink
+    torch.cuda.empty_cache()
+    med = ms[len(ms) // 2]
+    return {"bytes": nbytes, "us_median": round(med * 1e3, 2), "gbs_median": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "slices": nslice, "runs": runs}
+
+
 def with_probe(res, probe):
-    """Fractions of the measured streaming-read bandwidth."""
+    """Fractions of the measured streaming-read bandwidth: of the probe over
+    2 GiB, and of the probe over one launch's own byte count (its floor)."""
     ref = probe["gbs_median"]
-    res["roofline"]["frac_of_stream_probe"] = round(res["roofline"]["achieved"] / ref, 4)
+    r = res["roofline"]
+    r["frac_of_stream_probe"] = round(r["achieved"] / ref, 4)
     res["pct_of_stream_probe"] = round(100.0 * res["effective_kv_gbs"] / ref, 2)
+    at = probe_at_size(r.get("alg_bytes_per_launch", 0))
+    if at:
+        r["probe_at_size"] = at
+        r["frac_of_probe_at_size"] = round(r["achieved"] / at["gbs_median"], 4)
     return res
 
 
