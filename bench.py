@@ -572,14 +572,31 @@ def _csv_rows(directory, suffix):
 
 
 def _layer_pick(workload):
-    """(layers, dominant index) of a workload: attention dispatches alternate
-    over the layers in step order, so the dominant layer's are every
-    layers-th one from that index."""
+    """(dispatches per step, positions of the dominant layer's) of a
+    workload: every step runs the layers in order, each as hs attention
+    dispatches (hs head slices: the fewest equal slices of a kv head's query
+    group whose columns fit one workgroup, 64 columns, 32 for the compressed
+    format at d = 256), so the dominant (full-attention) layer's dispatches
+    are positions dom * hs .. dom * hs + hs - 1 of every step."""
     if workload not in workloads():
-        return 1, 0
+        return 1, [0]
     wl, layers = workloads()[workload]()
     layers = layers or [(wl.window, wl.softcap)]
-    return len(layers), max(range(len(layers)), key=lambda i: layers[i][0] == 0)
+    dom = max(range(len(layers)), key=lambda i: layers[i][0] == 0)
+    g, cols = wl.hq // wl.hkv, 5 if wl.vary_rows else max(wl.rows)
+    cap = 32 if wl.fmt == 2 and wl.d > 128 else 64
+    hs = min(h for h in range(1, g + 1) if g % h == 0 and cols * (g // h) <= cap)
+    return len(layers) * hs, [dom * hs + j for j in range(hs)]
+
+
+def _dominant(values, workload, per_call=False):
+    """The dominant layer's entries of per-dispatch values in dispatch order:
+    every one (per_call=False) or, per call, the sum over its head slices."""
+    n, pos = _layer_pick(workload)
+    steps = len(values) // n
+    if per_call:
+        return [sum(values[s * n + p] for p in pos) for s in range(steps)]
+    return [values[s * n + p] for s in range(steps) for p in pos]
 
 
 def _is_attn(name):
@@ -599,13 +616,13 @@ def summarize_trace(directory, workload, cmd, out_path=None):
             continue
         out.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}")
-    n_layers, dom = _layer_pick(workload)
+    n_disp, pos = _layer_pick(workload)
     disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
                   for r in _csv_rows(directory, "kernel_trace.csv") if _is_attn(r["Kernel_Name"]))
     if disp:
-        d = [t / 1e3 for _, t in disp[dom::n_layers]]
-        out.append(f"# attention dispatches of the dominant layer (every {n_layers}. from {dom}): calls | average_us | "
-                   "min_us | max_us")
+        d = _dominant([t / 1e3 for _, t in disp], workload, per_call=True)
+        out.append(f"# attention dispatches of the dominant layer (positions {pos} of every {n_disp}; one call's "
+                   "head slices summed): calls | average_us | min_us | max_us")
         out.append(f"dominant_layer_attention | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f}")
     path = out_path or os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_trace.txt")
     open(path, "w").write("\n".join(out) + "\n")
@@ -616,8 +633,6 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     """profiles/attn_kernel_<workload>_pmc.txt from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
     same counter reads for the 1 GiB copy probe."""
-    n_layers, dom = _layer_pick(workload)
-
     def per_kernel(directory, counter):
         acc = {}
         for r in _csv_rows(directory, "counter_collection.csv"):
@@ -631,7 +646,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     res = {}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(directory, counter)
-        attn = [v for _, v in sorted(x for k, vs in acc.items() if _is_attn(k) for x in vs)][dom::n_layers]
+        attn = _dominant([v for _, v in sorted(x for k, vs in acc.items() if _is_attn(k) for x in vs)], workload,
+                         per_call=True)
         acc = {k: [v for _, v in vs] for k, vs in acc.items()}
         copy = [v for k, vs in acc.items() if "MulFunctor" in k or "mul" in k.lower() and "elementwise" in k
                 for v in vs if v > kib / 4]
@@ -642,8 +658,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write, alg_byte
     traffic = (f_attn * f_scale + w_attn * w_scale) * 1024.0
     out = [f"# rocprofv3 --pmc summary for the attention kernel, workload {workload}",
            f"# fetch command: {cmd_fetch}", f"# write command: {cmd_write}",
-           "# counters are KiB per dispatch; each is scaled by its reading for a plain copy of 1 GiB;",
-           "# attention dispatches of the dominant (full-attention) layer only",
+           "# counters are KiB per dispatch, summed over one call's head slices (the dominant, full-attention",
+           "# layer's calls only); each is scaled by its reading for a plain copy of 1 GiB",
            f"kernel_sources_sha256_16: {source_hash()}",
            f"attn_dispatches_fetch: {n_f}", f"attn_dispatches_write: {n_w}",
            f"attn_fetch_kib_avg: {f_attn:.1f}", f"copy_fetch_kib: {f_copy:.1f}", f"fetch_scale: {f_scale:.4f}",
@@ -669,7 +685,6 @@ def summarize_sq(dirs, workload, cmds, out_path=None):
     per-dispatch averages of the attention kernel (the dominant layer's
     dispatches) and of the library's other kernels, and per-wave figures of
     the attention kernel."""
-    n_layers, dom = _layer_pick(workload)
     attn, other = {}, {}
     for d in dirs:
         per = {}
@@ -684,7 +699,7 @@ def summarize_sq(dirs, workload, cmds, out_path=None):
         counters = sorted({c for _, c in per})
         for c in counters:
             xs = sorted((did, v) for (k, cc), dv in per.items() if cc == c and _is_attn(k) for did, v in dv.items())
-            xs = [v for _, v in xs][dom::n_layers]
+            xs = _dominant([v for _, v in xs], workload)
             if xs:
                 attn[c] = (sum(xs) / len(xs), len(xs))
             for (k, cc), dv in per.items():

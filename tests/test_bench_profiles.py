@@ -82,6 +82,29 @@ def test_trace_summary_keeps_the_dominant_layer(tmp_path):
     assert float(avg) == 74.0 and float(lo) == 71.0 and float(hi) == 77.0  # 71, 73, 75, 77 us
 
 
+def test_trace_summary_sums_head_slices(tmp_path):
+    # compressed cache at d = 256 with 5 rows x 8 heads = 40 columns: two head
+    # slices per call, so a step is window slice 0, 1, then full slice 0, 1
+    tq3 = "void svattn::attn_tq3_kernel<256, 1, true>(svattn::AttnArgs)"
+    d = tmp_path / "t"
+    write_csv(str(d / "kt_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+              [dict(Name=tq3, Calls=12, AverageNs=30000, MinNs=5000, MaxNs=60000, Percentage=100.0)])
+    rows = []
+    for s in range(3):
+        for j, dur in enumerate((5_000, 6_000, 50_000 + 1000 * s, 52_000 + 1000 * s)):
+            i = 4 * s + j
+            rows.append(dict(Dispatch_Id=10 + i, Kernel_Name=tq3, Start_Timestamp=1_000_000 * i,
+                             End_Timestamp=1_000_000 * i + dur))
+    write_csv(str(d / "kt_kernel_trace.csv"), ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    out = str(tmp_path / "trace.txt")
+    assert bench._layer_pick("gemma_tq3") == (4, [2, 3])
+    bench.summarize_trace(str(d), "gemma_tq3", "cmd", out)
+    line = [x for x in open(out) if x.startswith("dominant_layer_attention")][0]
+    _, calls, avg, lo, hi = [x.strip() for x in line.split("|")]
+    assert int(calls) == 3
+    assert float(lo) == 102.0 and float(avg) == 104.0 and float(hi) == 106.0  # 50+52, 51+53, 52+54 us
+
+
 def test_sq_summary_per_wave_figures(tmp_path):
     a, b = tmp_path / "a", tmp_path / "b"
     p1, p2 = [], []
