@@ -128,8 +128,8 @@ def test_append5_rollback3_equals_append2():
     assert torch.equal(oa, ob)
 
 
-def run_and_check(wl, seqs=None, layers=None, scale_q=1.0, fused=False):
-    r = Runner(wl, layers=layers, track=True)
+def run_and_check(wl, seqs=None, layers=None, scale_q=1.0, fused=False, ring=False):
+    r = Runner(wl, layers=layers, track=True, ring=ring)
     r.fill()
     rows, q, outs = r.step(0, scale_q, fused=fused)
     torch.cuda.synchronize()
@@ -161,6 +161,18 @@ def test_tq3_40000_every_sequence():
 def test_tq3_100000_every_sequence():
     banner("tq3 4x100000, kv_append_verify (the bench's launch), every sequence")
     err = run_and_check(synth.tq3_long(100000), fused=True)
+    print(f"max abs err {err:.3e}", flush=True)
+    assert err <= TOL, err
+
+
+@pytest.mark.timeout(900)
+def test_gemma_tq3_full_fused_ring():
+    # the Gemma-shaped workload on a compressed cache at its bench size and
+    # launch: 8 x 32K, d = 256, 5 rows x 8 heads = 40 columns (two head
+    # slices), window layer on a ring cache + full layer, soft cap 50
+    banner("gemma tq3 8x32768, window layer on a ring cache + full layer, kv_append_verify, every sequence")
+    wl = synth.gemma_interleaved(fmt=KV_TQ3)
+    err = run_and_check(wl, layers=[(512, 50.0), (0, 50.0)], fused=True, ring=True)
     print(f"max abs err {err:.3e}", flush=True)
     assert err <= TOL, err
 
