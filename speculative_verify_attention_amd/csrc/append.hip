@@ -297,6 +297,9 @@ __global__ __launch_bounds__(64) void append_plain_kernel(AppendArgs a) {
 // across 16 tokens, so they are staged in LDS and then merged into their
 // fields by one thread each (one writer per field: no two workgroups race).
 constexpr int kAppendWaves = 8;
+// Rows of a sub-tile up to which keys and values are encoded on separate
+// waves: 2 (kAppendWaves - n) >= n.
+constexpr int kSplitRows = 2 * kAppendWaves / 3;
 
 // Shared memory of one TQ3 append workgroup.  S^T is staged in LDS once per
 // workgroup for d <= 128 (64 KiB), so the projections of the key residuals
@@ -366,7 +369,7 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
   {
     int t = -1;
     const void* base = a.k;
-    if (nr < kAppendWaves) {
+    if (nr <= kSplitRows) {
       if (wave < nr) {
         t = t0 + wave;
       } else if (wave - nr < nr) {
@@ -402,10 +405,11 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
   const float* s_t = kStage ? st_lds : a.s_t;
   uint32_t sat = 0;
   __syncthreads();
-  // one wave per encoded vector.  Up to kAppendWaves - 1 rows: the keys of
-  // rows t0 + w on waves w < nr, the values on the other waves, round robin
-  // (a key costs about two values: its residual projection); more rows:
-  // keys, then values, round robin over all waves.
+  // one wave per encoded vector.  Up to five rows (every value wave then
+  // has at most two values, and a key costs about two values: its residual
+  // projection): the keys of rows t0 + w on waves w < nr, the values on the
+  // other waves, round robin; more rows: keys, then values, round robin
+  // over all waves.
   auto enc_key = [&](int t, const SrcVec<D>& xs) {
     const int m = t & 31;
     EncOut<D> ko;
@@ -444,7 +448,7 @@ __device__ __forceinline__ void append_tq3_block(const AppendArgs& a, int unit, 
     const int64_t src_row = (int64_t)a.row0[seg] + (t - pos0);
     return reinterpret_cast<const float*>(base) + (src_row * a.lay.hkv + h) * D;
   };
-  if (nr < kAppendWaves) {
+  if (nr <= kSplitRows) {
     if (wave < nr) {
       enc_key(t0 + wave, first);
     } else {
