@@ -576,12 +576,29 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
       for (int e = 0; e < EL; ++e) acc[e] += accj[j][e] * f;
     }
   }
-  for (int j = KB; j < k; ++j) {
-    const float* slot = base + (int64_t)j * a.slot_stride;
-    const float f = fast_exp2((j < 64 ? lane_value(m_own, j) : slot[c]) - mu);
-    const float* src = slot + 2 * a.rpad + (int64_t)c * D + lane * EL;
+  // the other chunks KB at a time: a batch's loads are issued together (one
+  // round trip per batch, not per chunk), then folded in chunk order
+  for (int j0 = KB; j0 < k; j0 += KB) {
+    float xj[KB][EL], mx[KB];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] += src[e] * f;
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u;
+      if (j < k) {
+        const float* slot = base + (int64_t)j * a.slot_stride;
+        mx[u] = j < 64 ? lane_value(m_own, j) : slot[c];
+        const float* src = slot + 2 * a.rpad + (int64_t)c * D + lane * EL;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) xj[u][e] = src[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (j0 + u < k) {
+        const float f = fast_exp2(mx[u] - mu);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc[e] += xj[u][e] * f;
+      }
+    }
   }
   const float inv = 1.0f / lsum;
 #pragma unroll

@@ -159,7 +159,8 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
     t.sc = *reinterpret_cast<const uint32_t*>(sp);
 }
 
-// Shared memory of the partial kernel (NW waves; 8 = two per SIMD).
+// Shared memory of the partial kernel (NW waves: 8, two per SIMD, at
+// d <= 128; 4 at d = 256).
 //  * key table, indexed by (byte of two key nibbles, lane slot): every lane of
 //    a 32-lane group reads its own dword column (levels in the row's first
 //    half, signs in the second), so table reads never conflict on LDS banks
@@ -541,8 +542,9 @@ __global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a
     __builtin_amdgcn_wave_barrier();
   };
   if (cnt > 0) stage(0, buf[0]);
-  // the two waves of a SIMD (waves w and w + 4) start half a phase apart, so
-  // that one is in its matrix-core phase while the other is in its softmax
+  // the two waves of a SIMD (waves w and w + 4, at d <= 128) start half a
+  // phase apart, so that one is in its matrix-core phase while the other is
+  // in its softmax
   if (wave >= 4) __builtin_amdgcn_s_sleep(24);
   // Whole rounds of NBUF sub-tiles, then the last ones (fewer than NBUF, all
   // in flight already).  Inside a round the prefetch is unconditional: past
