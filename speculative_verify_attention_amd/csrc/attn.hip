@@ -529,7 +529,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   // One memory round trip for k <= KB: lane j holds chunk j's (m, l), and
   // the first KB chunks' accumulator parts are loaded beside them (they do
   // not depend on the maximum).
-  constexpr int KB = 8;
+  constexpr int KB = 32;
   float mj = NEG_INF, lj = 0.0f;
   if (lane < k) {
     mj = base[(int64_t)lane * a.slot_stride + c];
