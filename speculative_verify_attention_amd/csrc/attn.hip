@@ -528,8 +528,11 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnArgs a) {
   const float* base = a.part + (int64_t)w0 * a.slot_stride;
   // One memory round trip for k <= KB: lane j holds chunk j's (m, l), and
   // the first KB chunks' accumulator parts are loaded beside them (they do
-  // not depend on the maximum).
-  constexpr int KB = 32;
+  // not depend on the maximum).  d = 256 (few merge waves, up to 32 chunks
+  // a pair): 32; d <= 128, whose merges run many more waves: 8, so that the
+  // registers stay few (with 32 the dense and mixed workloads' merges took
+  // 1.5-2x as long).
+  constexpr int KB = D > 128 ? 32 : 8;
   float mj = NEG_INF, lj = 0.0f;
   if (lane < k) {
     mj = base[(int64_t)lane * a.slot_stride + c];
