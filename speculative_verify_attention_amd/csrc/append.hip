@@ -300,6 +300,8 @@ constexpr int kAppendWaves = 8;
 // Rows of a sub-tile up to which keys and values are encoded on separate
 // waves: 2 (kAppendWaves - n) >= n.
 constexpr int kSplitRows = 2 * kAppendWaves / 3;
+// Query vectors per wave in the rotation workgroups of the step launch.
+constexpr int kQVec = 3;
 
 // Shared memory of one TQ3 append workgroup.  S^T is staged in LDS once per
 // workgroup for d <= 128 (64 KiB), so the projections of the key residuals
@@ -310,7 +312,6 @@ constexpr int kSplitRows = 2 * kAppendWaves / 3;
 template <int D>
 struct AppendTq3Smem {
   static constexpr bool kStage = D <= 128;
-  static constexpr int kQVec = 3;  // query vectors per wave in the rotation workgroups
   struct Enc {
     double rbuf[kAppendWaves][D];
     uint8_t vcode[32][D];
@@ -324,8 +325,9 @@ struct AppendTq3Smem {
 };
 static_assert(sizeof(AppendTq3Smem<128>) <= 80 * 1024, "two encoding workgroups per CU");
 
-// S^T into LDS in two halves, so that the loads can be issued before the
-// work that does not need them: every thread holds NST 16-byte pieces.
+// S^T into LDS in two steps, loads into registers and then stores, so that
+// the loads can be issued ahead of work that does not need them: every
+// thread holds NST 16-byte pieces in between.
 template <int D>
 struct StStage {
   static constexpr int NST = AppendTq3Smem<D>::kStage ? D * D / 4 / (kAppendWaves * 64) : 0;
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_qprep_kernel(App
   // query rotation: S^T staged once, kQVec vectors per wave (their loads
   // issued alongside the staging)
   constexpr bool kStage = AppendTq3Smem<D>::kStage;
-  constexpr int NV = AppendTq3Smem<D>::kQVec;
+  constexpr int NV = kQVec;
   const int wave = threadIdx.x >> 6;
   const int64_t vec0 = ((int64_t)(b - n_app) * kAppendWaves + wave) * NV;
   QVecs<D, NV> qv;
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void append_tq3_qprep_kernel(App
 hipError_t launch_append_qprep(const AppendArgs& a, const QPrepArgs& q, hipStream_t s) {
   if (a.lay.fmt != 2 || q.d != a.lay.d) return hipErrorInvalidValue;
   const int64_t n_app = (int64_t)a.total_units * a.lay.hkv;
-  const int64_t per_wg = (int64_t)kAppendWaves * AppendTq3Smem<128>::kQVec;
+  const int64_t per_wg = (int64_t)kAppendWaves * kQVec;
   const int64_t n_q = (q.n_vec + per_wg - 1) / per_wg;
   if (n_app + n_q <= 0) return hipSuccess;
   if (n_app + n_q > INT32_MAX) return hipErrorInvalidValue;
