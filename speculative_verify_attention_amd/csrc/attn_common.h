@@ -203,10 +203,13 @@ struct CombineBuf {
   static_assert(TL >= 1 && TL < 16, "token lanes");
 };
 
-template <int D, int NCT, int NW = 4>
+// DS, dim0: the output's head size and the first dimension this state
+// holds (a state may hold a part of the dimensions); write_ml: this call
+// stores the partial slot's maxima and sums (one of the parts does).
+template <int D, int NCT, int NW = 4, int DS = D>
 __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, const AttnArgs& a, int w, int k,
                                                   int s, int h, int row_i, int head_j, bool col_ok, int lane,
-                                                  int ct, int tl) {
+                                                  int ct, int tl, int dim0 = 0, bool write_ml = true) {
   constexpr int TL = NW / NCT;
   constexpr int P = CombineBuf<D, NCT, NW>::P;
   constexpr int SLOTS = CombineBuf<D, NCT, NW>::SLOTS;
@@ -256,7 +259,7 @@ __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, 
   if (tl == 0 && col_ok) {
     if (k == 1 && !a.force_partial) {
       const float inv = 1.0f / cs.l;
-      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D;
+      float* o = a.out + ((int64_t)(a.qrow0[s] + row_i) * a.hq + h * a.gq + a.head0 + head_j) * DS + dim0;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -267,11 +270,11 @@ __device__ __forceinline__ void combine_and_store(ColState<D>& cs, float* cbuf, 
         }
     } else {
       float* slot = a.part + (int64_t)w * a.slot_stride;
-      if (hh == 0) {
+      if (hh == 0 && write_ml) {
         slot[c] = cs.m;
         slot[a.rpad + c] = cs.l;
       }
-      float* acc = slot + 2 * a.rpad + (int64_t)c * D;
+      float* acc = slot + 2 * a.rpad + (int64_t)c * DS + dim0;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

@@ -52,20 +52,16 @@
 
 namespace svattn {
 
-// Per head size: waves per workgroup and query-fragment parts (q' hi, q''
-// hi, q' lo, q'' lo) held in registers.  d <= 128: two waves per SIMD, the
-// first part in registers as well as all four in LDS (the others are read
-// from LDS at every use).  d = 256: one wave per SIMD (the output
-// accumulators alone take 128 registers); q' hi lives in registers only and
-// the other three parts in LDS only, so that they and the key table fit a
-// CU's 160 KiB; one column group (at most 32 query columns: the planner
-// splits wider groups into head slices).
+// Waves per workgroup and query-fragment parts (q' hi, q'' hi, q' lo,
+// q'' lo) held in registers, d <= 128: two waves per SIMD, the first part in
+// registers as well as all four in LDS (the others are read from LDS at
+// every use).  (d = 256 runs on wave pairs: attn_tq3_pair_kernel.)
 template <int D>
 struct TQ3Cfg {
-  static constexpr bool WIDE = D > 128;
-  static constexpr int NW = WIDE ? 4 : SVATTN_TQ3_WAVES;
-  static constexpr int NREG = WIDE ? 1 : SVATTN_TQ3_QREGS;
-  static constexpr int LDS_PART0 = WIDE ? 1 : 0;  // the first part kept in LDS
+  static_assert(D <= 128, "d = 256 runs on wave pairs");
+  static constexpr int NW = SVATTN_TQ3_WAVES;
+  static constexpr int NREG = SVATTN_TQ3_QREGS;
+  static constexpr int LDS_PART0 = 0;  // the first part kept in LDS
   static constexpr int NPART_LDS = 4 - LDS_PART0;
 };
 
@@ -159,8 +155,7 @@ __device__ __forceinline__ void load_tq3(TQ3Regs<D>& t, const uint8_t* __restric
     t.sc = *reinterpret_cast<const uint32_t*>(sp);
 }
 
-// Shared memory of the partial kernel (NW waves: 8, two per SIMD, at
-// d <= 128; 4 at d = 256).
+// Shared memory of the partial kernel (NW waves; 8 = two per SIMD).
 //  * key table, indexed by (byte of two key nibbles, lane slot): every lane of
 //    a 32-lane group reads its own dword column (levels in the row's first
 //    half, signs in the second), so table reads never conflict on LDS banks
@@ -198,50 +193,58 @@ struct TQ3Smem {
   static_assert(CBUF_OFF + CombineBuf<D, NCT, NW>::FLOATS * 4 <= BYTES, "combine buffer");
 };
 
-// LDS address of part `part`, k-step kk, of a lane's query fragments.
-template <int D>
+// LDS address of part `part`, k-step kk, of a lane's query fragments (P0:
+// the first part kept in LDS).
+template <int D, int P0 = TQ3Cfg<D>::LDS_PART0>
 __device__ __forceinline__ int qfrag_off(int part, int kk, int lane) {
-  return ((part - TQ3Cfg<D>::LDS_PART0) * (D / 16) + kk) * 1024 + lane * 16;
+  return ((part - P0) * (D / 16) + kk) * 1024 + lane * 16;
 }
-template <int D>
+template <int D, int P0 = TQ3Cfg<D>::LDS_PART0>
 __device__ __forceinline__ f16x8_t qfrag(const uint8_t* qf, int part, int kk, int lane) {
-  return *reinterpret_cast<const f16x8_t*>(qf + qfrag_off<D>(part, kk, lane));
+  return *reinterpret_cast<const f16x8_t*>(qf + qfrag_off<D, P0>(part, kk, lane));
 }
 
 // Query fragments of one lane: the leading NREG parts in registers, the
-// others read from LDS at every use.
-template <int D>
+// others read from LDS at every use.  P0: the first part kept in LDS (0:
+// every part is there, the register parts being copies; NREG: the register
+// parts are not in LDS and the prologue fills them itself).
+template <int D, int NREG_ = TQ3Cfg<D>::NREG, int P0 = TQ3Cfg<D>::LDS_PART0>
 struct QFrags {
-  static constexpr int NREG = TQ3Cfg<D>::NREG;
+  static constexpr int NREG = NREG_;
   static constexpr int NR = NREG > 0 ? NREG : 1;
   f16x8_t f[NR][D / 16];
   const uint8_t* qf;
   int lane;
-  // d <= 128: the register parts are copies of LDS parts; d = 256: the
-  // prologue fills them itself (they are not in LDS)
   __device__ __forceinline__ void init(const uint8_t* q, int l) {
     qf = q;
     lane = l;
-    if constexpr (!TQ3Cfg<D>::WIDE) {
+    if constexpr (P0 == 0) {
 #pragma unroll
       for (int pt = 0; pt < NREG; ++pt)
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D>(qf, pt, kk, lane);
+        for (int kk = 0; kk < D / 16; ++kk) f[pt][kk] = qfrag<D, P0>(qf, pt, kk, lane);
     }
   }
   __device__ __forceinline__ f16x8_t get(int pt, int kk) const {
     if (pt < NREG)
       return f[pt < NR ? pt : 0][kk];
     else
-      return qfrag<D>(qf, pt, kk, lane);
+      return qfrag<D, P0>(qf, pt, kk, lane);
   }
 };
 
-template <int D, bool CAP>
-__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const QFrags<D>& qr,
+struct NoScoreHook {
+  __device__ __forceinline__ void operator()(float (&)[16]) const {}
+};
+
+// scores(p) gets the sub-tile's scores before any non-linear step (the
+// multiplier's fold, the soft cap, the mask): the two-wave d = 256 kernel
+// adds the other half's partial scores there.
+template <int D, bool CAP, typename QF, typename ScoreHook = NoScoreHook>
+__device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t, const QF& qr,
                                             const uint8_t* __restrict__ lds, const uint32_t* __restrict__ vlut,
                                             uint32_t* scl, const AttnArgs& a, int key0, int L, int n, int ppos,
-                                            int lane, uint32_t kslot) {
+                                            int lane, uint32_t kslot, ScoreHook scores = ScoreHook()) {
   const int hh = lane >> 5;
   // scl: this sub-tile's scales (K norm, K residual norm, V norm), written
   // to the wave's LDS slot during the previous sub-tile
@@ -304,6 +307,7 @@ __device__ __forceinline__ void process_tq3(ColState<D>& cs, const TQ3Regs<D>& t
     scale_words(1, gw);
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[0][r] = fmaf(s2[r], half_at(gw, r), fmaf(s1[r], half_at(nw, r), 0.0f));
+    scores(p[0]);
     if (!fold) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -391,10 +395,6 @@ __global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a
   float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF);
   uint32_t* vlut = reinterpret_cast<uint32_t*>(smem + SM::VLUT_OFF);
 
-  // d = 256 needs more than the 256 vector registers a lane can address
-  // (the output accumulators alone take 128): naming an accumulation
-  // register lets the compiler hold the matrix-core accumulators there
-  if constexpr (TQ3Cfg<D>::WIDE) asm volatile("" ::: "a0");
   const int lane = threadIdx.x & 63;
   // wave-uniform by construction; readfirstlane makes the compiler see it, so
   // tile indices and block-table reads stay scalar (no wait on vector loads)
@@ -489,30 +489,14 @@ __global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a
         l2[e / 2] = sy[1];
       }
     };
-    if constexpr (TQ3Cfg<D>::WIDE) {
-      // every wave builds q' hi of every k-step in its registers and stores
-      // the other parts of k-steps tl, tl + TL, ...
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        u32x4_t h1, l1, h2, l2;
-        frags(kk, h1, l1, h2, l2);
-        qr.f[0][kk] = __builtin_bit_cast(f16x8_t, h1);
-        if (kk % TL == tl) {
-          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(1, kk, lane)) = h2;
-          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(2, kk, lane)) = l1;
-          *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(3, kk, lane)) = l2;
-        }
-      }
-    } else {
-      // query fragments of this wave's column group: k-steps tl, tl + TL, ...
-      for (int kk = tl; kk < D / 16; kk += TL) {
-        u32x4_t h1, l1, h2, l2;
-        frags(kk, h1, l1, h2, l2);
-        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(0, kk, lane)) = h1;
-        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(1, kk, lane)) = h2;
-        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(2, kk, lane)) = l1;
-        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(3, kk, lane)) = l2;
-      }
+    // query fragments of this wave's column group: k-steps tl, tl + TL, ...
+    for (int kk = tl; kk < D / 16; kk += TL) {
+      u32x4_t h1, l1, h2, l2;
+      frags(kk, h1, l1, h2, l2);
+      *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(0, kk, lane)) = h1;
+      *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(1, kk, lane)) = h2;
+      *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(2, kk, lane)) = l1;
+      *reinterpret_cast<u32x4_t*>(qf + qfrag_off<D>(3, kk, lane)) = l2;
     }
   }
   const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);  // table base (byte 2) | slot (byte 0)
@@ -542,9 +526,8 @@ __global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a
     __builtin_amdgcn_wave_barrier();
   };
   if (cnt > 0) stage(0, buf[0]);
-  // the two waves of a SIMD (waves w and w + 4, at d <= 128) start half a
-  // phase apart, so that one is in its matrix-core phase while the other is
-  // in its softmax
+  // the two waves of a SIMD (waves w and w + 4) start half a phase apart, so
+  // that one is in its matrix-core phase while the other is in its softmax
   if (wave >= 4) __builtin_amdgcn_s_sleep(24);
   // Whole rounds of NBUF sub-tiles, then the last ones (fewer than NBUF, all
   // in flight already).  Inside a round the prefetch is unconditional: past
@@ -569,6 +552,218 @@ __global__ __launch_bounds__(TQ3Cfg<D>::NW * 64) void attn_tq3_kernel(AttnArgs a
   combine_and_store<D, NCT, NW>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, ct, tl);
 }
 
+// ---- d = 256 on wave pairs ----------------------------------------------------------
+
+// Half hf of a d = 256 sub-tile's bytes (key-code planes 2hf and 2hf + 1,
+// value-code planes 2hf and 2hf + 1, the scales), in the d = 128 register
+// layout: a wave of a pair then runs the d = 128 code on its 128 dimensions.
+__device__ __forceinline__ void load_tq3_half(TQ3Regs<128>& t, const uint8_t* __restrict__ sub, int hf, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint8_t* kp = sub + (2 * hf + j) * 1024 + lane * 16;
+    const uint8_t* vp = sub + 16 * 256 + (2 * hf + j) * 768 + lane * 12;
+    if constexpr (SVATTN_TQ3_NT) {
+      t.kc[j] = ld_stream(kp);
+      t.vc[j][0] = ld_stream_u32(vp);
+      t.vc[j][1] = ld_stream_u32(vp + 4);
+      t.vc[j][2] = ld_stream_u32(vp + 8);
+    } else {
+      t.kc[j] = *reinterpret_cast<const u32x4_t*>(kp);
+      t.vc[j][0] = reinterpret_cast<const uint32_t*>(vp)[0];
+      t.vc[j][1] = reinterpret_cast<const uint32_t*>(vp)[1];
+      t.vc[j][2] = reinterpret_cast<const uint32_t*>(vp)[2];
+    }
+  }
+  const uint8_t* sp = sub + 28 * 256 + (lane < 48 ? lane : lane - 16) * 4;
+  if constexpr (SVATTN_TQ3_NT)
+    t.sc = ld_stream_u32(sp);
+  else
+    t.sc = *reinterpret_cast<const uint32_t*>(sp);
+}
+
+// Shared memory of the pair kernel (eight waves: four token lanes x two
+// halves of the dimensions, one 32-column group).  Below 64 KiB: the value
+// table, the scale slices and each half's query fragments (q'' hi, q' lo,
+// q'' lo; q' hi stays in registers); the key table in the next 64 KiB as in
+// the one-wave kernels; above it one 4 KiB slot per wave for its partial
+// scores.  The combine buffers (one per half) reuse the fragments and the
+// key table after the loop.
+struct TQ3PairSmem {
+  static constexpr int VLUT_OFF = 0;
+  static constexpr int SCL_OFF = 8192;
+  static constexpr int QF_OFF = 12288;
+  static constexpr int QF_HALF = 3 * 8 * 1024;
+  static constexpr int KLUT_OFF = 65536;
+  static constexpr int XCH_OFF = 131072;
+  static constexpr int BYTES = XCH_OFF + 8 * 4096;
+  static constexpr int CBUF_OFF = QF_OFF;
+  static constexpr int CBUF_HALF = CombineBuf<128, 1, 4>::FLOATS;  // floats
+  static_assert(SCL_OFF + 8 * 2 * 48 * 4 <= QF_OFF, "scale slices");
+  static_assert(QF_OFF + 2 * QF_HALF <= KLUT_OFF, "query fragments");
+  static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
+  static_assert(CBUF_OFF + 2 * CBUF_HALF * 4 <= XCH_OFF, "combine buffers");
+};
+
+// d = 256: every 32-key sub-tile is taken by a pair of waves (w, w + 4), each
+// holding half of the dimensions: its query fragments, key and value codes,
+// key products and output accumulators are those of the d = 128 kernel.
+// The two halves' partial scores (linear in the products: n16 <q', c>
+// + gamma <q'', b> over each half) meet in LDS and are added, half 0's
+// first, so both waves hold the same scores, run the same softmax and keep
+// the same (m, l).  Two workgroup barriers per sub-tile: after the partial
+// scores are written and after they are read; a wave whose token lane has
+// run out of sub-tiles still takes both, so every wave passes the same
+// barriers.  Two waves per SIMD fit (the d = 128 register budget), which
+// the one-wave d = 256 layout (128 accumulator registers alone) does not.
+template <bool CAP>
+__global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
+  constexpr int D = 256, DH = 128, TL = 4;
+  constexpr int SB = tq3_sub_bytes(D);
+  using SM = TQ3PairSmem;
+  __shared__ __align__(16) uint8_t smem[SM::BYTES];
+  uint8_t* klut = smem + SM::KLUT_OFF;
+  uint32_t* vlut = reinterpret_cast<uint32_t*>(smem + SM::VLUT_OFF);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tl = wave & 3, hf = wave >> 2;  // token lane, half of the dimensions
+  uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 96;
+  uint8_t* qf = smem + SM::QF_OFF + hf * SM::QF_HALF;
+  float* xmine = reinterpret_cast<float*>(smem + SM::XCH_OFF + wave * 4096) + lane * 16;
+  const float* xother = reinterpret_cast<const float*>(smem + SM::XCH_OFF + (wave ^ 4) * 4096) + lane * 16;
+  const int col = lane & 31, hh = lane >> 5;
+  const int c = col;
+  const int w = blockIdx.x;
+  const Chunk ch = chunk_of(a, w);
+  const int s = ch.s, h = ch.h, tlo = ch.tlo;
+  const int L = ch.L, n = ch.n;
+  const int R = n * a.g;
+  const bool col_ok = c < R;
+  const int row_i = col_ok ? c / a.g : 0;
+  const int head_j = col_ok ? c - row_i * a.g : 0;
+  const int ppos = L - n + row_i;
+
+  // block-table entries held one per lane, as in the one-wave kernels
+  const int32_t* trow = a.table + (int64_t)ch.seq * a.max_bps;
+  auto tab_load = [&](int b0) { return trow[min(b0 + lane, a.max_bps - 1)]; };
+  int tb = (tlo + ch.t_begin) >> 3;
+  int tab = tab_load(tb);
+  auto sub_of = [&](int t) {
+    const int key0 = (tlo + t) * 32;
+    const int blk = key0 >> 8;
+    if ((unsigned)(blk - tb) >= 64u) {
+      tb = blk;
+      tab = tab_load(tb);
+    }
+    const int e = __builtin_amdgcn_readlane(tab, blk - tb);
+    return a.pool + (int64_t)e * a.lay.block_bytes + ((int64_t)h * 8 + ((key0 & 255) >> 5)) * SB;
+  };
+  const int t_first = ch.t_begin + tl;
+  const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
+  const int cnt_max = ch.t_end > ch.t_begin ? (ch.t_end - ch.t_begin + TL - 1) / TL : 0;  // token lane 0's
+  TQ3Regs<DH> buf[2];
+  if (cnt > 0) load_tq3_half(buf[0], sub_of(t_first), hf, lane);
+
+  QFrags<DH, 1, 1> qr;  // q' hi in registers; q'' hi, q' lo, q'' lo in LDS
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) scl[j] = a.lev16_bits[j];
+  }
+  __syncthreads();
+  {
+    const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
+    for (int j = threadIdx.x; j < 256 * 64; j += 512) {
+      const uint32_t i = j >> 6, lo = i & 15, hi = i >> 4;
+      reinterpret_cast<uint32_t*>(klut)[j] =
+          (j & 32) ? (((lo & 8) ? 0x3C00u : 0xBC00u) | (((hi & 8) ? 0x3C00u : 0xBC00u) << 16))
+                   : (lv[lo & 7] | (lv[hi & 7] << 16));
+    }
+    for (int idx = threadIdx.x; idx < 64 * 32; idx += 512) {
+      const int e = idx >> 5;
+      vlut[idx] = lv[e & 7] | (lv[e >> 3] << 16);
+    }
+    // this half's query fragments: k-steps 8 hf .. 8 hf + 7 of the head
+    const int64_t qrow = ((int64_t)(ch.qrow0 + row_i) * a.hq + h * a.gq + a.head0 + head_j) * D + DH * hf;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      u32x4_t h1{}, l1{}, h2{}, l2{};
+      if (col_ok) {
+        const float* q1p = a.q + qrow + 16 * kk + 8 * hh;
+        const float* q2p = a.q2 + qrow + 16 * kk + 8 * hh;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(q1p);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(q1p + 4);
+        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(q2p);
+        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(q2p + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float xa = e < 4 ? x0[e] : x1[e - 4], xb = e < 4 ? x0[e + 1] : x1[e - 3];
+          const float ya = (e < 4 ? y0[e] : y1[e - 4]) * a.q2_mul;
+          const float yb = (e < 4 ? y0[e + 1] : y1[e - 3]) * a.q2_mul;
+          const u32x2_t sx = split_f16_pair(xa, xb), sy = split_f16_pair(ya, yb);
+          h1[e / 2] = sx[0];
+          l1[e / 2] = sx[1];
+          h2[e / 2] = sy[0];
+          l2[e / 2] = sy[1];
+        }
+      }
+      qr.f[0][kk] = __builtin_bit_cast(f16x8_t, h1);
+      if (kk % TL == tl) {
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<DH, 1>(1, kk, lane)) = h2;
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<DH, 1>(2, kk, lane)) = l1;
+        *reinterpret_cast<u32x4_t*>(qf + qfrag_off<DH, 1>(3, kk, lane)) = l2;
+      }
+    }
+  }
+  const uint32_t kslot = 0x10000u | ((uint32_t)(lane & 31) * 4);
+  __syncthreads();
+
+  qr.init(qf, lane);
+  ColState<DH> cs;
+  cs.m = NEG_INF;
+  cs.l = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt) cs.acc[dt] = f32x16_t{};
+
+  const int sl = lane < 48 ? lane : lane - 16;
+  auto stage = [&](int k, const TQ3Regs<DH>& b) { scl[(k & 1) * 48 + sl] = b.sc; };
+  // the partial scores out and the other half's in: scores = half 0's +
+  // half 1's in both waves
+  auto exchange = [&](float (&p)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      reinterpret_cast<f32x4_t*>(xmine)[j] = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t o = reinterpret_cast<const f32x4_t*>(xother)[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[4 * j + e] = hf == 0 ? p[4 * j + e] + o[e] : o[e] + p[4 * j + e];
+    }
+  };
+  auto step = [&](int k, const TQ3Regs<DH>& cur, TQ3Regs<DH>& next) {
+    if (k < cnt) {
+      load_tq3_half(next, sub_of(t_first + min(k + 1, cnt - 1) * TL), hf, lane);
+      process_tq3<DH, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
+                           (tlo + t_first + k * TL) * 32, L, n, ppos, lane, kslot, exchange);
+      stage(k + 1, next);
+    } else {
+      __syncthreads();  // the exchange's barrier, for a token lane with no sub-tile left
+    }
+    __syncthreads();  // the slots are written again next sub-tile
+  };
+  if (cnt > 0) stage(0, buf[0]);
+  int k = 0;
+  for (; k + 2 <= cnt_max; k += 2) {
+    step(k, buf[0], buf[1]);
+    step(k + 1, buf[1], buf[0]);
+  }
+  if (k < cnt_max) step(k, buf[0], buf[1]);
+  // the combine buffers overlay the fragments and tables (every wave is past
+  // the last barrier of the loop)
+  float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF) + hf * SM::CBUF_HALF;
+  combine_and_store<DH, 1, 4, D>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, 0, tl, DH * hf, hf == 0);
+}
+
 template <int D, int NCT>
 static hipError_t launch_tq3_dn(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_wg), block(TQ3Cfg<D>::NW * 64);
@@ -584,7 +779,14 @@ hipError_t launch_attn_tq3(const AttnArgs& a, int nct, hipStream_t s) {
   const int d = a.lay.d;
   if (d == 64) return nct == 1 ? launch_tq3_dn<64, 1>(a, s) : launch_tq3_dn<64, 2>(a, s);
   if (d == 128) return nct == 1 ? launch_tq3_dn<128, 1>(a, s) : launch_tq3_dn<128, 2>(a, s);
-  if (d == 256 && nct == 1) return launch_tq3_dn<256, 1>(a, s);
+  if (d == 256 && nct == 1) {
+    dim3 grid(a.n_wg), block(512);
+    if (a.softcap > 0.0f)
+      hipLaunchKernelGGL(attn_tq3_pair_kernel<true>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_tq3_pair_kernel<false>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
