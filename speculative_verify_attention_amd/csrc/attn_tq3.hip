@@ -591,6 +591,7 @@ __device__ __forceinline__ void load_tq3_half(TQ3Regs<128>& t, const uint8_t* __
 struct TQ3PairSmem {
   static constexpr int VLUT_OFF = 0;
   static constexpr int SCL_OFF = 8192;
+  static constexpr int FLAG_OFF = SCL_OFF + 8 * 2 * 48 * 4;  // per wave: scores ready, partner's read
   static constexpr int QF_OFF = 12288;
   static constexpr int QF_HALF = 3 * 8 * 1024;
   static constexpr int KLUT_OFF = 65536;
@@ -598,23 +599,23 @@ struct TQ3PairSmem {
   static constexpr int BYTES = XCH_OFF + 8 * 4096;
   static constexpr int CBUF_OFF = QF_OFF;
   static constexpr int CBUF_HALF = CombineBuf<128, 1, 4>::FLOATS;  // floats
-  static_assert(SCL_OFF + 8 * 2 * 48 * 4 <= QF_OFF, "scale slices");
+  static_assert(FLAG_OFF + 2 * 8 * 4 <= QF_OFF, "scale slices and flags");
   static_assert(QF_OFF + 2 * QF_HALF <= KLUT_OFF, "query fragments");
   static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
   static_assert(CBUF_OFF + 2 * CBUF_HALF * 4 <= XCH_OFF, "combine buffers");
 };
 
-// d = 256: every 32-key sub-tile is taken by a pair of waves (w, w + 4), each
-// holding half of the dimensions: its query fragments, key and value codes,
-// key products and output accumulators are those of the d = 128 kernel.
-// The two halves' partial scores (linear in the products: n16 <q', c>
-// + gamma <q'', b> over each half) meet in LDS and are added, half 0's
-// first, so both waves hold the same scores, run the same softmax and keep
-// the same (m, l).  Two workgroup barriers per sub-tile: after the partial
-// scores are written and after they are read; a wave whose token lane has
-// run out of sub-tiles still takes both, so every wave passes the same
-// barriers.  Two waves per SIMD fit (the d = 128 register budget), which
-// the one-wave d = 256 layout (128 accumulator registers alone) does not.
+// d = 256: every 32-key sub-tile is taken by a pair of waves (2p, 2p + 1,
+// on two SIMDs), each holding half of the dimensions: its query fragments,
+// key and value codes, key products and output accumulators are those of
+// the d = 128 kernel.  The two halves' partial scores (linear in the
+// products: n16 <q', c> + gamma <q'', b> over each half) meet in LDS and
+// are added, half 0's first, so both waves hold the same scores, run the
+// same softmax and keep the same (m, l).  The pair synchronises through two
+// LDS counters per wave (scores written, partner's scores read), so pairs
+// run independently and the two waves on a SIMD (pairs p and p + 2) can be
+// in different phases, as in the d = 128 kernel.  Every wait is bounded.
+// Two waves per SIMD fit the d = 128 register budget.
 template <bool CAP>
 __global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
   constexpr int D = 256, DH = 128, TL = 4;
@@ -626,11 +627,18 @@ __global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tl = wave & 3, hf = wave >> 2;  // token lane, half of the dimensions
+  const int tl = wave >> 1, hf = wave & 1;  // token lane (pair), half of the dimensions
   uint32_t* scl = reinterpret_cast<uint32_t*>(smem + SM::SCL_OFF) + wave * 96;
   uint8_t* qf = smem + SM::QF_OFF + hf * SM::QF_HALF;
-  float* xmine = reinterpret_cast<float*>(smem + SM::XCH_OFF + wave * 4096) + lane * 16;
-  const float* xother = reinterpret_cast<const float*>(smem + SM::XCH_OFF + (wave ^ 4) * 4096) + lane * 16;
+  // the exchange slots and counters, as LDS pointers (a generic pointer
+  // would make the counter reads flat loads, which wait for the sub-tile
+  // loads in flight)
+  typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+  typedef __attribute__((address_space(3))) volatile uint32_t lds_flag_t;
+  lds_f32x4_t* xmine = (lds_f32x4_t*)(smem + SM::XCH_OFF + wave * 4096) + lane * 4;
+  const lds_f32x4_t* xother = (const lds_f32x4_t*)(smem + SM::XCH_OFF + (wave ^ 1) * 4096) + lane * 4;
+  lds_flag_t* ready = (lds_flag_t*)(smem + SM::FLAG_OFF);  // [wave]: sub-tiles whose scores are out
+  lds_flag_t* taken = ready + 8;  // [wave]: sub-tiles whose partner scores this wave has read
   const int col = lane & 31, hh = lane >> 5;
   const int c = col;
   const int w = blockIdx.x;
@@ -660,7 +668,6 @@ __global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
   };
   const int t_first = ch.t_begin + tl;
   const int cnt = t_first < ch.t_end ? (ch.t_end - t_first + TL - 1) / TL : 0;
-  const int cnt_max = ch.t_end > ch.t_begin ? (ch.t_end - ch.t_begin + TL - 1) / TL : 0;  // token lane 0's
   TQ3Regs<DH> buf[2];
   if (cnt > 0) load_tq3_half(buf[0], sub_of(t_first), hf, lane);
 
@@ -669,6 +676,7 @@ __global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) scl[j] = a.lev16_bits[j];
   }
+  if (threadIdx.x < 16) ready[threadIdx.x] = 0u;  // and taken[]
   __syncthreads();
   {
     const uint32_t* lv = reinterpret_cast<const uint32_t*>(smem + SM::SCL_OFF);
@@ -726,40 +734,61 @@ __global__ __launch_bounds__(512) void attn_tq3_pair_kernel(AttnArgs a) {
 
   const int sl = lane < 48 ? lane : lane - 16;
   auto stage = [&](int k, const TQ3Regs<DH>& b) { scl[(k & 1) * 48 + sl] = b.sc; };
-  // the partial scores out and the other half's in: scores = half 0's +
-  // half 1's in both waves
+  // Wait (bounded) until counter f reaches v; every lane reads the same
+  // word.  The LDS serves a wave's accesses in order; the empty asm keeps the
+  // compiler from moving LDS accesses across the wait.
+  auto wait_for = [](lds_flag_t* f, uint32_t v) {
+    for (int i = 0; i < (1 << 22); ++i) {
+      if (*f >= v) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+  };
+  // the partial scores out and the other half's in (sub-tile xk of the
+  // pair): scores = half 0's + half 1's in both waves.  The slot is
+  // rewritten only once the partner has read its previous contents.
+  uint32_t xk = 0;
   auto exchange = [&](float (&p)[16]) {
+    if (xk > 0) wait_for(&taken[wave ^ 1], xk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xmine[j] = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the scores are in LDS before the counter moves
+    ready[wave] = xk + 1;
+    wait_for(&ready[wave ^ 1], xk + 1);
+    f32x4_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = xother[j];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the partner may rewrite its slot
+    taken[wave] = xk + 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      reinterpret_cast<f32x4_t*>(xmine)[j] = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4_t o = reinterpret_cast<const f32x4_t*>(xother)[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[4 * j + e] = hf == 0 ? p[4 * j + e] + o[e] : o[e] + p[4 * j + e];
-    }
+      for (int e = 0; e < 4; ++e) p[4 * j + e] = hf == 0 ? p[4 * j + e] + o[j][e] : o[j][e] + p[4 * j + e];
+    ++xk;
   };
   auto step = [&](int k, const TQ3Regs<DH>& cur, TQ3Regs<DH>& next) {
-    if (k < cnt) {
-      load_tq3_half(next, sub_of(t_first + min(k + 1, cnt - 1) * TL), hf, lane);
-      process_tq3<DH, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
-                           (tlo + t_first + k * TL) * 32, L, n, ppos, lane, kslot, exchange);
-      stage(k + 1, next);
-    } else {
-      __syncthreads();  // the exchange's barrier, for a token lane with no sub-tile left
-    }
-    __syncthreads();  // the slots are written again next sub-tile
+    __builtin_amdgcn_wave_barrier();
+    process_tq3<DH, CAP>(cs, cur, qr, smem, vlut + (lane & 31), scl + (k & 1) * 48, a,
+                         (tlo + t_first + k * TL) * 32, L, n, ppos, lane, kslot, exchange);
+    stage(k + 1, next);
+    __builtin_amdgcn_wave_barrier();
   };
   if (cnt > 0) stage(0, buf[0]);
+  // pairs 2 and 3 (waves 4..7, the second wave of each SIMD) start half a
+  // phase after pairs 0 and 1
+  if (wave >= 4) __builtin_amdgcn_s_sleep(24);
+  // the ring as in the one-wave kernels: whole rounds of two, the prefetch
+  // unconditional (past the end it reloads the last sub-tile), then the last
   int k = 0;
-  for (; k + 2 <= cnt_max; k += 2) {
+  for (; k + 2 <= cnt; k += 2) {
+    load_tq3_half(buf[1], sub_of(t_first + min(k + 1, cnt - 1) * TL), hf, lane);
     step(k, buf[0], buf[1]);
+    load_tq3_half(buf[0], sub_of(t_first + min(k + 2, cnt - 1) * TL), hf, lane);
     step(k + 1, buf[1], buf[0]);
   }
-  if (k < cnt_max) step(k, buf[0], buf[1]);
-  // the combine buffers overlay the fragments and tables (every wave is past
-  // the last barrier of the loop)
+  if (k < cnt) step(k, buf[0], buf[1]);
+  // the combine buffers overlay the fragments and tables
+  __syncthreads();
   float* cbuf = reinterpret_cast<float*>(smem + SM::CBUF_OFF) + hf * SM::CBUF_HALF;
   combine_and_store<DH, 1, 4, D>(cs, cbuf, a, w, ch.k, s, h, row_i, head_j, col_ok, lane, 0, tl, DH * hf, hf == 0);
 }
