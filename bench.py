@@ -446,7 +446,8 @@ def run(args, name):
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_valu_kernel" if args.valu else "attn_tq3_kernel" if wl.fmt == 2 else "attn_kernel",
+            "kernel": ("attn_valu_kernel" if args.valu else
+                       ("attn_tq3_pair_kernel" if wl.d > 128 else "attn_tq3_kernel") if wl.fmt == 2 else "attn_kernel"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -600,7 +601,7 @@ def _dominant(values, workload, per_call=False):
 
 
 def _is_attn(name):
-    return "attn_kernel" in name or "attn_tq3_kernel" in name or "attn_valu_kernel" in name
+    return "attn_kernel" in name or "attn_tq3_kernel" in name or "attn_tq3_pair_kernel" in name or "attn_valu_kernel" in name
 
 
 def summarize_trace(directory, workload, cmd, out_path=None):
