@@ -71,8 +71,9 @@ def event_stride(steps):
     adds ~5 us of GPU time to its step (measured on the dense workload: 66.1
     us per step with events on every step, 60.5 us with none), so the events
     bracket the attention launch of every EVENT_STRIDE-th timed step only
-    (all of them when there are few steps); the step rate counts every step."""
-    return EVENT_STRIDE if steps >= 10 * EVENT_STRIDE else 1
+    (of fewer steps, every k-th with k chosen for at least five samples); the
+    step rate counts every step."""
+    return max(1, min(EVENT_STRIDE, steps // 5))
 
 
 def percentiles(ms):
