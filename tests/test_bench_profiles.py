@@ -129,3 +129,19 @@ def test_sq_summary_per_wave_figures(tmp_path):
     assert per["active_inst_valu_over_wave_cycles"] == 0.25
     assert "== attention kernel (3 dispatches)" in text
     assert "== merge_kernel<256, false> (6 dispatches)" in text
+
+
+def test_every_attention_kernel_is_counted():
+    """The summaries count the dispatches of every partial-attention kernel
+    the library launches (plain, TQ3 one-wave, TQ3 wave-pair, vector-unit)
+    and of nothing else."""
+    for name in ("void svattn::attn_kernel<1, 128, 1, false, true>(svattn::AttnArgs)",
+                 "void svattn::attn_tq3_kernel<128, 1, false>(svattn::AttnArgs)",
+                 "void svattn::attn_tq3_pair_kernel<true>(svattn::AttnArgs)",
+                 "void svattn::attn_valu_kernel<128, false>(svattn::AttnArgs)"):
+        assert bench._is_attn(name), name
+    for name in ("void svattn::merge_kernel<256, true>(svattn::AttnArgs)",
+                 "void svattn::append_tq3_kernel<256>(svattn::AppendArgs)",
+                 "void svattn::append_tq3_qprep_kernel<256>(svattn::AppendArgs, svattn::QPrepArgs, int)",
+                 "void svattn::stream_probe_kernel<16>(unsigned int __vector(4) const*, long, unsigned int*)"):
+        assert not bench._is_attn(name), name
